@@ -1,0 +1,269 @@
+"""numpy front end of the CPU oracle (``oracle/moe_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the product library.  Every function
+forwards host arrays to the single-threaded C oracle, which computes the
+method's plain definition (the header of moe_oracle.c names the passages of
+"UMDK/CAM communication acceleration library deep analysis v2", section 2, it
+follows and the readings it takes).
+
+Receive buffers are returned in canonical form: passthrough rows as uint16
+patterns ``[rows, h]``; quantised rows as int8 codes ``[rows, h]`` plus the
+float32 inverse scales ``[rows]``.  ``rows = bs * k`` is the capacity; rows past
+the dispatched total stay zero.
+
+``Oracle(path)`` wraps one build of the library; the module-level functions use
+the default build ``oracle/liboracle.so`` (compiled on first use if missing).
+The mutation tests load deliberately broken builds through ``Oracle(path)``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import numpy as np
+
+from . import build as _build
+
+KIND_BF16, KIND_FP16, KIND_FP32, KIND_INT8 = 0, 1, 2, 3
+_KIND = {"bf16": KIND_BF16, "fp16": KIND_FP16, "fp32": KIND_FP32, "int8": KIND_INT8}
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+
+_SIGS = {
+    "oracle_bf16_to_f32": [_P, _P, _I64],
+    "oracle_f16_to_f32": [_P, _P, _I64],
+    "oracle_f32_to_bf16": [_P, _P, _I64],
+    "oracle_f32_to_f16": [_P, _P, _I64],
+    "oracle_layout": [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P],
+    "oracle_notify": [_P, _I64, _I64, _P, _P, _P, _P],
+    "oracle_quant_row": [_P, _INT, _I64, _P, _P, _P],
+    "oracle_dispatch": [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _I64, _I64, _INT, _I64,
+                        _P, _P, _P],
+    "oracle_combine": [_P, _P, _P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _I64,
+                       _I64, _P, _INT, _P],
+}
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise OracleError(f"{what} returned {rc}")
+
+
+class Oracle:
+    """One loaded build of the C oracle."""
+
+    def __init__(self, path: str):
+        self.path = path
+        L = ctypes.CDLL(path)
+        for name, argtypes in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = argtypes
+            fn.restype = ctypes.c_int
+        self.L = L
+
+    # -- conversions (exported for the exhaustive pins) --------------------
+
+    def bf16_to_f32(self, bits: np.ndarray) -> np.ndarray:
+        bits = np.ascontiguousarray(bits, dtype=np.uint16)
+        out = np.empty(bits.shape, np.float32)
+        _check(self.L.oracle_bf16_to_f32(_ptr(bits), _ptr(out), bits.size), "bf16_to_f32")
+        return out
+
+    def f16_to_f32(self, bits: np.ndarray) -> np.ndarray:
+        bits = np.ascontiguousarray(bits, dtype=np.uint16)
+        out = np.empty(bits.shape, np.float32)
+        _check(self.L.oracle_f16_to_f32(_ptr(bits), _ptr(out), bits.size), "f16_to_f32")
+        return out
+
+    def f32_to_bf16(self, x: np.ndarray) -> np.ndarray:
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(x.shape, np.uint16)
+        _check(self.L.oracle_f32_to_bf16(_ptr(x), _ptr(out), x.size), "f32_to_bf16")
+        return out
+
+    def f32_to_f16(self, x: np.ndarray) -> np.ndarray:
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(x.shape, np.uint16)
+        _check(self.L.oracle_f32_to_f16(_ptr(x), _ptr(out), x.size), "f32_to_f16")
+        return out
+
+    # -- the four stages ---------------------------------------------------
+
+    def layout(self, topk_idx: np.ndarray, expert_num_per_rank: int,
+               rank_size: int) -> Dict[str, object]:
+        """Stage 1: tokenPerExpert [E], tokenPerRank [R], sendTokenIdx [bs, k], bad."""
+        idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+        if idx.ndim != 2:
+            raise ValueError("topk_idx must be [bs, k]")
+        bs, k = idx.shape
+        e = expert_num_per_rank * rank_size
+        tpe = np.zeros(e, np.int32)
+        tpr = np.zeros(rank_size, np.int32)
+        slot = np.zeros((bs, k), np.int32)
+        bad = ctypes.c_int64(0)
+        _check(self.L.oracle_layout(_ptr(idx), bs, k, expert_num_per_rank, rank_size, _ptr(tpe),
+                                    _ptr(tpr), _ptr(slot), ctypes.addressof(bad)), "layout")
+        return dict(token_per_expert=tpe, token_per_rank=tpr, send_token_idx=slot,
+                    bad=int(bad.value))
+
+    def notify(self, token_per_expert: np.ndarray, expert_num_per_rank: int,
+               rank_size: int) -> Dict[str, np.ndarray]:
+        """Stage 2: putOffset [E], recvCount [R], recvBase [R], recvTokenPerExpert [E]."""
+        tpe = np.ascontiguousarray(token_per_expert, dtype=np.int32)
+        e = expert_num_per_rank * rank_size
+        if tpe.shape != (e,):
+            raise ValueError("token_per_expert must be [E]")
+        put = np.zeros(e, np.int32)
+        cnt = np.zeros(rank_size, np.int32)
+        base = np.zeros(rank_size, np.int32)
+        rtpe = np.zeros(e, np.int32)
+        _check(self.L.oracle_notify(_ptr(tpe), expert_num_per_rank, rank_size, _ptr(put),
+                                    _ptr(cnt), _ptr(base), _ptr(rtpe)), "notify")
+        return dict(put_offset=put, recv_count=cnt, recv_base=base, recv_token_per_expert=rtpe)
+
+    def quant_row(self, x_bits: np.ndarray, x_kind: str = "bf16"):
+        """QuantProcess on one row: (codes int8 [h], inv float32, scale float32)."""
+        x = np.ascontiguousarray(x_bits, dtype=np.uint16).reshape(-1)
+        codes = np.zeros(x.size, np.int8)
+        inv = ctypes.c_float(0.0)
+        s = ctypes.c_float(0.0)
+        _check(self.L.oracle_quant_row(_ptr(x), _KIND[x_kind], x.size, _ptr(codes),
+                                       ctypes.addressof(inv), ctypes.addressof(s)), "quant_row")
+        return codes, np.float32(inv.value), np.float32(s.value)
+
+    def dispatch(self, x_bits: np.ndarray, x_kind: str, topk_idx: np.ndarray,
+                 send_token_idx: np.ndarray, put_offset: np.ndarray, recv_base: np.ndarray,
+                 expert_num_per_rank: int, rank_size: int, quant: bool) -> Dict[str, np.ndarray]:
+        """Stage 3: scatter rows (optionally quantised) into a [bs*k]-row buffer."""
+        x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        bs, h = x.shape
+        idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+        k = idx.shape[1]
+        slot = np.ascontiguousarray(send_token_idx, dtype=np.int32)
+        put = np.ascontiguousarray(put_offset, dtype=np.int32)
+        base = np.ascontiguousarray(recv_base, dtype=np.int32)
+        rows = bs * k
+        recv = codes = inv = None
+        if quant:
+            codes = np.zeros((rows, h), np.int8)
+            inv = np.zeros(rows, np.float32)
+        else:
+            recv = np.zeros((rows, h), np.uint16)
+        _check(self.L.oracle_dispatch(_ptr(x), _KIND[x_kind], bs, h, k, _ptr(idx), _ptr(slot),
+                                      _ptr(put), _ptr(base), expert_num_per_rank, rank_size,
+                                      1 if quant else 0, rows, _ptr(recv), _ptr(codes),
+                                      _ptr(inv)), "dispatch")
+        if quant:
+            return dict(codes=codes, inv=inv)
+        return dict(rows=recv)
+
+    def combine(self, recv: Dict[str, np.ndarray], recv_kind: str, topk_idx: np.ndarray,
+                topk_w: np.ndarray, send_token_idx: np.ndarray, put_offset: np.ndarray,
+                recv_base: np.ndarray, expert_num_per_rank: int, rank_size: int,
+                out_kind: str) -> np.ndarray:
+        """Stage 4: weighted gather.  Returns uint16 patterns (bf16/fp16) or float32."""
+        idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+        bs, k = idx.shape
+        w = np.ascontiguousarray(topk_w, dtype=np.float32)
+        slot = np.ascontiguousarray(send_token_idx, dtype=np.int32)
+        put = np.ascontiguousarray(put_offset, dtype=np.int32)
+        base = np.ascontiguousarray(recv_base, dtype=np.int32)
+        if recv_kind == "int8":
+            codes = np.ascontiguousarray(recv["codes"], dtype=np.int8)
+            inv = np.ascontiguousarray(recv["inv"], dtype=np.float32)
+            rows_arr = None
+            rows, h = codes.shape
+        else:
+            rows_arr = np.ascontiguousarray(recv["rows"], dtype=np.uint16)
+            codes = inv = None
+            rows, h = rows_arr.shape
+        out = np.zeros((bs, h), np.float32 if out_kind == "fp32" else np.uint16)
+        scratch = np.zeros(h, np.float32)
+        _check(self.L.oracle_combine(_ptr(rows_arr), _ptr(codes), _ptr(inv), _KIND[recv_kind], bs,
+                                     h, k, _ptr(idx), _ptr(w), _ptr(slot), _ptr(put), _ptr(base),
+                                     expert_num_per_rank, rank_size, rows, _ptr(out),
+                                     _KIND[out_kind], _ptr(scratch)), "combine")
+        return out
+
+    def pipeline(self, x_bits: np.ndarray, x_kind: str, topk_idx: np.ndarray,
+                 topk_w: np.ndarray, expert_num_per_rank: int, rank_size: int, quant: bool,
+                 out_kind: Optional[str] = None) -> Dict[str, object]:
+        """All four stages in order; returns every intermediate."""
+        lay = self.layout(topk_idx, expert_num_per_rank, rank_size)
+        no = self.notify(lay["token_per_expert"], expert_num_per_rank, rank_size)
+        dis = self.dispatch(x_bits, x_kind, topk_idx, lay["send_token_idx"], no["put_offset"],
+                            no["recv_base"], expert_num_per_rank, rank_size, quant)
+        out_kind = out_kind or x_kind
+        out = self.combine(dis, "int8" if quant else x_kind, topk_idx, topk_w,
+                           lay["send_token_idx"], no["put_offset"], no["recv_base"],
+                           expert_num_per_rank, rank_size, out_kind)
+        return dict(layout=lay, notify=no, dispatch=dis, out=out)
+
+
+_default: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    """The oracle built from oracle/moe_oracle.c (compiled here if missing)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        _default = Oracle(_build.LIB)
+    return _default
+
+
+def bf16_to_f32(bits):
+    return default().bf16_to_f32(bits)
+
+
+def f16_to_f32(bits):
+    return default().f16_to_f32(bits)
+
+
+def f32_to_bf16(x):
+    return default().f32_to_bf16(x)
+
+
+def f32_to_f16(x):
+    return default().f32_to_f16(x)
+
+
+def layout(*a, **kw):
+    return default().layout(*a, **kw)
+
+
+def notify(*a, **kw):
+    return default().notify(*a, **kw)
+
+
+def quant_row(*a, **kw):
+    return default().quant_row(*a, **kw)
+
+
+def dispatch(*a, **kw):
+    return default().dispatch(*a, **kw)
+
+
+def combine(*a, **kw):
+    return default().combine(*a, **kw)
+
+
+def pipeline(*a, **kw):
+    return default().pipeline(*a, **kw)

@@ -1,0 +1,377 @@
+/*
+ * CPU oracle for the MoE expert-parallel "EP normal" dispatch/combine
+ * pipeline: layout -> notify -> dispatch (optional dynamic int8 quant) ->
+ * combine.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no source
+ * with the HIP library and the HIP library never calls it.
+ *
+ * Source of the method: the page "UMDK/CAM communication acceleration library
+ * deep analysis v2" (backyes.github.io, CAM v2 analysis), section 2 "EP Normal
+ * communication operators":
+ *   2.1  the four stages and their order,
+ *   2.2.1 comm_args.h (UB_ALIGN_SIZE = 32 bytes; the CommArgs scalars),
+ *   2.3  moe_dispatch_layout_zb (per-expert counts, per-(token,k) send index),
+ *   2.4  moe_notify_dispatch_zb (prefix sums: putOffset, receive counts),
+ *   2.5  moe_dispatch_normal_zb / QuantProcess (row scatter, dynamic int8),
+ *   2.6  moe_combine_normal_zb / ReadBufferAndWeightedSum (weighted gather),
+ *   2.8  the per-rank zero-buffer layout (token region read by combine).
+ *
+ * Everything here is the plain definition, in the order the page gives,
+ * single-threaded, in IEEE binary32 where the page fixes float (the quantiser
+ * and the combine accumulator are float on the page).  Build with
+ *   gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math
+ * so that every multiply and every add is rounded on its own.
+ *
+ * Readings taken where the page leaves a step open:
+ *  - send slots are the stable counting-sort rank: entries of one expert are
+ *    numbered in flat (token, k) order, token-ascending;
+ *  - per-rank counts count rows (one per (token, k) entry), since combine
+ *    reads one row per entry;
+ *  - on one device the logical ranks' receive regions are concatenated in
+ *    rank order with no gaps, and inside a rank the experts' rows are
+ *    contiguous in expert order;
+ *  - the quantiser stores the inverse scale 1/s; combine dequantises with
+ *    (float)q * inv before the weight multiply;
+ *  - combine sums j = 0..k-1 from +0.0f, multiply then add, each rounded;
+ *  - expert ids outside [0, E) are counted as bad, get slot -1, are not
+ *    dispatched and add nothing in combine.
+ *
+ * Parity pins live in tests/ (brute force, stable-sort and prefix-sum
+ * equivalence, hand-worked quantiser rows, order-sensitive combine rows,
+ * float64 error bounds, exhaustive conversion checks).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG (-1)
+#define ORACLE_INTERNAL (-2)
+
+/* Element kinds used by the oracle's entry points. */
+#define KIND_BF16 0
+#define KIND_FP16 1
+#define KIND_FP32 2
+#define KIND_INT8 3
+
+/* ------------------------------------------------------------------------ */
+/* Scalar conversions, written from the IEEE 754 / bfloat16 definitions.     */
+/* ------------------------------------------------------------------------ */
+
+static float bits_to_f32(uint32_t u) {
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+static uint32_t f32_to_bits(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return u;
+}
+
+/* bfloat16 is the upper half of a binary32: widening is exact. */
+static float bf16_to_f32(uint16_t b) { return bits_to_f32((uint32_t)b << 16); }
+
+/* binary16 -> binary32, exact: value = (-1)^s * m * 2^(exp-25) for normal
+ * numbers with implicit bit, m * 2^-24 for subnormals. */
+static float f16_to_f32(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int exp = (h >> 10) & 0x1F;
+  int man = h & 0x3FF;
+  float mag;
+  if (exp == 0) {
+    mag = ldexpf((float)man, -24);
+  } else if (exp == 31) {
+    mag = man ? NAN : INFINITY;
+  } else {
+    mag = ldexpf((float)(1024 + man), exp - 25);
+  }
+  return sign ? -mag : mag;
+}
+
+/* binary32 -> bfloat16 with round-half-to-even.  The two candidates are the
+ * truncation T (upper 16 bits) and T + 1; the discarded low half decides:
+ * above 0x8000 rounds up, below rounds down, exactly 0x8000 picks the even
+ * one.  Carries ripple into the exponent, which is the correct result
+ * (including rounding up to infinity). */
+static uint16_t f32_to_bf16(float f) {
+  uint32_t u = f32_to_bits(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) {
+    return (uint16_t)((u >> 16) | 0x0040u); /* quiet NaN, keep sign */
+  }
+  uint32_t upper = u >> 16;
+  uint32_t lower = u & 0xFFFFu;
+  if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;
+  return (uint16_t)upper;
+}
+
+/* binary32 -> binary16 with round-half-to-even, from the definition: find
+ * the binade of |f|, scale the significand to an integer count of binary16
+ * ulps in double (exact), round that count to nearest-even, re-encode. */
+static uint16_t f32_to_f16(float f) {
+  uint16_t sign = (f32_to_bits(f) >> 16) & 0x8000u;
+  if (isnan(f)) return (uint16_t)(sign | 0x7E00u);
+  double a = fabs((double)f);
+  if (isinf(f)) return (uint16_t)(sign | 0x7C00u);
+  if (a < ldexp(1.0, -14)) {
+    /* subnormal range: ulp is 2^-24; a count of 1024 is the smallest normal,
+     * whose encoding 0x0400 is the same integer. */
+    double m = nearbyint(a * ldexp(1.0, 24));
+    return (uint16_t)(sign | (uint16_t)m);
+  }
+  int e2;
+  (void)frexp(a, &e2); /* a = fr * 2^e2, fr in [0.5, 1) */
+  int e = e2 - 1;      /* a in [2^e, 2^(e+1)) */
+  double m = nearbyint(ldexp(a, 10 - e)); /* in [1024, 2048] */
+  if (m == 2048.0) {
+    m = 1024.0;
+    e += 1;
+  }
+  if (e > 15) return (uint16_t)(sign | 0x7C00u);
+  return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)((int)m - 1024));
+}
+
+static float to_f32(uint16_t v, int kind) {
+  return kind == KIND_FP16 ? f16_to_f32(v) : bf16_to_f32(v);
+}
+
+/* Array forms, exported so the tests can pin the conversions exhaustively. */
+int oracle_bf16_to_f32(const uint16_t *in, float *out, int64_t n) {
+  if ((n && (!in || !out)) || n < 0) return ORACLE_BAD_ARG;
+  for (int64_t i = 0; i < n; ++i) out[i] = bf16_to_f32(in[i]);
+  return ORACLE_OK;
+}
+int oracle_f16_to_f32(const uint16_t *in, float *out, int64_t n) {
+  if ((n && (!in || !out)) || n < 0) return ORACLE_BAD_ARG;
+  for (int64_t i = 0; i < n; ++i) out[i] = f16_to_f32(in[i]);
+  return ORACLE_OK;
+}
+int oracle_f32_to_bf16(const float *in, uint16_t *out, int64_t n) {
+  if ((n && (!in || !out)) || n < 0) return ORACLE_BAD_ARG;
+  for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16(in[i]);
+  return ORACLE_OK;
+}
+int oracle_f32_to_f16(const float *in, uint16_t *out, int64_t n) {
+  if ((n && (!in || !out)) || n < 0) return ORACLE_BAD_ARG;
+  for (int64_t i = 0; i < n; ++i) out[i] = f32_to_f16(in[i]);
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Stage 1: dispatch layout (page section 2.3).                              */
+/* ------------------------------------------------------------------------ */
+
+/* tokenPerExpert[e] = number of (t, j) with topkIdx[t, j] == e.
+ * sendTokenIdx[t, j] = how many earlier entries (in flat t*k + j order) went
+ * to the same expert -- the entry's position inside its expert's region.
+ * tokenPerRank[r] = sum of tokenPerExpert over rank r's experts
+ * e in [r*EPR, (r+1)*EPR).  Ids outside [0, E) are bad: slot -1. */
+int oracle_layout(const int32_t *topk_idx, int64_t bs, int64_t k, int64_t epr,
+                  int64_t ranks, int32_t *token_per_expert, int32_t *token_per_rank,
+                  int32_t *send_token_idx, int64_t *bad_count) {
+  if (bs < 0 || k < 1 || epr < 1 || ranks < 1) return ORACLE_BAD_ARG;
+  if (!token_per_expert || !token_per_rank || !bad_count) return ORACLE_BAD_ARG;
+  if (bs > 0 && (!topk_idx || !send_token_idx)) return ORACLE_BAD_ARG;
+  int64_t num_experts = epr * ranks;
+
+  for (int64_t e = 0; e < num_experts; ++e) token_per_expert[e] = 0;
+  int64_t bad = 0;
+  for (int64_t t = 0; t < bs; ++t) {
+    for (int64_t j = 0; j < k; ++j) {
+      int32_t e = topk_idx[t * k + j];
+      if (e < 0 || e >= num_experts) {
+        send_token_idx[t * k + j] = -1;
+        bad += 1;
+        continue;
+      }
+      send_token_idx[t * k + j] = token_per_expert[e];
+      token_per_expert[e] += 1;
+    }
+  }
+  for (int64_t r = 0; r < ranks; ++r) {
+    int32_t sum = 0;
+    for (int64_t e = r * epr; e < (r + 1) * epr; ++e) sum += token_per_expert[e];
+    token_per_rank[r] = sum;
+  }
+  *bad_count = bad;
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Stage 2: notify (page section 2.4).                                       */
+/* ------------------------------------------------------------------------ */
+
+/* With one source the all-gather of tokenPerExpert is the identity.  Inside
+ * each destination rank r the experts' regions follow each other in expert
+ * order: putOffset[e] = sum of the counts of r's earlier experts, and
+ * recvCount[r] = the total of r's experts.  The ranks' regions follow each
+ * other in rank order: recvBase[r] = sum of recvCount[r'] for r' < r.
+ * recvTokenPerExpert is the per-expert receive count (one source: the same
+ * numbers as the input). */
+int oracle_notify(const int32_t *token_per_expert, int64_t epr, int64_t ranks,
+                  int32_t *put_offset, int32_t *recv_count, int32_t *recv_base,
+                  int32_t *recv_token_per_expert) {
+  if (epr < 1 || ranks < 1) return ORACLE_BAD_ARG;
+  if (!token_per_expert || !put_offset || !recv_count || !recv_base || !recv_token_per_expert)
+    return ORACLE_BAD_ARG;
+  int32_t base = 0;
+  for (int64_t r = 0; r < ranks; ++r) {
+    int32_t acc = 0;
+    for (int64_t e = r * epr; e < (r + 1) * epr; ++e) {
+      put_offset[e] = acc;
+      acc += token_per_expert[e];
+      recv_token_per_expert[e] = token_per_expert[e];
+    }
+    recv_count[r] = acc;
+    recv_base[r] = base;
+    base += acc;
+  }
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Stage 3: dispatch (page section 2.5).                                     */
+/* ------------------------------------------------------------------------ */
+
+/* QuantProcess for one row of h elements:
+ *   f_i  = float(x_i)                          (exact widening)
+ *   amax = max_i |f_i|
+ *   s    = 127.0f / (amax + 1e-12f)            (binary32 add, then divide)
+ *   q_i  = round-half-even(f_i * s)            (one binary32 multiply)
+ *   inv  = 1.0f / s                            (stored after the row)
+ * The page's cast chain int32 -> half -> int8 is exact here: |f_i * s| can
+ * not reach 127.5, so q_i is already in [-127, 127]. */
+int oracle_quant_row(const uint16_t *x, int x_kind, int64_t h, int8_t *codes, float *inv,
+                     float *scale_out) {
+  if (!x || !codes || !inv || h < 1) return ORACLE_BAD_ARG;
+  if (x_kind != KIND_BF16 && x_kind != KIND_FP16) return ORACLE_BAD_ARG;
+  float amax = 0.0f;
+  for (int64_t i = 0; i < h; ++i) {
+    float a = fabsf(to_f32(x[i], x_kind));
+    if (a > amax) amax = a;
+  }
+  float denom = amax + 1e-12f;
+  float s = 127.0f / denom;
+  for (int64_t i = 0; i < h; ++i) {
+    float y = to_f32(x[i], x_kind) * s;
+    float r = nearbyintf(y); /* default rounding mode: to nearest, ties even */
+    if (r > 127.0f || r < -127.0f) return ORACLE_INTERNAL;
+    codes[i] = (int8_t)(int32_t)r;
+  }
+  *inv = 1.0f / s;
+  if (scale_out) *scale_out = s;
+  return ORACLE_OK;
+}
+
+/* Destination row of entry (t, j), or -1 if the entry is not dispatched. */
+static int64_t dest_row(const int32_t *topk_idx, const int32_t *send_token_idx,
+                        const int32_t *put_offset, const int32_t *recv_base, int64_t k,
+                        int64_t epr, int64_t num_experts, int64_t t, int64_t j) {
+  int32_t e = topk_idx[t * k + j];
+  int32_t slot = send_token_idx[t * k + j];
+  if (e < 0 || e >= num_experts || slot < 0) return -1;
+  return (int64_t)recv_base[e / epr] + put_offset[e] + slot;
+}
+
+/* Scatter: row dst(t, j) of the receive buffer gets token t's row, either as
+ * is (quant == 0: recv_rows[rows][h], 16-bit patterns of x's type) or as
+ * int8 codes plus inverse scale (quant == 1: codes[rows][h], inv[rows]).
+ * Every one of a token's k copies carries the same bytes.  Rows never
+ * written are left as the caller initialised them. */
+int oracle_dispatch(const uint16_t *x, int x_kind, int64_t bs, int64_t h, int64_t k,
+                    const int32_t *topk_idx, const int32_t *send_token_idx,
+                    const int32_t *put_offset, const int32_t *recv_base, int64_t epr,
+                    int64_t ranks, int quant, int64_t rows, uint16_t *recv_rows,
+                    int8_t *codes, float *inv) {
+  if (bs < 0 || h < 1 || k < 1 || epr < 1 || ranks < 1 || rows < 0) return ORACLE_BAD_ARG;
+  if (x_kind != KIND_BF16 && x_kind != KIND_FP16) return ORACLE_BAD_ARG;
+  if (bs == 0) return ORACLE_OK;
+  if (!x || !topk_idx || !send_token_idx || !put_offset || !recv_base) return ORACLE_BAD_ARG;
+  if (quant ? (!codes || !inv) : !recv_rows) return ORACLE_BAD_ARG;
+  int64_t num_experts = epr * ranks;
+  for (int64_t t = 0; t < bs; ++t) {
+    const uint16_t *src = x + t * h;
+    for (int64_t j = 0; j < k; ++j) {
+      int64_t dst = dest_row(topk_idx, send_token_idx, put_offset, recv_base, k, epr,
+                             num_experts, t, j);
+      if (dst < 0) continue;
+      if (dst >= rows) return ORACLE_INTERNAL;
+      if (!quant) {
+        for (int64_t i = 0; i < h; ++i) recv_rows[dst * h + i] = src[i];
+      } else {
+        /* each copy is quantised from the source row on its own; the result
+         * only depends on the row, so all k copies carry the same bytes */
+        int rc = oracle_quant_row(src, x_kind, h, codes + dst * h, &inv[dst], NULL);
+        if (rc) return rc;
+      }
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Stage 4: combine (page section 2.6).                                      */
+/* ------------------------------------------------------------------------ */
+
+/* For each token t and element i:
+ *   acc = +0.0f
+ *   for j = 0 .. k-1 (dispatched entries only):
+ *       v   = float(row[dst(t,j)][i])            (bf16 / fp16 rows)
+ *          or float(code) * inv[dst(t,j)]         (int8 rows; dequantise)
+ *       p   = v * topkWeights[t, j]              (rounded)
+ *       acc = acc + p                            (rounded)
+ *   out[t, i] = acc rounded half-even to the output type (or acc for fp32).
+ * recv_kind: KIND_BF16 / KIND_FP16 with recv_rows, or KIND_INT8 with codes
+ * and inv.  out_kind: KIND_BF16, KIND_FP16 (uint16 patterns) or KIND_FP32. */
+int oracle_combine(const uint16_t *recv_rows, const int8_t *codes, const float *inv,
+                   int recv_kind, int64_t bs, int64_t h, int64_t k, const int32_t *topk_idx,
+                   const float *topk_w, const int32_t *send_token_idx,
+                   const int32_t *put_offset, const int32_t *recv_base, int64_t epr,
+                   int64_t ranks, int64_t rows, void *out, int out_kind, float *acc_scratch) {
+  if (bs < 0 || h < 1 || k < 1 || epr < 1 || ranks < 1 || rows < 0) return ORACLE_BAD_ARG;
+  if (recv_kind != KIND_BF16 && recv_kind != KIND_FP16 && recv_kind != KIND_INT8)
+    return ORACLE_BAD_ARG;
+  if (out_kind != KIND_BF16 && out_kind != KIND_FP16 && out_kind != KIND_FP32)
+    return ORACLE_BAD_ARG;
+  if (bs == 0) return ORACLE_OK;
+  if (!topk_idx || !topk_w || !send_token_idx || !put_offset || !recv_base || !out ||
+      !acc_scratch)
+    return ORACLE_BAD_ARG;
+  if (recv_kind == KIND_INT8 ? (!codes || !inv) : !recv_rows) return ORACLE_BAD_ARG;
+  int64_t num_experts = epr * ranks;
+  float *acc = acc_scratch; /* h floats, supplied by the caller */
+  for (int64_t t = 0; t < bs; ++t) {
+    for (int64_t i = 0; i < h; ++i) acc[i] = 0.0f;
+    for (int64_t j = 0; j < k; ++j) {
+      int64_t dst = dest_row(topk_idx, send_token_idx, put_offset, recv_base, k, epr,
+                             num_experts, t, j);
+      if (dst < 0) continue;
+      if (dst >= rows) return ORACLE_INTERNAL;
+      float w = topk_w[t * k + j];
+      for (int64_t i = 0; i < h; ++i) {
+        float v;
+        if (recv_kind == KIND_INT8) {
+          v = (float)codes[dst * h + i] * inv[dst];
+        } else {
+          v = to_f32(recv_rows[dst * h + i], recv_kind);
+        }
+        float p = v * w;
+        acc[i] = acc[i] + p;
+      }
+    }
+    for (int64_t i = 0; i < h; ++i) {
+      if (out_kind == KIND_FP32) {
+        ((float *)out)[t * h + i] = acc[i];
+      } else if (out_kind == KIND_BF16) {
+        ((uint16_t *)out)[t * h + i] = f32_to_bf16(acc[i]);
+      } else {
+        ((uint16_t *)out)[t * h + i] = f32_to_f16(acc[i]);
+      }
+    }
+  }
+  return ORACLE_OK;
+}
