@@ -1,0 +1,249 @@
+"""Python binding of libmoe_ep.so, the MI355X (gfx950) MoE expert-parallel
+dispatch/combine library.
+
+The functions below carry the names of the C entry points declared in
+include/moe_ep.h and only marshal arguments: they check that tensors are
+CUDA (HIP) tensors of the right dtype and contiguity, pass their device
+pointers and torch's current stream to the C call, and raise ``MoeEpError``
+on a non-zero status.  Every step of the path runs in the library's HIP
+kernels; there is no fallback.  Importing this module fails loudly if the
+library has not been built (``python combine_moe_layout_03_amd/build.py`` or
+``__graft_entry__.build()``).
+
+``EpBuffers`` allocates (through torch) every device buffer the four stages
+need for one shape, so a caller can run the pipeline without allocating.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "MOE_BF16", "MOE_FP16", "MOE_FP32", "MOE_INT8_ROWSCALE", "MoeEpError", "LIB_PATH",
+    "moe_recv_row_bytes", "moe_layout_workspace_bytes", "moe_layout", "moe_notify",
+    "moe_dispatch", "moe_combine", "moe_status_str", "moe_last_hip_error", "EpBuffers",
+    "dtype_code",
+]
+
+MOE_BF16, MOE_FP16, MOE_FP32, MOE_INT8_ROWSCALE = 0, 1, 2, 3
+MOE_MAX_EXPERTS, MOE_MAX_HIDDEN, MOE_MAX_TOPK = 2048, 16384, 32
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_ep.so")
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_INT = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+# name -> (argtypes, restype); mirrors include/moe_ep.h
+_SIGS = {
+    "moe_recv_row_bytes": ([_I32, _INT, ctypes.POINTER(_SZ)], _INT),
+    "moe_layout_workspace_bytes": ([_I32, _I32, _I32, ctypes.POINTER(_SZ)], _INT),
+    "moe_layout": ([_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P], _INT),
+    "moe_notify": ([_P, _I32, _I32, _P, _P, _P, _P, _P], _INT),
+    "moe_dispatch": ([_P, _INT, _I32, _I32, _I32, _P, _P, _P, _P, _I32, _I32, _INT, _P, _SZ, _P],
+                     _INT),
+    "moe_combine": ([_P, _INT, _SZ, _I32, _I32, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _INT, _P],
+                    _INT),
+    "moe_status_str": ([_INT], ctypes.c_char_p),
+    "moe_last_hip_error": ([], _INT),
+}
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; build it with `python combine_moe_layout_03_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (argtypes, restype) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = restype
+    return lib
+
+
+_lib = _load()
+
+
+class MoeEpError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = _lib.moe_status_str(status).decode()
+        if status == 8:
+            msg += f" (hipError {_lib.moe_last_hip_error()})"
+        super().__init__(f"{fn}: status {status}: {msg}")
+        self.status = status
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MoeEpError(fn, status)
+
+
+def moe_status_str(status: int) -> str:
+    return _lib.moe_status_str(status).decode()
+
+
+def moe_last_hip_error() -> int:
+    return _lib.moe_last_hip_error()
+
+
+_DTYPE = {torch.bfloat16: MOE_BF16, torch.float16: MOE_FP16, torch.float32: MOE_FP32}
+
+
+def dtype_code(dtype: torch.dtype) -> int:
+    try:
+        return _DTYPE[dtype]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {dtype}") from None
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None, optional: bool = False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def moe_recv_row_bytes(hidden: int, recv_type: int) -> int:
+    out = _SZ(0)
+    _check("moe_recv_row_bytes", _lib.moe_recv_row_bytes(hidden, recv_type, ctypes.byref(out)))
+    return out.value
+
+
+def moe_layout_workspace_bytes(bs: int, topk: int, num_experts: int) -> int:
+    out = _SZ(0)
+    _check("moe_layout_workspace_bytes",
+           _lib.moe_layout_workspace_bytes(bs, topk, num_experts, ctypes.byref(out)))
+    return out.value
+
+
+def moe_layout(topk_idx: torch.Tensor, expert_num_per_rank: int, rank_size: int,
+               token_per_expert: torch.Tensor, token_per_rank: torch.Tensor,
+               send_token_idx: torch.Tensor, bad_id_count: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [bs, topk]")
+    bs, topk = topk_idx.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("moe_layout", _lib.moe_layout(
+        _dev(topk_idx, "topk_idx", torch.int32), bs, topk, expert_num_per_rank, rank_size,
+        _dev(token_per_expert, "token_per_expert", torch.int32),
+        _dev(token_per_rank, "token_per_rank", torch.int32),
+        _dev(send_token_idx, "send_token_idx", torch.int32),
+        _dev(bad_id_count, "bad_id_count", torch.int32, optional=True),
+        _dev(workspace, "workspace", optional=True), ws_bytes, _stream(stream)))
+
+
+def moe_notify(token_per_expert: torch.Tensor, expert_num_per_rank: int, rank_size: int,
+               put_offset: torch.Tensor, recv_count: torch.Tensor, recv_base: torch.Tensor,
+               recv_token_per_expert: torch.Tensor, stream=None) -> None:
+    _check("moe_notify", _lib.moe_notify(
+        _dev(token_per_expert, "token_per_expert", torch.int32), expert_num_per_rank, rank_size,
+        _dev(put_offset, "put_offset", torch.int32), _dev(recv_count, "recv_count", torch.int32),
+        _dev(recv_base, "recv_base", torch.int32),
+        _dev(recv_token_per_expert, "recv_token_per_expert", torch.int32), _stream(stream)))
+
+
+def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, send_token_idx: torch.Tensor,
+                 put_offset: torch.Tensor, recv_base: torch.Tensor, expert_num_per_rank: int,
+                 rank_size: int, quant_int8: bool, recv_x: torch.Tensor, stream=None) -> None:
+    if x.dim() != 2 or topk_idx.dim() != 2:
+        raise ValueError("x must be [bs, hidden] and topk_idx [bs, topk]")
+    bs, hidden = x.shape
+    topk = topk_idx.shape[1]
+    _check("moe_dispatch", _lib.moe_dispatch(
+        _dev(x, "x"), dtype_code(x.dtype), bs, hidden, topk,
+        _dev(topk_idx, "topk_idx", torch.int32), _dev(send_token_idx, "send_token_idx", torch.int32),
+        _dev(put_offset, "put_offset", torch.int32), _dev(recv_base, "recv_base", torch.int32),
+        expert_num_per_rank, rank_size, 1 if quant_int8 else 0, _dev(recv_x, "recv_x"),
+        recv_x.numel() * recv_x.element_size(), _stream(stream)))
+
+
+def moe_combine(recv_x: torch.Tensor, recv_type: int, hidden: int, topk_idx: torch.Tensor,
+                topk_weights: torch.Tensor, send_token_idx: torch.Tensor, put_offset: torch.Tensor,
+                recv_base: torch.Tensor, expert_num_per_rank: int, rank_size: int,
+                out: torch.Tensor, stream=None) -> None:
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [bs, topk]")
+    bs, topk = topk_idx.shape
+    if out.dim() != 2 or tuple(out.shape) != (bs, hidden):
+        raise ValueError("out must be [bs, hidden]")
+    _check("moe_combine", _lib.moe_combine(
+        _dev(recv_x, "recv_x"), recv_type, recv_x.numel() * recv_x.element_size(), bs, hidden, topk,
+        _dev(topk_idx, "topk_idx", torch.int32), _dev(topk_weights, "topk_weights", torch.float32),
+        _dev(send_token_idx, "send_token_idx", torch.int32), _dev(put_offset, "put_offset", torch.int32),
+        _dev(recv_base, "recv_base", torch.int32), expert_num_per_rank, rank_size, _dev(out, "out"),
+        dtype_code(out.dtype), _stream(stream)))
+
+
+class EpBuffers:
+    """Device buffers of one pipeline shape, allocated once through torch.
+
+    ``run`` enqueues layout -> notify -> dispatch -> combine on the current
+    stream and allocates nothing."""
+
+    def __init__(self, bs: int, hidden: int, topk: int, expert_num_per_rank: int, rank_size: int,
+                 x_dtype: torch.dtype = torch.bfloat16, quant_int8: bool = True,
+                 out_dtype: Optional[torch.dtype] = None, device="cuda"):
+        e = expert_num_per_rank * rank_size
+        self.bs, self.hidden, self.topk = bs, hidden, topk
+        self.epr, self.ranks, self.num_experts = expert_num_per_rank, rank_size, e
+        self.quant_int8 = quant_int8
+        self.x_dtype = x_dtype
+        self.recv_type = MOE_INT8_ROWSCALE if quant_int8 else dtype_code(x_dtype)
+        self.row_bytes = moe_recv_row_bytes(hidden, self.recv_type)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.token_per_expert = torch.zeros(e, **i32)
+        self.token_per_rank = torch.zeros(rank_size, **i32)
+        self.send_token_idx = torch.zeros((bs, topk), **i32)
+        self.bad_id_count = torch.zeros(1, **i32)
+        ws = moe_layout_workspace_bytes(bs, topk, e)
+        self.workspace = torch.zeros(max(ws, 4) // 4, **i32)
+        self.put_offset = torch.zeros(e, **i32)
+        self.recv_count = torch.zeros(rank_size, **i32)
+        self.recv_base = torch.zeros(rank_size, **i32)
+        self.recv_token_per_expert = torch.zeros(e, **i32)
+        self.recv_x = torch.zeros(bs * topk * self.row_bytes, dtype=torch.uint8, device=device)
+        self.out = torch.zeros((bs, hidden), dtype=out_dtype or x_dtype, device=device)
+
+    def layout(self, topk_idx, stream=None):
+        moe_layout(topk_idx, self.epr, self.ranks, self.token_per_expert, self.token_per_rank,
+                   self.send_token_idx, self.bad_id_count, self.workspace, stream)
+
+    def notify(self, stream=None):
+        moe_notify(self.token_per_expert, self.epr, self.ranks, self.put_offset, self.recv_count,
+                   self.recv_base, self.recv_token_per_expert, stream)
+
+    def dispatch(self, x, topk_idx, stream=None):
+        moe_dispatch(x, topk_idx, self.send_token_idx, self.put_offset, self.recv_base, self.epr,
+                     self.ranks, self.quant_int8, self.recv_x, stream)
+
+    def combine(self, topk_idx, topk_w, stream=None):
+        moe_combine(self.recv_x, self.recv_type, self.hidden, topk_idx, topk_w, self.send_token_idx,
+                    self.put_offset, self.recv_base, self.epr, self.ranks, self.out, stream)
+
+    def run(self, x, topk_idx, topk_w, stream=None):
+        self.layout(topk_idx, stream)
+        self.notify(stream)
+        self.dispatch(x, topk_idx, stream)
+        self.combine(topk_idx, topk_w, stream)
+        return self.out

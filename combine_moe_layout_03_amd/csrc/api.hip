@@ -1,0 +1,209 @@
+// C entry points of libmoe_ep: argument checks on the host, then kernel
+// launches on the caller's stream.  Every check runs before anything is
+// enqueued, so a call that returns an error has enqueued nothing.  No call
+// allocates, frees or waits.
+#include <hip/hip_runtime.h>
+
+#include <limits>
+
+#include "launch.h"
+#include "moe_ep.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t err) {
+  if (err == hipSuccess) return MOE_OK;
+  g_last_hip_error = static_cast<int>(err);
+  return MOE_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align32(int64_t v) { return static_cast<size_t>((v + 31) / 32 * 32); }
+
+// Shared checks on the routing scalars.
+int check_experts(int32_t epr, int32_t ranks) {
+  if (epr < 1 || ranks < 1) return MOE_ERR_BAD_SHAPE;
+  const int64_t e = static_cast<int64_t>(epr) * ranks;
+  if (e > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_tokens(int32_t bs, int32_t topk) {
+  if (bs < 0 || topk < 1) return MOE_ERR_BAD_SHAPE;
+  if (topk > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(bs) * topk > std::numeric_limits<int32_t>::max()) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_hidden(int32_t hidden) {
+  if (hidden < 1) return MOE_ERR_BAD_SHAPE;
+  if (hidden % 8 != 0 || hidden > MOE_MAX_HIDDEN) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int row_bytes(int32_t hidden, moe_dtype recv, size_t* bytes) {
+  switch (recv) {
+    case MOE_BF16:
+    case MOE_FP16:
+      *bytes = static_cast<size_t>(hidden) * 2u;
+      return MOE_OK;
+    case MOE_INT8_ROWSCALE:
+      *bytes = align32(hidden) + 32u;
+      return MOE_OK;
+    default:
+      return MOE_ERR_BAD_DTYPE;
+  }
+}
+
+// Routing arguments common to dispatch and combine.
+int make_route(int32_t bs, int32_t hidden, int32_t topk, const int32_t* topk_idx,
+               const int32_t* send_token_idx, const int32_t* put_offset, const int32_t* recv_base,
+               int32_t epr, int32_t ranks, moe_dtype recv_type, size_t recv_bytes,
+               moe::RouteArgs* r) {
+  int st = check_tokens(bs, topk);
+  if (st) return st;
+  if ((st = check_experts(epr, ranks))) return st;
+  if ((st = check_hidden(hidden))) return st;
+  size_t rb = 0;
+  if ((st = row_bytes(hidden, recv_type, &rb))) return st;
+  if (bs == 0) return MOE_OK;  // nothing to move; empty tensors may have NULL data
+  if (!topk_idx || !send_token_idx || !put_offset || !recv_base) return MOE_ERR_NULL_PTR;
+  if (!aligned(topk_idx, 4) || !aligned(send_token_idx, 4) || !aligned(put_offset, 4) ||
+      !aligned(recv_base, 4))
+    return MOE_ERR_BAD_ALIGN;
+  const size_t need = rb * static_cast<size_t>(bs) * static_cast<size_t>(topk);
+  if (recv_bytes < need) return MOE_ERR_BUFFER_TOO_SMALL;
+  r->topk_idx = topk_idx;
+  r->send_token_idx = send_token_idx;
+  r->put_offset = put_offset;
+  r->recv_base = recv_base;
+  r->bs = bs;
+  r->hidden = hidden;
+  r->k = topk;
+  r->epr = epr;
+  r->num_experts = epr * ranks;
+  r->row_bytes = static_cast<int64_t>(rb);
+  r->cap_rows = static_cast<int64_t>(recv_bytes / rb);
+  r->scale_off = static_cast<int32_t>(align32(hidden));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_recv_row_bytes(int32_t hidden, moe_dtype recv, size_t* bytes) {
+  if (!bytes) return MOE_ERR_NULL_PTR;
+  if (hidden < 1) return MOE_ERR_BAD_SHAPE;
+  return row_bytes(hidden, recv, bytes);
+}
+
+int moe_layout_workspace_bytes(int32_t bs, int32_t topk, int32_t num_experts, size_t* bytes) {
+  if (!bytes) return MOE_ERR_NULL_PTR;
+  int st = check_tokens(bs, topk);
+  if (st) return st;
+  if (num_experts < 1) return MOE_ERR_BAD_SHAPE;
+  if (num_experts > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  *bytes = moe::layout_workspace_bytes(static_cast<int64_t>(bs) * topk, num_experts);
+  return MOE_OK;
+}
+
+int moe_layout(const int32_t* topk_idx, int32_t bs, int32_t topk, int32_t epr, int32_t ranks,
+               int32_t* token_per_expert, int32_t* token_per_rank, int32_t* send_token_idx,
+               int32_t* bad_id_count, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_tokens(bs, topk);
+  if (st) return st;
+  if ((st = check_experts(epr, ranks))) return st;
+  if (!token_per_expert || !token_per_rank) return MOE_ERR_NULL_PTR;
+  if (bs > 0 && (!topk_idx || !send_token_idx)) return MOE_ERR_NULL_PTR;
+  const int32_t e = epr * ranks;
+  const int64_t n = static_cast<int64_t>(bs) * topk;
+  const size_t need = moe::layout_workspace_bytes(n, e);
+  if (workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && !workspace) return MOE_ERR_NULL_PTR;
+  if (!aligned(workspace, 4) || !aligned(token_per_expert, 4) || !aligned(token_per_rank, 4) ||
+      !aligned(send_token_idx, 4) || !aligned(topk_idx, 4) || !aligned(bad_id_count, 4))
+    return MOE_ERR_BAD_ALIGN;
+  return hip_status(moe::launch_layout(topk_idx, static_cast<int32_t>(n), e, epr, ranks,
+                                       token_per_expert, token_per_rank, send_token_idx,
+                                       bad_id_count, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int moe_notify(const int32_t* token_per_expert, int32_t epr, int32_t ranks, int32_t* put_offset,
+               int32_t* recv_count, int32_t* recv_base, int32_t* recv_token_per_expert,
+               void* stream) {
+  int st = check_experts(epr, ranks);
+  if (st) return st;
+  if (!token_per_expert || !put_offset || !recv_count || !recv_base || !recv_token_per_expert)
+    return MOE_ERR_NULL_PTR;
+  if (!aligned(token_per_expert, 4) || !aligned(put_offset, 4) || !aligned(recv_count, 4) ||
+      !aligned(recv_base, 4) || !aligned(recv_token_per_expert, 4))
+    return MOE_ERR_BAD_ALIGN;
+  return hip_status(moe::launch_notify(token_per_expert, epr, ranks, put_offset, recv_count,
+                                       recv_base, recv_token_per_expert,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int moe_dispatch(const void* x, moe_dtype x_type, int32_t bs, int32_t hidden, int32_t topk,
+                 const int32_t* topk_idx, const int32_t* send_token_idx, const int32_t* put_offset,
+                 const int32_t* recv_base, int32_t epr, int32_t ranks, int quant_int8,
+                 void* recv_x, size_t recv_x_bytes, void* stream) {
+  if (x_type != MOE_BF16 && x_type != MOE_FP16) return MOE_ERR_BAD_DTYPE;
+  if (quant_int8 != 0 && quant_int8 != 1) return MOE_ERR_BAD_DTYPE;
+  const moe_dtype recv_type = quant_int8 ? MOE_INT8_ROWSCALE : x_type;
+  moe::RouteArgs r{};
+  int st = make_route(bs, hidden, topk, topk_idx, send_token_idx, put_offset, recv_base, epr, ranks,
+                      recv_type, recv_x_bytes, &r);
+  if (st) return st;
+  if (bs == 0) return MOE_OK;
+  if (!x || !recv_x) return MOE_ERR_NULL_PTR;
+  if (!aligned(x, 16) || !aligned(recv_x, 16)) return MOE_ERR_BAD_ALIGN;
+  return hip_status(moe::launch_dispatch(r, x, x_type == MOE_FP16 ? moe::Half::kFp16 : moe::Half::kBf16,
+                                         quant_int8 != 0, recv_x, static_cast<hipStream_t>(stream)));
+}
+
+int moe_combine(const void* recv_x, moe_dtype recv_type, size_t recv_x_bytes, int32_t bs,
+                int32_t hidden, int32_t topk, const int32_t* topk_idx, const float* topk_weights,
+                const int32_t* send_token_idx, const int32_t* put_offset, const int32_t* recv_base,
+                int32_t epr, int32_t ranks, void* out, moe_dtype out_type, void* stream) {
+  if (recv_type != MOE_BF16 && recv_type != MOE_FP16 && recv_type != MOE_INT8_ROWSCALE)
+    return MOE_ERR_BAD_DTYPE;
+  if (out_type != MOE_BF16 && out_type != MOE_FP16 && out_type != MOE_FP32) return MOE_ERR_BAD_DTYPE;
+  moe::RouteArgs r{};
+  int st = make_route(bs, hidden, topk, topk_idx, send_token_idx, put_offset, recv_base, epr, ranks,
+                      recv_type, recv_x_bytes, &r);
+  if (st) return st;
+  if (bs == 0) return MOE_OK;
+  if (!recv_x || !out || !topk_weights) return MOE_ERR_NULL_PTR;
+  if (!aligned(recv_x, 16) || !aligned(out, 16) || !aligned(topk_weights, 4)) return MOE_ERR_BAD_ALIGN;
+  const moe::Recv rt = recv_type == MOE_INT8_ROWSCALE ? moe::Recv::kInt8
+                       : recv_type == MOE_FP16        ? moe::Recv::kFp16
+                                                      : moe::Recv::kBf16;
+  const moe::Out ot = out_type == MOE_FP32 ? moe::Out::kF32
+                      : out_type == MOE_FP16 ? moe::Out::kFp16
+                                             : moe::Out::kBf16;
+  return hip_status(moe::launch_combine(r, recv_x, rt, topk_weights, out, ot,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL_PTR: return "a required pointer is NULL";
+    case MOE_ERR_BAD_SHAPE: return "bad shape (a size is out of range)";
+    case MOE_ERR_BAD_ALIGN: return "pointer not aligned (16 bytes for rows, 4 for index arrays)";
+    case MOE_ERR_BAD_DTYPE: return "unsupported element type for this argument";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than moe_layout_workspace_bytes()";
+    case MOE_ERR_BUFFER_TOO_SMALL: return "receive buffer smaller than bs * topk rows";
+    case MOE_ERR_UNSUPPORTED: return "size not supported by this build (see MOE_MAX_* and hidden % 8)";
+    case MOE_ERR_HIP: return "HIP launch failed (see moe_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Kernel launchers of libmoe_ep.  Arguments are validated by the C entry
+// points (api.hip) before any of these is called; each launcher only
+// enqueues work on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- layout -------------------------------------------------------------------
+// Entries are processed in tiles of kLayoutTile flat (token, k) entries; a
+// tile is one 256-thread workgroup whose four waves each own a contiguous
+// quarter, walked in rounds of 64 entries.
+constexpr int kLayoutThreads = 256;
+constexpr int kLayoutRounds = 8;
+constexpr int kLayoutSegment = kLayoutRounds * 64;                    // entries per wave
+constexpr int kLayoutTile = (kLayoutThreads / 64) * kLayoutSegment;  // 2048
+
+inline int64_t layout_num_tiles(int64_t n) { return n <= 0 ? 1 : (n + kLayoutTile - 1) / kLayoutTile; }
+// Workspace: per-tile expert counts plus a bad-id count for every tile but
+// the last (the last tile's workgroup counts its own entries).
+inline size_t layout_workspace_bytes(int64_t n, int64_t num_experts) {
+  return static_cast<size_t>(layout_num_tiles(n) - 1) * static_cast<size_t>(num_experts + 1) * 4u;
+}
+
+hipError_t launch_layout(const int32_t* topk_idx, int32_t n, int32_t num_experts, int32_t epr,
+                         int32_t ranks, int32_t* token_per_expert, int32_t* token_per_rank,
+                         int32_t* send_token_idx, int32_t* bad_count, void* workspace,
+                         hipStream_t stream);
+
+// ---- notify -------------------------------------------------------------------
+hipError_t launch_notify(const int32_t* token_per_expert, int32_t epr, int32_t ranks,
+                         int32_t* put_offset, int32_t* recv_count, int32_t* recv_base,
+                         int32_t* recv_token_per_expert, hipStream_t stream);
+
+// ---- dispatch / combine ---------------------------------------------------------
+struct RouteArgs {
+  const int32_t* topk_idx;        // [bs, k]
+  const int32_t* send_token_idx;  // [bs, k]
+  const int32_t* put_offset;      // [E]
+  const int32_t* recv_base;       // [R]
+  int32_t bs, hidden, k, epr, num_experts;
+  int64_t row_bytes;   // bytes per receive row
+  int64_t cap_rows;    // rows that fit in the receive buffer
+  int32_t scale_off;   // byte offset of the inverse scale in an int8 row
+};
+
+enum class Half { kBf16 = 0, kFp16 = 1 };
+enum class Recv { kBf16 = 0, kFp16 = 1, kInt8 = 2 };
+enum class Out { kBf16 = 0, kFp16 = 1, kF32 = 2 };
+
+hipError_t launch_dispatch(const RouteArgs& r, const void* x, Half x_type, bool quant,
+                           void* recv_x, hipStream_t stream);
+
+hipError_t launch_combine(const RouteArgs& r, const void* recv_x, Recv recv_type,
+                          const float* topk_w, void* out, Out out_type, hipStream_t stream);
+
+}  // namespace moe

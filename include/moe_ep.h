@@ -1,0 +1,177 @@
+/*
+ * moe_ep.h -- C ABI of the MoE expert-parallel dispatch/combine library
+ * (libmoe_ep.so, HIP kernels for gfx950 / MI355X).
+ *
+ * The four entry points are the four stages of the "EP normal" pipeline
+ * described on the page "UMDK/CAM communication acceleration library deep
+ * analysis v2", section 2 (2.1 gives the stage order):
+ *
+ *   moe_layout   -- 2.3 moe_dispatch_layout_zb
+ *   moe_notify   -- 2.4 moe_notify_dispatch_zb
+ *   moe_dispatch -- 2.5 moe_dispatch_normal_zb (with QuantProcess)
+ *   moe_combine  -- 2.6 moe_combine_normal_zb (ReadBufferAndWeightedSum)
+ *
+ * Scalars follow the page's CommArgs (2.2.1): batch size bs, hidden size h,
+ * topk k, expertNumPerRank EPR and rankSize R; E = R * EPR experts and the
+ * destination rank of expert e is e / EPR.
+ *
+ * Single device.  The R ranks are logical: their receive regions are
+ * concatenated, in rank order, inside one device buffer.  Region r starts at
+ * row recvBase[r]; inside it expert e's rows start at putOffset[e] and are
+ * ordered by send slot (token order).  Row r of the receive buffer lives at
+ * byte offset r * moe_recv_row_bytes(h, type).
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as device pointers must point to device memory (or to
+ *    memory the device can address); the library never allocates, frees or
+ *    keeps device memory, and keeps no state between calls.
+ *  - Arrays are dense, row-major, in the element types given below.
+ *  - Work is only enqueued on `stream` (a hipStream_t; NULL means the null
+ *    stream) and the call returns without waiting.  Stage order on one stream
+ *    replaces the page's SyncAll / BarrierAll between stages.
+ *  - Argument errors (NULL pointer, bad shape, alignment, dtype, buffer too
+ *    small, unsupported size) are found on the host before anything is
+ *    enqueued; the call then returns the error code and enqueues nothing.
+ *    MOE_ERR_HIP means a launch failed (see moe_last_hip_error()).
+ *  - Calls on different streams that share output buffers race; the library
+ *    has no global state, so calls on different buffers may run concurrently.
+ */
+#ifndef MOE_EP_H
+#define MOE_EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+typedef enum {
+  MOE_BF16 = 0,          /* bfloat16 */
+  MOE_FP16 = 1,          /* IEEE binary16 */
+  MOE_FP32 = 2,          /* IEEE binary32 (combine output only) */
+  MOE_INT8_ROWSCALE = 3  /* int8 codes + float inverse scale per row (receive buffer) */
+} moe_dtype;
+
+/* Status codes. */
+enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL_PTR = 1,
+  MOE_ERR_BAD_SHAPE = 2,
+  MOE_ERR_BAD_ALIGN = 3,
+  MOE_ERR_BAD_DTYPE = 4,
+  MOE_ERR_WORKSPACE_TOO_SMALL = 5,
+  MOE_ERR_BUFFER_TOO_SMALL = 6,
+  MOE_ERR_UNSUPPORTED = 7,
+  MOE_ERR_HIP = 8
+};
+
+/* Limits of this build. */
+#define MOE_MAX_EXPERTS 2048   /* E = R * EPR */
+#define MOE_MAX_HIDDEN 16384   /* h */
+#define MOE_MAX_TOPK 32        /* k */
+
+/* Bytes of one receive-buffer row for hidden size `hidden` and receive type
+ * `recv` (page 2.5 and 2.2.1):
+ *   MOE_BF16, MOE_FP16:   2 * hidden (the row as is);
+ *   MOE_INT8_ROWSCALE:    align32(hidden) + 32 -- int8 codes at bytes
+ *                         [0, hidden), the float inverse scale 1/s at byte
+ *                         align32(hidden) (UB_ALIGN_SIZE = 32), the other
+ *                         bytes are padding with unspecified contents.
+ * Host only; writes *bytes.  Errors: NULL_PTR, BAD_SHAPE (hidden < 1),
+ * BAD_DTYPE. */
+int moe_recv_row_bytes(int32_t hidden, moe_dtype recv, size_t* bytes);
+
+/* Device workspace that moe_layout needs for `bs` tokens, `topk` entries per
+ * token and `numExperts` experts (a per-tile count table).  May be 0, in
+ * which case moe_layout accepts a NULL workspace.  Host only. */
+int moe_layout_workspace_bytes(int32_t bs, int32_t topk, int32_t numExperts, size_t* bytes);
+
+/* Stage 1, dispatch layout (page 2.3).
+ * In:  topkIdx        device int32 [bs, topk], expert id of each (token, k)
+ *                     entry; ids outside [0, E) are "bad".
+ * Out: tokenPerExpert device int32 [E]: entries routed to each expert.
+ *      tokenPerRank   device int32 [R]: rows each logical rank receives
+ *                     (sum of tokenPerExpert over its EPR experts).
+ *      sendTokenIdx   device int32 [bs, topk]: the entry's slot inside its
+ *                     expert's region = the number of earlier entries (flat
+ *                     t*topk + j order) with the same expert; -1 for bad ids.
+ *      badIdCount     device int32 [1] or NULL: number of bad entries.
+ * workspace: device memory of at least moe_layout_workspace_bytes(...) bytes,
+ * 4-byte aligned; contents on entry do not matter.
+ * bs may be 0 (outputs are still written).  Deterministic: the result does
+ * not depend on scheduling. */
+int moe_layout(const int32_t* topkIdx, int32_t bs, int32_t topk, int32_t expertNumPerRank,
+               int32_t rankSize, int32_t* tokenPerExpert, int32_t* tokenPerRank,
+               int32_t* sendTokenIdx, int32_t* badIdCount, void* workspace,
+               size_t workspaceBytes, void* stream);
+
+/* Stage 2, notify (page 2.4).  With a single source the page's all-gather of
+ * tokenPerExpert is the identity and the prefix sums remain:
+ * In:  tokenPerExpert     device int32 [E] (from moe_layout).
+ * Out: putOffset          device int32 [E]: start of expert e's rows inside
+ *                         its rank's region (exclusive scan over the rank's
+ *                         experts in id order).
+ *      recvCount          device int32 [R]: rows in rank r's region.
+ *      recvBase           device int32 [R]: first row of rank r's region
+ *                         (exclusive scan of recvCount).
+ *      recvTokenPerExpert device int32 [E]: rows each expert receives. */
+int moe_notify(const int32_t* tokenPerExpert, int32_t expertNumPerRank, int32_t rankSize,
+               int32_t* putOffset, int32_t* recvCount, int32_t* recvBase,
+               int32_t* recvTokenPerExpert, void* stream);
+
+/* Stage 3, dispatch (page 2.5).  Entry (t, j) with a valid id e and slot
+ * s >= 0 writes token t's row to receive row
+ *     recvBase[e / EPR] + putOffset[e] + s.
+ * In:  x         device [bs, hidden] of xType (MOE_BF16 or MOE_FP16), 16-byte
+ *                aligned.
+ *      topkIdx, sendTokenIdx  device int32 [bs, topk] (from moe_layout).
+ *      putOffset device int32 [E], recvBase device int32 [R] (from moe_notify).
+ *      quantInt8 0: rows are copied as is (receive type = xType);
+ *                1: rows are quantised (receive type MOE_INT8_ROWSCALE):
+ *                   s = 127 / (max|x_t| + 1e-12), codes = round-half-even
+ *                   (x * s) in binary32, inverse scale 1/s stored after the
+ *                   codes (correctly rounded binary32 divisions).
+ * Out: recvX     device buffer of recvXBytes bytes, 16-byte aligned; needs
+ *                bs * topk rows of moe_recv_row_bytes(hidden, recvType).
+ * Entries whose row would fall outside recvXBytes are skipped.  Requires
+ * hidden % 8 == 0 and hidden <= MOE_MAX_HIDDEN (else MOE_ERR_UNSUPPORTED). */
+int moe_dispatch(const void* x, moe_dtype xType, int32_t bs, int32_t hidden, int32_t topk,
+                 const int32_t* topkIdx, const int32_t* sendTokenIdx, const int32_t* putOffset,
+                 const int32_t* recvBase, int32_t expertNumPerRank, int32_t rankSize,
+                 int quantInt8, void* recvX, size_t recvXBytes, void* stream);
+
+/* Stage 4, combine (page 2.6).  For each token t and element i:
+ *     acc = +0.0f
+ *     for j = 0 .. topk-1 with a valid id and slot (row as in dispatch):
+ *         v   = float(row[i])                (MOE_BF16 / MOE_FP16 rows)
+ *            or float(code[i]) * inv(row)    (MOE_INT8_ROWSCALE rows)
+ *         acc = acc + v * topkWeights[t, j]  (multiply and add rounded apart)
+ *     out[t, i] = acc, rounded half-even to outType.
+ * The result is bit-identical to that sequential binary32 definition.
+ * In:  recvX       device receive buffer of recvType, recvXBytes bytes,
+ *                  16-byte aligned; rows outside it contribute nothing.
+ *      topkIdx, sendTokenIdx device int32 [bs, topk]; topkWeights device
+ *                  float [bs, topk]; putOffset [E], recvBase [R] as above.
+ * Out: out         device [bs, hidden] of outType (MOE_BF16, MOE_FP16 or
+ *                  MOE_FP32), 16-byte aligned.
+ * Requires hidden % 8 == 0 and hidden <= MOE_MAX_HIDDEN. */
+int moe_combine(const void* recvX, moe_dtype recvType, size_t recvXBytes, int32_t bs,
+                int32_t hidden, int32_t topk, const int32_t* topkIdx, const float* topkWeights,
+                const int32_t* sendTokenIdx, const int32_t* putOffset, const int32_t* recvBase,
+                int32_t expertNumPerRank, int32_t rankSize, void* out, moe_dtype outType,
+                void* stream);
+
+/* Text for a status code (static storage). */
+const char* moe_status_str(int status);
+
+/* The hipError_t value of the last MOE_ERR_HIP returned on this thread
+ * (0 if none). */
+int moe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EP_H */

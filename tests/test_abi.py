@@ -1,0 +1,153 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/moe_ep.h declares, and rejects bad arguments on the host (these
+paths return before any HIP call, so they run anywhere)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_ep.h")
+
+
+@pytest.fixture(scope="module")
+def M():
+    import combine_moe_layout_03_amd as mod
+
+    return mod
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(M):
+    names = declared_functions()
+    assert {"moe_layout", "moe_notify", "moe_dispatch", "moe_combine"} <= set(names)
+    lib = ctypes.CDLL(M.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in moe_ep.h but not exported"
+
+
+def test_header_constants_match_binding(M):
+    text = open(HEADER).read()
+    for name in ("MOE_MAX_EXPERTS", "MOE_MAX_HIDDEN", "MOE_MAX_TOPK"):
+        val = int(re.search(rf"#define {name} (\d+)", text).group(1))
+        assert getattr(M, name) == val
+
+
+@pytest.mark.parametrize("hidden,dtype,expect", [(7168, 3, 7200), (1000, 3, 1056), (8, 3, 64),
+                                                 (8, 0, 16), (7168, 1, 14336)])
+def test_recv_row_bytes(M, hidden, dtype, expect):
+    assert M.moe_recv_row_bytes(hidden, dtype) == expect
+
+
+def test_recv_row_bytes_errors(M):
+    out = ctypes.c_size_t(0)
+    assert M._lib.moe_recv_row_bytes(0, 0, ctypes.byref(out)) == 2
+    assert M._lib.moe_recv_row_bytes(8, 2, ctypes.byref(out)) == 4   # fp32 is not a receive type
+    assert M._lib.moe_recv_row_bytes(8, 0, None) == 1
+
+
+@pytest.mark.parametrize("bs,k,e,expect", [(4096, 8, 256, 15 * 257 * 4), (0, 1, 1, 0), (256, 8, 16, 0),
+                                           (257, 8, 16, 17 * 4), (16384, 8, 256, 63 * 257 * 4)])
+def test_layout_workspace_bytes(M, bs, k, e, expect):
+    assert M.moe_layout_workspace_bytes(bs, k, e) == expect
+
+
+def test_status_strings(M):
+    for s in range(9):
+        assert M.moe_status_str(s) and M.moe_status_str(s) != "unknown status"
+    assert M.moe_status_str(99) == "unknown status"
+
+
+P = 0x100000  # a non-NULL, 256-byte aligned stand-in pointer (never dereferenced: every call below fails validation)
+
+
+def test_layout_rejects_on_host(M):
+    L = M._lib
+    ws = M.moe_layout_workspace_bytes(4096, 8, 256)
+    assert L.moe_layout(P, -1, 8, 16, 16, P, P, P, None, P, ws, None) == 2
+    assert L.moe_layout(P, 16, 0, 16, 16, P, P, P, None, P, ws, None) == 2
+    assert L.moe_layout(P, 16, 33, 16, 16, P, P, P, None, P, ws, None) == 7
+    assert L.moe_layout(P, 16, 8, 0, 16, P, P, P, None, P, ws, None) == 2
+    assert L.moe_layout(P, 16, 8, 2049, 1, P, P, P, None, P, ws, None) == 7
+    assert L.moe_layout(P, 16, 8, 16, 16, None, P, P, None, P, ws, None) == 1
+    assert L.moe_layout(None, 16, 8, 16, 16, P, P, P, None, P, ws, None) == 1
+    assert L.moe_layout(P, 4096, 8, 16, 16, P, P, P, None, P, ws - 4, None) == 5
+    assert L.moe_layout(P, 4096, 8, 16, 16, P, P, P, None, None, ws, None) == 1
+    assert L.moe_layout(P + 2, 16, 8, 16, 16, P, P, P, None, P, ws, None) == 3
+    assert L.moe_layout(P, 16, 8, 16, 16, P, P, P, P + 1, P, ws, None) == 3
+
+
+def test_notify_rejects_on_host(M):
+    L = M._lib
+    assert L.moe_notify(P, 0, 4, P, P, P, P, None) == 2
+    assert L.moe_notify(P, 4, 1024, P, P, P, P, None) == 7
+    assert L.moe_notify(None, 4, 4, P, P, P, P, None) == 1
+    assert L.moe_notify(P, 4, 4, P, P, None, P, None) == 1
+    assert L.moe_notify(P, 4, 4, P + 2, P, P, P, None) == 3
+
+
+def test_dispatch_rejects_on_host(M):
+    L = M._lib
+    rb = M.moe_recv_row_bytes(7168, 3)
+    cap = 4096 * 8 * rb
+    args = lambda **kw: [kw.get("x", P), kw.get("xt", 0), kw.get("bs", 4096), kw.get("h", 7168),
+                         kw.get("k", 8), kw.get("idx", P), P, P, P, 16, 16, kw.get("q", 1),
+                         kw.get("recv", P), kw.get("cap", cap), None]
+    assert L.moe_dispatch(*args(xt=2)) == 4        # fp32 input
+    assert L.moe_dispatch(*args(q=2)) == 4         # quant flag not 0/1
+    assert L.moe_dispatch(*args(h=7164)) == 7      # hidden % 8
+    assert L.moe_dispatch(*args(h=16392)) == 7     # hidden > max
+    assert L.moe_dispatch(*args(h=0)) == 2
+    assert L.moe_dispatch(*args(k=0)) == 2
+    assert L.moe_dispatch(*args(cap=cap - 1)) == 6
+    assert L.moe_dispatch(*args(x=None)) == 1
+    assert L.moe_dispatch(*args(idx=None)) == 1
+    assert L.moe_dispatch(*args(x=P + 8)) == 3
+    assert L.moe_dispatch(*args(recv=P + 4)) == 3
+    # passthrough needs 2*h bytes per row
+    assert L.moe_dispatch(*args(q=0, cap=cap)) == 6
+    # an empty batch is accepted with NULL pointers and enqueues nothing
+    assert L.moe_dispatch(*args(bs=0, x=None, idx=None, recv=None, cap=0)) == 0
+
+
+def test_combine_rejects_on_host(M):
+    L = M._lib
+    rb = M.moe_recv_row_bytes(7168, 3)
+    cap = 4096 * 8 * rb
+    args = lambda **kw: [kw.get("recv", P), kw.get("rt", 3), kw.get("cap", cap), kw.get("bs", 4096),
+                         kw.get("h", 7168), 8, P, kw.get("w", P), P, P, P, 16, 16, kw.get("out", P),
+                         kw.get("ot", 0), None]
+    assert L.moe_combine(*args(rt=2)) == 4
+    assert L.moe_combine(*args(ot=3)) == 4
+    assert L.moe_combine(*args(cap=cap - 32)) == 6
+    assert L.moe_combine(*args(w=None)) == 1
+    assert L.moe_combine(*args(out=P + 2)) == 3
+    assert L.moe_combine(*args(h=12)) == 7
+    assert L.moe_combine(*args(bs=0, recv=None, out=None, w=None, cap=0)) == 0
+
+
+def test_binding_rejects_host_tensors(M):
+    import torch
+
+    idx = torch.zeros((4, 2), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        M.moe_layout(idx, 2, 2, torch.zeros(4, dtype=torch.int32), torch.zeros(2, dtype=torch.int32),
+                     torch.zeros((4, 2), dtype=torch.int32))
+
+
+def test_product_path_never_touches_the_oracle():
+    """Nothing in the package or the header refers to the CPU oracle."""
+    pkg = os.path.join(ROOT, "combine_moe_layout_03_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f"{f} mentions the oracle"
+    assert "oracle" not in open(HEADER).read().lower()

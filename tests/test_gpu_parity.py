@@ -1,0 +1,305 @@
+"""HIP library vs CPU oracle, element by element, through the C ABI.
+
+Bar: counts, offsets, send slots, receive rows, int8 codes and inverse
+scales bit-exact; combine outputs bit-exact too (the kernel keeps the
+sequential binary32 order with separate roundings).  The looser float
+tolerance of the method statement (1e-5 relative for fp32 output, 1 ulp for
+bf16/fp16 output, relative to sum_j |v_j w_j|) is also asserted, so a
+failure says which bar broke.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pins
+import workloads as W
+from gpu_util import GpuRun, dev_f32, dev_half, dev_i32, host_bits, log, pack_recv, unpack_recv
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X")
+
+
+_WL = {}
+
+
+def workload(name, kind="bf16"):
+    key = (name, kind)
+    if key not in _WL:
+        _WL[key] = W.make_workload(name, x_dtype=kind)
+    return _WL[key]
+
+
+def oracle_run(w, quant, out_kind):
+    return oracle.pipeline(w.x, w.x_dtype, w.topk_idx, w.topk_w, w.expert_num_per_rank,
+                           w.rank_size, quant, out_kind)
+
+
+def widen(bits, kind):
+    return pins.widen16(bits, kind).astype(np.float64)
+
+
+def assert_close_tolerance(got, exp, out_kind, scale):
+    """The method statement's float bar: fp32 within 1e-5 of sum|v w|;
+    16-bit outputs within one ulp of the output type."""
+    if out_kind == "fp32":
+        err = np.abs(got.astype(np.float64) - exp.astype(np.float64))
+        assert np.all(err <= 1e-5 * scale + 1e-30), float(err.max())
+    else:
+        g = got.view(np.int16).astype(np.int32)
+        e = exp.view(np.int16).astype(np.int32)
+        # adjacent patterns of the same sign differ by one ulp
+        assert np.all(np.abs(g - e) <= 1) or np.array_equal(widen(got, out_kind), widen(exp, out_kind))
+
+
+def compare(w, quant, out_kind, g, o, check_out=True):
+    lay, no, dis = o["layout"], o["notify"], o["dispatch"]
+    np.testing.assert_array_equal(g["token_per_expert"], lay["token_per_expert"])
+    np.testing.assert_array_equal(g["token_per_rank"], lay["token_per_rank"])
+    np.testing.assert_array_equal(g["send_token_idx"], lay["send_token_idx"])
+    assert g["bad"] == lay["bad"]
+    for k in ("put_offset", "recv_count", "recv_base", "recv_token_per_expert"):
+        np.testing.assert_array_equal(g[k], no[k], err_msg=k)
+    total = w.bs * w.topk - lay["bad"]
+    if quant:
+        np.testing.assert_array_equal(g["recv"]["codes"][:total], dis["codes"][:total])
+        np.testing.assert_array_equal(g["recv"]["inv"][:total].view(np.uint32),
+                                      dis["inv"][:total].view(np.uint32))
+        assert not g["recv"]["codes"][total:].any(), "rows past the total were written"
+    else:
+        np.testing.assert_array_equal(g["recv"]["rows"][:total], dis["rows"][:total])
+        assert not g["recv"]["rows"][total:].any(), "rows past the total were written"
+    if check_out:
+        exp = o["out"]
+        got = g["out"]
+        if out_kind == "fp32":
+            np.testing.assert_array_equal(got.view(np.uint32), exp.view(np.uint32))
+        else:
+            np.testing.assert_array_equal(got, exp)
+
+
+CONFIG_CASES = [
+    ("tiny", "bf16", False, None),
+    ("small", "bf16", True, None),
+    ("small", "bf16", True, "fp32"),
+    ("mid", "bf16", False, None),
+    ("mid", "fp16", False, None),
+    ("mid", "bf16", True, None),
+    ("mid", "fp16", True, None),
+    ("mid", "bf16", True, "fp32"),
+]
+
+
+@pytest.mark.parametrize("name,kind,quant,out_kind", CONFIG_CASES)
+def test_pipeline_configs(name, kind, quant, out_kind):
+    w = workload(name, kind)
+    out_kind = out_kind or kind
+    log(f"pipeline {name} {kind} quant={quant} out={out_kind}")
+    g = GpuRun(w, quant, out_kind).run_all().host()
+    o = oracle_run(w, quant, out_kind)
+    compare(w, quant, out_kind, g, o)
+
+
+@pytest.mark.parametrize("name,quant", [("large", True), ("large", False), ("stress", True)])
+def test_pipeline_full_size(name, quant):
+    """The full headline shapes, whole outputs compared, in the launch
+    configuration the benchmark times (same entry points, same buffers)."""
+    w = workload(name)
+    log(f"full-size pipeline {name} quant={quant}")
+    g = GpuRun(w, quant).run_all().host()
+    o = oracle_run(w, quant, "bf16")
+    compare(w, quant, "bf16", g, o)
+
+
+RANDOM_CASES = [
+    # seed, bs, h, k, E, R, routing, bad, kind, quant
+    (101, 1, 8, 1, 1, 1, "uniform", 0.0, "bf16", True),
+    (102, 3, 136, 2, 4, 2, "dup", 0.0, "bf16", False),
+    (103, 37, 1000, 3, 12, 3, "dup", 0.1, "bf16", True),
+    (104, 256, 64, 8, 1, 1, "hot", 0.0, "bf16", True),
+    (105, 512, 64, 4, 8, 8, "hot", 0.0, "fp16", False),
+    (106, 300, 256, 8, 2048, 16, "uniform", 0.0, "bf16", True),
+    (107, 64, 128, 32, 64, 4, "dup", 0.05, "bf16", True),
+    (108, 5, 16384, 3, 8, 2, "uniform", 0.0, "bf16", True),
+    (109, 5, 16384, 3, 8, 2, "uniform", 0.0, "fp16", False),
+    (110, 256, 96, 8, 32, 4, "zipf1.2", 0.0, "fp16", True),
+    (111, 257, 40, 8, 16, 4, "dup", 0.0, "bf16", True),      # n = 2056: one full tile + ragged
+    (112, 512, 40, 4, 16, 4, "dup", 0.0, "bf16", False),     # n = 2048: exactly one tile
+    (113, 4100, 24, 8, 64, 8, "dup", 0.2, "bf16", True),     # 17 tiles, bad ids across tiles
+    (114, 33, 72, 5, 7, 7, "dup", 0.0, "fp16", True),
+]
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=[str(c[0]) for c in RANDOM_CASES])
+def test_pipeline_random(case):
+    seed, bs, h, k, e, r, routing, bad, kind, quant = case
+    w = W.random_case(seed, bs, h, k, e, r, x_dtype=kind, routing=routing, bad_frac=bad,
+                      zero_rows=1 if bs > 1 else 0, x_std=1e-5 if kind == "fp16" and seed == 110 else 1.0)
+    for out_kind in ([kind, "fp32"] if seed % 2 else [kind]):
+        log(f"random case {case} out={out_kind}")
+        g = GpuRun(w, quant, out_kind).run_all().host()
+        o = oracle_run(w, quant, out_kind)
+        compare(w, quant, out_kind, g, o)
+
+
+@pytest.mark.parametrize("recv_kind,out_kind", [("bf16", "bf16"), ("bf16", "fp32"), ("int8", "bf16"),
+                                                ("int8", "fp32"), ("fp16", "fp16"), ("int8", "fp16")])
+def test_combine_on_oracle_buffer(recv_kind, out_kind):
+    """Combine alone, on a receive buffer the oracle side made (rows that all
+    differ, as after a real expert), so a permuted weight or a wrong row would
+    show even where dispatch copies are identical."""
+    import combine_moe_layout_03_amd as M
+
+    bs, h, k, e, r = 77, 264, 6, 24, 4
+    w = W.random_case(9, bs, h, k, e, r, routing="dup", bad_frac=0.05)
+    epr = e // r
+    lay = oracle.layout(w.topk_idx, epr, r)
+    no = oracle.notify(lay["token_per_expert"], epr, r)
+    canon = pins.random_receive_buffer(10, bs * k, h, recv_kind)
+    exp = oracle.combine(canon, recv_kind, w.topk_idx, w.topk_w, lay["send_token_idx"],
+                         no["put_offset"], no["recv_base"], epr, r, out_kind)
+    log(f"combine on oracle buffer {recv_kind}->{out_kind}")
+    recv = torch.from_numpy(pack_recv(canon, h, recv_kind)).cuda()
+    out_dtype = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[out_kind]
+    out = torch.zeros((bs, h), dtype=out_dtype, device="cuda")
+    rtype = {"bf16": M.MOE_BF16, "fp16": M.MOE_FP16, "int8": M.MOE_INT8_ROWSCALE}[recv_kind]
+    M.moe_combine(recv, rtype, h, dev_i32(w.topk_idx), dev_f32(w.topk_w), dev_i32(lay["send_token_idx"]),
+                  dev_i32(no["put_offset"]), dev_i32(no["recv_base"]), epr, r, out)
+    got = out.cpu().numpy() if out_kind == "fp32" else host_bits(out)
+    terms = pins.combine_terms(canon, recv_kind, w.topk_idx, w.topk_w, lay["send_token_idx"],
+                               no["put_offset"], no["recv_base"], epr)
+    assert_close_tolerance(got, exp, out_kind, np.abs(terms).sum(axis=1))
+    if out_kind == "fp32":
+        np.testing.assert_array_equal(got.view(np.uint32), exp.view(np.uint32))
+    else:
+        np.testing.assert_array_equal(got, exp)
+
+
+def test_combine_golden_rows_on_gpu():
+    """The hand-worked order-sensitive rows of tests/golden/combine_order.json."""
+    import combine_moe_layout_03_amd as M
+
+    g = pins.load_golden("combine_order.json")
+    for case in g["cases"]:
+        k = len(case["rows"])
+        idx, wts, rows = pins._one_token_case(case["rows"], case["weights"], h=8)
+        log(f"golden combine {case['name']}")
+        recv = torch.from_numpy(np.ascontiguousarray(rows).view(np.uint8).reshape(-1)).cuda()
+        slot = np.zeros((1, k), np.int32)
+        put = np.zeros(k, np.int32)
+        base = np.arange(k, dtype=np.int32)
+        for out_kind in ("fp32", "bf16"):
+            out_dtype = torch.float32 if out_kind == "fp32" else torch.bfloat16
+            out = torch.zeros((1, 8), dtype=out_dtype, device="cuda")
+            M.moe_combine(recv, M.MOE_BF16, 8, dev_i32(idx), dev_f32(wts), dev_i32(slot), dev_i32(put),
+                          dev_i32(base), 1, k, out)
+            if out_kind == "fp32":
+                assert np.all(out.cpu().numpy() == np.float32(case["out_fp32"])), case["name"]
+                assert pins.f32_bits(out.cpu().numpy()[0, 0]) == pins.f32_bits(np.float32(case["out_fp32"]))
+            elif "out_bf16_hex" in case:
+                assert np.all(host_bits(out) == int(case["out_bf16_hex"], 16)), case["name"]
+
+
+def test_quant_golden_rows_on_gpu():
+    """The hand-worked quantiser rows of tests/golden/quant_rows.json, each
+    padded with zeros to a multiple of 8 elements (zeros change no maximum)."""
+    import combine_moe_layout_03_amd as M
+
+    g = pins.load_golden("quant_rows.json")
+    for case in g["cases"]:
+        kind = case["x_kind"]
+        n = len(case["x"])
+        h = (n + 7) // 8 * 8
+        bits = np.zeros((1, h), np.uint16)
+        bits[0, :n] = pins.to_bits16(case["x"], kind)
+        log(f"golden quant {case['name']}")
+        idx = dev_i32(np.zeros((1, 1), np.int32))
+        slot = dev_i32(np.zeros((1, 1), np.int32))
+        zero1 = dev_i32(np.zeros(1, np.int32))
+        rb = M.moe_recv_row_bytes(h, M.MOE_INT8_ROWSCALE)
+        recv = torch.zeros(rb, dtype=torch.uint8, device="cuda")
+        M.moe_dispatch(dev_half(bits, kind), idx, slot, zero1, zero1, 1, 1, True, recv)
+        c = unpack_recv(recv, h, "int8")
+        assert c["codes"][0, :n].tolist() == case["codes"], case["name"]
+        assert not c["codes"][0, n:].any()
+        if case["scale_hex"] is not None:
+            assert pins.f32_bits(c["inv"][0]) == int(case["inv_hex"], 16), case["name"]
+        else:
+            _, exp_inv = pins.quant_expected(bits[0], kind)
+            assert pins.f32_bits(c["inv"][0]) == pins.f32_bits(exp_inv), case["name"]
+
+
+def test_identity_k1_unit_weight():
+    """k = 1, weight 1: combine returns the dequantised row exactly."""
+    w = W.random_case(201, 64, 512, 1, 8, 2, zero_rows=2)
+    w.topk_w[:] = 1.0
+    log("identity k=1")
+    g = GpuRun(w, True, "fp32").run_all().host()
+    rows = g["recv_base"][w.topk_idx[:, 0] // 4] + g["put_offset"][w.topk_idx[:, 0]] + g["send_token_idx"][:, 0]
+    deq = g["recv"]["codes"][rows].astype(np.float32) * g["recv"]["inv"][rows][:, None]
+    np.testing.assert_array_equal(g["out"].view(np.uint32), deq.astype(np.float32).view(np.uint32))
+    g2 = GpuRun(w, False, "bf16").run_all().host()
+    np.testing.assert_array_equal(g2["out"], w.x)
+
+
+def test_empty_batch():
+    import combine_moe_layout_03_amd as M
+
+    log("empty batch")
+    buf = M.EpBuffers(0, 64, 4, 2, 3, quant_int8=True)
+    buf.token_per_expert.fill_(7)
+    buf.token_per_rank.fill_(7)
+    buf.bad_id_count.fill_(7)
+    idx = torch.zeros((0, 4), dtype=torch.int32, device="cuda")
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    wts = torch.zeros((0, 4), dtype=torch.float32, device="cuda")
+    buf.recv_x = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    buf.layout(idx)
+    buf.notify()
+    buf.dispatch(x, idx)
+    buf.combine(idx, wts)
+    torch.cuda.synchronize()
+    assert buf.token_per_expert.cpu().tolist() == [0] * 6
+    assert buf.token_per_rank.cpu().tolist() == [0] * 3
+    assert buf.bad_id_count.item() == 0
+    assert buf.recv_base.cpu().tolist() == [0] * 3 and buf.put_offset.cpu().tolist() == [0] * 6
+
+
+def test_deterministic_repeat():
+    """Two runs of the same input give identical bytes everywhere."""
+    w = workload("mid")
+    log("determinism mid int8 x2")
+    a = GpuRun(w, True).run_all().host()
+    b = GpuRun(w, True).run_all().host()
+    for key in ("send_token_idx", "put_offset", "out"):
+        np.testing.assert_array_equal(a[key], b[key])
+    np.testing.assert_array_equal(a["recv"]["codes"], b["recv"]["codes"])
+
+
+def test_errors_enqueue_nothing():
+    """A call rejected on the host leaves its outputs untouched."""
+    import combine_moe_layout_03_amd as M
+
+    w = W.random_case(301, 16, 64, 2, 4, 2)
+    log("error paths")
+    run = GpuRun(w, True).layout().notify()
+    small = torch.full((100,), 9, dtype=torch.uint8, device="cuda")
+    with pytest.raises(M.MoeEpError) as ei:
+        M.moe_dispatch(run.x, run.idx, run.buf.send_token_idx, run.buf.put_offset, run.buf.recv_base,
+                       2, 2, True, small)
+    assert ei.value.status == 6
+    torch.cuda.synchronize()
+    assert torch.all(small == 9).item()
+    before = run.buf.token_per_expert.clone()
+    with pytest.raises(M.MoeEpError) as ei:
+        M.moe_layout(run.idx, 4096, 1, run.buf.token_per_expert, run.buf.token_per_rank,
+                     run.buf.send_token_idx, None, None)
+    assert ei.value.status == 7
+    torch.cuda.synchronize()
+    assert torch.equal(before, run.buf.token_per_expert)
