@@ -88,6 +88,7 @@ int make_route(int32_t bs, int32_t hidden, int32_t topk, const int32_t* topk_idx
   r->row_bytes = static_cast<int64_t>(rb);
   r->cap_rows = static_cast<int64_t>(recv_bytes / rb);
   r->scale_off = static_cast<int32_t>(align32(hidden));
+  r->epr_magic = moe::div_magic(epr);
   return MOE_OK;
 }
 

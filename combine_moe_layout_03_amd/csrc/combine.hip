@@ -1,16 +1,19 @@
 // Stage 4, combine ("UMDK/CAM communication acceleration library deep
 // analysis v2", section 2.6, moe_combine_normal_zb::ReadBufferAndWeightedSum).
 //
-// One wave per token.  The wave first resolves, in scalar registers, the
+// kWpt waves per token.  Each wave first resolves, in scalar registers, the
 // receive row, weight and (int8) inverse scale of each of the token's k
-// entries.  Then each lane walks chunks of eight elements: it issues the k
-// row loads of a chunk together, and folds them into eight binary32
+// entries.  Then each lane walks chunks of kElems elements of the row with
+// 16-byte loads, software-pipelined: the k row loads of the next chunk are
+// issued before the current chunk is summed, so loads and arithmetic
+// overlap inside every wave.  The loaded values are folded into binary32
 // accumulators in entry order j = 0..k-1, exactly as the page does:
 //   acc = +0; acc = acc + v_j * w_j  (v_j = float(row) or float(q) * inv)
 // with every multiply and add rounded separately (this file is compiled with
 // floating-point contraction off), so the result is bit-identical to the
 // sequential binary32 definition.  The sum is rounded half-even to the
-// output type.
+// output type (bf16: the hardware v_cvt_pk_bf16_f32 pair conversion) and
+// stored with 16-byte stores.
 #include "device_util.h"
 #include "launch.h"
 
@@ -20,124 +23,211 @@ namespace moe {
 namespace {
 
 constexpr int kCombineThreads = 256;
-constexpr int kTokensPerBlock = kCombineThreads / kWave;
 
 template <Recv kRecv>
-struct ChunkOf;
-template <>
-struct ChunkOf<Recv::kBf16> { using T = uint4; static constexpr int kBytes = 16; };
-template <>
-struct ChunkOf<Recv::kFp16> { using T = uint4; static constexpr int kBytes = 16; };
-template <>
-struct ChunkOf<Recv::kInt8> { using T = uint2; static constexpr int kBytes = 8; };
+constexpr int elem_bytes() {
+  return kRecv == Recv::kInt8 ? 1 : 2;
+}
 
-// Element e (0..7) of a loaded chunk, widened to binary32 (before the weight).
-template <Recv kRecv>
-__device__ __forceinline__ float element(const typename ChunkOf<kRecv>::T& c, int e, float inv) {
+// kElems elements of one row, as 32-bit words.
+template <Recv kRecv, int kElems>
+struct Chunk {
+  static constexpr int kWords = kElems * elem_bytes<kRecv>() / 4;
+  uint32_t w[kWords];
+};
+
+// Element e of a chunk, widened to binary32 and dequantised (before the weight).
+template <Recv kRecv, int kElems>
+__device__ __forceinline__ float element(const Chunk<kRecv, kElems>& c, int e, float inv) {
   if constexpr (kRecv == Recv::kInt8) {
-    const uint32_t w = e < 4 ? c.x : c.y;
+    const uint32_t w = c.w[e >> 2];
     const int8_t q = static_cast<int8_t>((w >> (8 * (e & 3))) & 0xffu);
     return static_cast<float>(q) * inv;
   } else {
-    const uint32_t w = e < 2 ? c.x : e < 4 ? c.y : e < 6 ? c.z : c.w;
+    const uint32_t w = c.w[e >> 1];
     const uint32_t b = (e & 1) ? (w >> 16) : (w & 0xffffu);
     return half_to_f32<kRecv == Recv::kFp16>(b);
   }
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two binary32 values -> two 16-bit patterns, round half to even.  For bf16
+// this is one v_cvt_pk_bf16_f32 (rounds in the default nearest-even mode).
 template <Out kOut>
-__device__ __forceinline__ void store_out(void* out, size_t elem_offset, const float (&acc)[8]) {
-  if constexpr (kOut == Out::kF32) {
-    float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + elem_offset);
-    p[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    p[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (kOut == Out::kBf16) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
   } else {
-    uint32_t w[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint32_t lo = kOut == Out::kBf16 ? f32_to_bf16(acc[2 * d]) : f32_to_f16(acc[2 * d]);
-      const uint32_t hi = kOut == Out::kBf16 ? f32_to_bf16(acc[2 * d + 1]) : f32_to_f16(acc[2 * d + 1]);
-      w[d] = lo | (hi << 16);
-    }
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + elem_offset) =
-        make_uint4(w[0], w[1], w[2], w[3]);
+    return f32_to_f16(a) | (f32_to_f16(b) << 16);
   }
 }
 
-template <Recv kRecv, Out kOut, int kMaxK>
+template <Out kOut, int kElems>
+__device__ __forceinline__ void store_out(void* out, size_t elem_offset, const float (&acc)[kElems]) {
+  if constexpr (kOut == Out::kF32) {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + elem_offset);
+#pragma unroll
+    for (int q = 0; q < kElems / 4; ++q)
+      p[q] = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+  } else {
+    uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + elem_offset);
+#pragma unroll
+    for (int q = 0; q < kElems / 8; ++q) {
+      p[q] = make_uint4(pack2<kOut>(acc[8 * q + 0], acc[8 * q + 1]), pack2<kOut>(acc[8 * q + 2], acc[8 * q + 3]),
+                        pack2<kOut>(acc[8 * q + 4], acc[8 * q + 5]), pack2<kOut>(acc[8 * q + 6], acc[8 * q + 7]));
+    }
+  }
+}
+
+// Global-memory pointers: loads through them compile to global_load (vmcnt
+// only), which lets the compiler wait for exactly the loads a chunk needs.
+#define MOE_GLOBAL __attribute__((address_space(1)))
+typedef const MOE_GLOBAL uint8_t* gbytes;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <Recv kRecv, int kElems>
+__device__ __forceinline__ void load_chunk(Chunk<kRecv, kElems>& c, gbytes p) {
+  constexpr int kWords = Chunk<kRecv, kElems>::kWords;
+  if constexpr (kWords == 2) {
+    const u32x2 v = *reinterpret_cast<const MOE_GLOBAL u32x2*>(p);
+    c.w[0] = v.x;
+    c.w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int q = 0; q < kWords / 4; ++q) {
+      const u32x4 v = *reinterpret_cast<const MOE_GLOBAL u32x4*>(p + 16 * q);
+      c.w[4 * q + 0] = v.x;
+      c.w[4 * q + 1] = v.y;
+      c.w[4 * q + 2] = v.z;
+      c.w[4 * q + 3] = v.w;
+    }
+  }
+}
+
+// The chunk c of all kMaxK rows (entries that are not dispatched point at
+// row 0 and are skipped when summing): no branches, so no waits between.
+template <Recv kRecv, int kMaxK, int kElems>
+__device__ __forceinline__ void load_rows(Chunk<kRecv, kElems> (&raw)[kMaxK], gbytes base,
+                                          const int64_t (&row_off)[kMaxK], int c) {
+  constexpr int kChunkBytes = kElems * elem_bytes<kRecv>();
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) load_chunk(raw[j], base + row_off[j] + static_cast<int64_t>(c) * kChunkBytes);
+}
+
+// Weighted sum of one chunk in entry order, then the store.
+template <Recv kRecv, Out kOut, int kMaxK, int kElems>
+__device__ __forceinline__ void fold_and_store(const Chunk<kRecv, kElems> (&raw)[kMaxK],
+                                               const bool (&valid)[kMaxK], const float (&wj)[kMaxK],
+                                               const float (&invj)[kMaxK], void* out,
+                                               size_t elem_offset) {
+  float acc[kElems];
+#pragma unroll
+  for (int e = 0; e < kElems; ++e) acc[e] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (!valid[j]) continue;
+#pragma unroll
+    for (int e = 0; e < kElems; ++e) {
+      const float v = element<kRecv, kElems>(raw[j], e, invj[j]);
+      const float p = v * wj[j];
+      acc[e] = acc[e] + p;
+    }
+  }
+  store_out<kOut, kElems>(out, elem_offset, acc);
+}
+
+template <Recv kRecv, Out kOut, int kMaxK, int kElems, int kWpt>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(RouteArgs a,
                                                                   const uint8_t* __restrict__ recv,
                                                                   const float* __restrict__ topk_w,
                                                                   void* __restrict__ out) {
-  using Chunk = typename ChunkOf<kRecv>::T;
-  constexpr int kChunkBytes = ChunkOf<kRecv>::kBytes;
+  using C = Chunk<kRecv, kElems>;
+  constexpr int kTokensPerBlock = kCombineThreads / kWave / kWpt;
   const int lane = threadIdx.x & (kWave - 1);
-  const int t = uniform(blockIdx.x * kTokensPerBlock + static_cast<int>(threadIdx.x / kWave));
+  const int wave = uniform(static_cast<int>(threadIdx.x / kWave));
+  const int t = uniform(blockIdx.x * kTokensPerBlock + wave / kWpt);
+  const int part = wave % kWpt;
   if (t >= a.bs) return;
+  const gbytes base = (gbytes)(recv);
 
-  // Wave-uniform prologue: row, weight and inverse scale of every entry.
-  const uint8_t* row_ptr[kMaxK];
+  // Wave-uniform prologue: row offset, weight and inverse scale of every
+  // entry, resolved one entry per lane and broadcast (see resolve_rows).
+  int64_t row_off[kMaxK];
+  bool valid[kMaxK];
+  int64_t my_off = 0;
+  resolve_rows<kMaxK>(a, t, 0, lane, row_off, valid, &my_off);
+  const int my_j = min(lane, kMaxK - 1);
+  const float my_w = topk_w[min(t * a.k + my_j, a.bs * a.k - 1)];
+  float my_inv = 1.0f;
+  if constexpr (kRecv == Recv::kInt8)
+    my_inv = *reinterpret_cast<const MOE_GLOBAL float*>(base + my_off + a.scale_off);
   float wj[kMaxK];
   float invj[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
-    row_ptr[j] = nullptr;
-    wj[j] = 0.0f;
-    invj[j] = 1.0f;
-    if (j < a.k) {
-      const int e = a.topk_idx[t * a.k + j];
-      const int slot = a.send_token_idx[t * a.k + j];
-      if (static_cast<unsigned>(e) < static_cast<unsigned>(a.num_experts) && slot >= 0) {
-        const int64_t row = static_cast<int64_t>(a.recv_base[e / a.epr]) + a.put_offset[e] + slot;
-        if (row >= 0 && row < a.cap_rows) {
-          row_ptr[j] = recv + row * a.row_bytes;
-          wj[j] = topk_w[t * a.k + j];
-          if constexpr (kRecv == Recv::kInt8)
-            invj[j] = *reinterpret_cast<const float*>(row_ptr[j] + a.scale_off);
-        }
-      }
-    }
+    wj[j] = lane_float(my_w, j);
+    invj[j] = lane_float(my_inv, j);
   }
 
-  const int chunks = a.hidden >> 3;
+  // Software pipeline over this lane's chunks c, c + S, c + 2S, ...: the k
+  // loads of the next chunk are issued before the current one is summed.
+  // Chunk indices past the row's end are clamped for the loads (the data is
+  // not used), so every load is issued unconditionally.
+  const int chunks = a.hidden / kElems;
+  constexpr int kStride = kWave * kWpt;
+  const int iters = (chunks + kStride - 1) / kStride;
   const size_t out_base = static_cast<size_t>(t) * a.hidden;
-  for (int c = lane; c < chunks; c += kWave) {
-    Chunk raw[kMaxK];
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (row_ptr[j] != nullptr)
-        raw[j] = *reinterpret_cast<const Chunk*>(row_ptr[j] + static_cast<size_t>(c) * kChunkBytes);
-    }
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (row_ptr[j] == nullptr) continue;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = element<kRecv>(raw[j], e, invj[j]);
-        const float p = v * wj[j];
-        acc[e] = acc[e] + p;
-      }
-    }
-    store_out<kOut>(out, out_base + static_cast<size_t>(c) * 8, acc);
+  int c = lane + part * kWave;
+  C buf_a[kMaxK], buf_b[kMaxK];
+  load_rows<kRecv, kMaxK, kElems>(buf_a, base, row_off, min(c, chunks - 1));
+  for (int it = 0; it < iters; it += 2) {
+    load_rows<kRecv, kMaxK, kElems>(buf_b, base, row_off, min(c + kStride, chunks - 1));
+    if (c < chunks)
+      fold_and_store<kRecv, kOut, kMaxK, kElems>(buf_a, valid, wj, invj, out,
+                                                 out_base + static_cast<size_t>(c) * kElems);
+    c += kStride;
+    if (it + 1 >= iters) break;
+    load_rows<kRecv, kMaxK, kElems>(buf_a, base, row_off, min(c + kStride, chunks - 1));
+    if (c < chunks)
+      fold_and_store<kRecv, kOut, kMaxK, kElems>(buf_b, valid, wj, invj, out,
+                                                 out_base + static_cast<size_t>(c) * kElems);
+    c += kStride;
   }
+}
+
+// Launch shape: one wave per token.
+template <Recv kRecv, Out kOut, int kMaxK>
+hipError_t launch_shape(const RouteArgs& a, const uint8_t* recv, const float* w, void* out,
+                        hipStream_t stream) {
+  constexpr int kWpt = 1;
+  constexpr int kTokensPerBlock = kCombineThreads / kWave / kWpt;
+  // 16-element chunks (16-byte int8 loads; two 16-byte loads per 16-bit
+  // row) except for 16-bit rows with up to 32 entries, which use 8-element
+  // chunks so that two buffers of k chunks stay in registers.
+  constexpr bool kWide = kRecv == Recv::kInt8 || kMaxK <= 8;
+  const dim3 block(kCombineThreads);
+  const dim3 grid((a.bs + kTokensPerBlock - 1) / kTokensPerBlock);
+  if constexpr (kWide) {
+    if (a.hidden % 16 == 0) {
+      hipLaunchKernelGGL((combine_kernel<kRecv, kOut, kMaxK, 16, kWpt>), grid, block, 0, stream, a,
+                         recv, w, out);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((combine_kernel<kRecv, kOut, kMaxK, 8, kWpt>), grid, block, 0, stream, a, recv,
+                     w, out);
+  return hipGetLastError();
 }
 
 template <Recv kRecv, Out kOut>
 hipError_t launch_k(const RouteArgs& a, const uint8_t* recv, const float* w, void* out,
                     hipStream_t stream) {
-  const dim3 grid((a.bs + kTokensPerBlock - 1) / kTokensPerBlock);
-  const dim3 block(kCombineThreads);
-  if (a.k <= 4) {
-    hipLaunchKernelGGL((combine_kernel<kRecv, kOut, 4>), grid, block, 0, stream, a, recv, w, out);
-  } else if (a.k <= 8) {
-    hipLaunchKernelGGL((combine_kernel<kRecv, kOut, 8>), grid, block, 0, stream, a, recv, w, out);
-  } else {
-    hipLaunchKernelGGL((combine_kernel<kRecv, kOut, 32>), grid, block, 0, stream, a, recv, w, out);
-  }
-  return hipGetLastError();
+  if (a.k <= 4) return launch_shape<kRecv, kOut, 4>(a, recv, w, out, stream);
+  if (a.k <= 8) return launch_shape<kRecv, kOut, 8>(a, recv, w, out, stream);
+  return launch_shape<kRecv, kOut, 32>(a, recv, w, out, stream);
 }
 
 template <Recv kRecv>

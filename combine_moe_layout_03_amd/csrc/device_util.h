@@ -67,4 +67,47 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 // A value known to be the same in every lane, moved to a scalar register.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Receive rows of kN (<= 64) consecutive entries j0 .. j0+kN-1 of token t.
+// Entry j goes to row recvBase[e / EPR] + putOffset[e] + sendTokenIdx[t, j];
+// an entry that is past topk, has an id outside [0, E) or a negative slot,
+// or whose row falls outside the buffer, is not dispatched (valid = false,
+// offset 0).  Lane j resolves entry j0 + j with vector loads (one load
+// instruction per array for all entries, every index clamped into its
+// array), and readlane broadcasts the results to wave-uniform registers; so
+// the whole resolution costs two rounds of memory latency.  `lane_row_off`
+// returns each lane's own offset (for further per-entry gathers).
+template <int kN, typename Route>
+__device__ __forceinline__ void resolve_rows(const Route& a, int t, int j0, int lane,
+                                             int64_t (&row_off)[kN], bool (&valid)[kN],
+                                             int64_t* lane_row_off = nullptr) {
+  static_assert(kN <= kWave, "one entry per lane");
+  const int last = a.bs * a.k - 1;
+  const int j = min(lane, kN - 1);
+  const int i = min(t * a.k + j0 + j, last);
+  const int e = a.topk_idx[i];
+  const int slot = a.send_token_idx[i];
+  const int ec = min(max(e, 0), a.num_experts - 1);
+  const int rank = static_cast<int>((static_cast<uint64_t>(ec) * a.epr_magic) >> 32);
+  const int64_t row = static_cast<int64_t>(a.recv_base[rank]) + a.put_offset[ec] + slot;
+  const bool ok = (j0 + j < a.k) && static_cast<unsigned>(e) < static_cast<unsigned>(a.num_experts) &&
+                  slot >= 0 && row >= 0 && row < a.cap_rows;
+  const int64_t off = ok ? row * a.row_bytes : 0;
+  if (lane_row_off != nullptr) *lane_row_off = off;
+  const int off_lo = static_cast<int>(static_cast<uint64_t>(off) & 0xffffffffu);
+  const int off_hi = static_cast<int>(static_cast<uint64_t>(off) >> 32);
+  const int okv = ok ? 1 : 0;
+#pragma unroll
+  for (int q = 0; q < kN; ++q) {
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(off_lo, q));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(off_hi, q));
+    row_off[q] = static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+    valid[q] = __builtin_amdgcn_readlane(okv, q) != 0;
+  }
+}
+
+// A lane's float broadcast from lane q.
+__device__ __forceinline__ float lane_float(float v, int q) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), q));
+}
+
 }  // namespace moe

@@ -10,39 +10,46 @@
 //                                  order), reduced across the wave by shuffles
 //   s    = 127.0f / (amax + 1e-12f),  inv = 1.0f / s
 //                               -- correctly rounded binary32 divisions
-//   q_i  = rint(x_i * s)        -- one binary32 multiply, v_rndne (ties even)
+//   q_i  = rint(x_i * s)        -- one binary32 multiply, then round half to
+//                                  even to an integer (see code_bits)
 // |x_i * s| < 127.5, so the page's int32 -> half -> int8 casts are exact and
-// q_i is the int32 value narrowed.
+// q_i is the integer narrowed.
 //
 // Each int8 row holds h code bytes, then the float inverse scale at byte
 // align32(h); each lane stores eight codes (8 bytes) per chunk.
 #include "device_util.h"
 #include "launch.h"
 
+#pragma clang fp contract(off)
+
 namespace moe {
 namespace {
 
 constexpr int kDispatchThreads = 256;
-constexpr int kTokensPerBlock = kDispatchThreads / kWave;
+constexpr int kGroup = 8;  // destinations resolved together
 
-template <bool kFp16>
-__device__ __forceinline__ uint32_t max_magnitude(const uint4& v) {
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// Running maximum of |x| over eight 16-bit elements, two at a time: with the
+// sign bits cleared, bf16 and fp16 magnitudes order like unsigned integers,
+// so a packed 16-bit integer max (v_pk_max_u16) does the comparison.
+__device__ __forceinline__ u16x2 max_magnitude(u16x2 m, const uint4& v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = w[i] & 0x7fffu;
-    const uint32_t hi = (w[i] >> 16) & 0x7fffu;
-    m = m > lo ? m : lo;
-    m = m > hi ? m : hi;
-  }
+  for (int i = 0; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu));
   return m;
 }
 
-__device__ __forceinline__ uint32_t code_byte(float f, float s) {
+// int8 code of one element in the low byte of the result.  y = f * s is one
+// rounded binary32 multiply; adding 1.5 * 2^23 (binade [2^23, 2^24), ulp 1)
+// rounds y half-to-even to an integer n exactly, since |y| < 127.5 < 2^22,
+// and the sum's bit pattern is 0x4b400000 + n, whose low byte is n as a
+// two's-complement int8 -- the same code as rint, int32 conversion and
+// narrowing, in two instructions.  (This file is compiled with contraction
+// off, so the multiply and the add stay separate.)
+__device__ __forceinline__ uint32_t code_bits(float f, float s) {
   const float y = f * s;
-  const float r = __builtin_rintf(y);
-  return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xffu;
+  return __float_as_uint(y + 12582912.0f);
 }
 
 // Eight elements -> eight int8 codes packed little-endian in two dwords.
@@ -53,90 +60,130 @@ __device__ __forceinline__ uint2 quantise_chunk(const uint4& v, float s) {
 #pragma unroll
   for (int d = 0; d < 2; ++d) {
     const uint32_t a = w[2 * d], b = w[2 * d + 1];
-    out[d] = code_byte(half_to_f32<kFp16>(a & 0xffffu), s) |
-             (code_byte(half_to_f32<kFp16>(a >> 16), s) << 8) |
-             (code_byte(half_to_f32<kFp16>(b & 0xffffu), s) << 16) |
-             (code_byte(half_to_f32<kFp16>(b >> 16), s) << 24);
+    const uint32_t c0 = code_bits(half_to_f32<kFp16>(a & 0xffffu), s);
+    const uint32_t c1 = code_bits(half_to_f32<kFp16>(a >> 16), s);
+    const uint32_t c2 = code_bits(half_to_f32<kFp16>(b & 0xffffu), s);
+    const uint32_t c3 = code_bits(half_to_f32<kFp16>(b >> 16), s);
+    out[d] = (c0 & 0xffu) | ((c1 & 0xffu) << 8) | ((c2 & 0xffu) << 16) | (c3 << 24);
   }
   return make_uint2(out[0], out[1]);
 }
 
-// Receive row of entry (t, j), or -1 when the entry is not dispatched.
-__device__ __forceinline__ int64_t dest_row(const RouteArgs& a, int t, int j) {
-  const int e = a.topk_idx[t * a.k + j];
-  const int slot = a.send_token_idx[t * a.k + j];
-  if (static_cast<unsigned>(e) >= static_cast<unsigned>(a.num_experts) || slot < 0) return -1;
-  const int64_t row = static_cast<int64_t>(a.recv_base[e / a.epr]) + a.put_offset[e] + slot;
-  return (row >= 0 && row < a.cap_rows) ? row : -1;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16- and 8-byte stores; kNt marks them non-temporal (streaming).
+template <bool kNt>
+__device__ __forceinline__ void put(uint4* p, const uint4& v) {
+  if constexpr (kNt) {
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+  } else {
+    *p = v;
+  }
+}
+template <bool kNt>
+__device__ __forceinline__ void put(uint2* p, const uint2& v) {
+  if constexpr (kNt) {
+    __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
+  } else {
+    *p = v;
+  }
 }
 
-template <bool kFp16, bool kQuant, int kVpl>
+// kWpt waves per token (a workgroup holds kDispatchThreads / 64 / kWpt
+// tokens).  Wave part p of a token owns the 64-chunk groups p, p + kWpt,
+// p + 2 kWpt, ... of the row; a lane holds chunk lane + 64 * group, i.e.
+// kVpl chunks of 8 elements (16 bytes) each.  With kWpt > 1 the parts combine
+// their maxima through LDS.  kNt selects non-temporal stores.
+template <bool kFp16, bool kQuant, int kVpl, int kWpt, bool kNt>
 __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(RouteArgs a,
                                                                     const uint16_t* __restrict__ x,
                                                                     uint8_t* __restrict__ recv) {
+  constexpr int kTok = kDispatchThreads / kWave / kWpt;
   const int lane = threadIdx.x & (kWave - 1);
-  const int t = uniform(blockIdx.x * kTokensPerBlock + static_cast<int>(threadIdx.x / kWave));
-  if (t >= a.bs) return;
-  const int chunks = a.hidden >> 3;  // 8 elements per chunk
-  const uint4* src = reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * a.hidden);
+  const int wave = uniform(static_cast<int>(threadIdx.x / kWave));
+  const int t = uniform(blockIdx.x * kTok + wave / kWpt);
+  const int part = wave % kWpt;
+  // No early return before the barrier below: inactive waves skip the work.
+  const bool active = t < a.bs;
+  const int chunks = a.hidden >> 3;
+  const uint4* src = reinterpret_cast<const uint4*>(x + static_cast<size_t>(active ? t : 0) * a.hidden);
 
   uint4 v[kVpl];
 #pragma unroll
   for (int i = 0; i < kVpl; ++i) {
-    const int c = lane + i * kWave;
-    v[i] = c < chunks ? src[c] : make_uint4(0u, 0u, 0u, 0u);
+    const int c = lane + (i * kWpt + part) * kWave;
+    v[i] = (active && c < chunks) ? src[c] : make_uint4(0u, 0u, 0u, 0u);
   }
 
   if constexpr (!kQuant) {
-    for (int j = 0; j < a.k; ++j) {
-      const int64_t row = dest_row(a, t, j);
-      if (row < 0) continue;
-      uint4* dst = reinterpret_cast<uint4*>(recv + row * a.row_bytes);
+    if (!active) return;
+    for (int j0 = 0; j0 < a.k; j0 += kGroup) {
+      int64_t row_off[kGroup];
+      bool valid[kGroup];
+      resolve_rows<kGroup>(a, t, j0, lane, row_off, valid);
 #pragma unroll
-      for (int i = 0; i < kVpl; ++i) {
-        const int c = lane + i * kWave;
-        if (c < chunks) dst[c] = v[i];
+      for (int j = 0; j < kGroup; ++j) {
+        if (!valid[j]) continue;
+        uint4* dst = reinterpret_cast<uint4*>(recv + row_off[j]);
+#pragma unroll
+        for (int i = 0; i < kVpl; ++i) {
+          const int c = lane + (i * kWpt + part) * kWave;
+          if (c < chunks) put<kNt>(dst + c, v[i]);
+        }
       }
     }
   } else {
-    uint32_t m = 0;
+    u16x2 m2 = {0, 0};
 #pragma unroll
-    for (int i = 0; i < kVpl; ++i) {
-      const uint32_t mi = max_magnitude<kFp16>(v[i]);
-      m = m > mi ? m : mi;
+    for (int i = 0; i < kVpl; ++i) m2 = max_magnitude(m2, v[i]);
+    uint32_t m = wave_max_u32(m2.x > m2.y ? m2.x : m2.y);
+    if constexpr (kWpt > 1) {
+      __shared__ uint32_t part_max[kDispatchThreads / kWave];
+      if (lane == 0) part_max[wave] = m;
+      __syncthreads();
+      const int first = (wave / kWpt) * kWpt;
+#pragma unroll
+      for (int q = 0; q < kWpt; ++q) m = m > part_max[first + q] ? m : part_max[first + q];
     }
-    m = wave_max_u32(m);
+    if (!active) return;
     const float amax = half_to_f32<kFp16>(m);
     const float s = 127.0f / (amax + 1e-12f);
     const float inv = 1.0f / s;
     uint2 q[kVpl];
 #pragma unroll
     for (int i = 0; i < kVpl; ++i) q[i] = quantise_chunk<kFp16>(v[i], s);
-    for (int j = 0; j < a.k; ++j) {
-      const int64_t row = dest_row(a, t, j);
-      if (row < 0) continue;
-      uint8_t* base = recv + row * a.row_bytes;
-      uint2* dst = reinterpret_cast<uint2*>(base);
+    for (int j0 = 0; j0 < a.k; j0 += kGroup) {
+      int64_t row_off[kGroup];
+      bool valid[kGroup];
+      resolve_rows<kGroup>(a, t, j0, lane, row_off, valid);
 #pragma unroll
-      for (int i = 0; i < kVpl; ++i) {
-        const int c = lane + i * kWave;
-        if (c < chunks) dst[c] = q[i];
+      for (int j = 0; j < kGroup; ++j) {
+        if (!valid[j]) continue;
+        uint8_t* base = recv + row_off[j];
+#pragma unroll
+        for (int i = 0; i < kVpl; ++i) {
+          const int c = lane + (i * kWpt + part) * kWave;
+          if (c < chunks) put<kNt>(reinterpret_cast<uint2*>(base) + c, q[i]);
+        }
+        if (part == 0 && lane == 0) *reinterpret_cast<float*>(base + a.scale_off) = inv;
       }
-      if (lane == 0) *reinterpret_cast<float*>(base + a.scale_off) = inv;
     }
   }
 }
 
 template <bool kFp16, bool kQuant>
 hipError_t launch_vpl(const RouteArgs& a, const uint16_t* x, uint8_t* recv, hipStream_t stream) {
+  constexpr int kWpt = 1;
+  constexpr int kTok = kDispatchThreads / kWave / kWpt;
   const int chunks = a.hidden / 8;
-  const int per_lane = (chunks + kWave - 1) / kWave;
-  const dim3 grid((a.bs + kTokensPerBlock - 1) / kTokensPerBlock);
+  const int per_lane = (chunks + kWave * kWpt - 1) / (kWave * kWpt);
+  const dim3 grid((a.bs + kTok - 1) / kTok);
   const dim3 block(kDispatchThreads);
-#define MOE_DISPATCH_CASE(V)                                                                     \
-  if (per_lane <= V) {                                                                           \
-    hipLaunchKernelGGL((dispatch_kernel<kFp16, kQuant, V>), grid, block, 0, stream, a, x, recv); \
-    return hipGetLastError();                                                                    \
+#define MOE_DISPATCH_CASE(V)                                                                             \
+  if (per_lane <= V) {                                                                                   \
+    hipLaunchKernelGGL((dispatch_kernel<kFp16, kQuant, V, kWpt, false>), grid, block, 0, stream, a, x, recv); \
+    return hipGetLastError();                                                                            \
   }
   MOE_DISPATCH_CASE(1)
   MOE_DISPATCH_CASE(2)

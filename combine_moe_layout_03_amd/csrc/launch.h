@@ -45,7 +45,10 @@ struct RouteArgs {
   int64_t row_bytes;   // bytes per receive row
   int64_t cap_rows;    // rows that fit in the receive buffer
   int32_t scale_off;   // byte offset of the inverse scale in an int8 row
+  uint64_t epr_magic;  // ceil(2^32 / epr): e / epr == (e * epr_magic) >> 32 for e < 2^21
 };
+
+inline uint64_t div_magic(int32_t d) { return ((uint64_t(1) << 32) + uint64_t(d) - 1) / uint64_t(d); }
 
 enum class Half { kBf16 = 0, kFp16 = 1 };
 enum class Recv { kBf16 = 0, kFp16 = 1, kInt8 = 2 };

@@ -61,18 +61,19 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
   const int wave = uniform(tid / kWave);
   const int tile = blockIdx.x;
 
-  // Starting count of every expert for this tile: the sum over earlier tiles.
+  // Starting count of every expert for this tile: the sum over earlier
+  // tiles, 16 independent loads in flight per thread per batch.
   for (int e = tid; e < num_experts; e += kLayoutThreads) {
-    int s0 = 0, s1 = 0, s2 = 0, s3 = 0;
-    int t = 0;
-    for (; t + 4 <= tile; t += 4) {
-      s0 += tile_count[static_cast<size_t>(t) * num_experts + e];
-      s1 += tile_count[static_cast<size_t>(t + 1) * num_experts + e];
-      s2 += tile_count[static_cast<size_t>(t + 2) * num_experts + e];
-      s3 += tile_count[static_cast<size_t>(t + 3) * num_experts + e];
+    int s = 0;
+    for (int t0 = 0; t0 < tile; t0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        v[u] = (t0 + u < tile) ? tile_count[static_cast<size_t>(t0 + u) * num_experts + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) s += v[u];
     }
-    for (; t < tile; ++t) s0 += tile_count[static_cast<size_t>(t) * num_experts + e];
-    base[e] = s0 + s1 + s2 + s3;
+    base[e] = s;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) wave_cnt[w * num_experts + e] = 0;
   }

@@ -151,3 +151,14 @@ def test_product_path_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f"{f} mentions the oracle"
     assert "oracle" not in open(HEADER).read().lower()
+
+
+def test_rank_division_by_multiply_high_is_exact():
+    """The kernels find an expert's rank as (e * ceil(2^32 / EPR)) >> 32; this
+    equals e // EPR for every expert id and every EPR the library accepts."""
+    import numpy as np
+
+    e = np.arange(2048, dtype=np.uint64)
+    for d in range(1, 2049):
+        m = np.uint64(((1 << 32) + d - 1) // d)
+        assert np.array_equal((e * m) >> np.uint64(32), e // np.uint64(d)), d

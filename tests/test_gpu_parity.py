@@ -235,6 +235,17 @@ def test_quant_golden_rows_on_gpu():
             assert pins.f32_bits(c["inv"][0]) == pins.f32_bits(exp_inv), case["name"]
 
 
+@pytest.mark.parametrize("quant,out_kind", [(False, "fp32"), (False, "bf16"), (True, "fp32")])
+def test_subnormal_values(quant, out_kind):
+    """Rows around the binary32 normal limit (1.2e-38): widening, products and
+    sums of subnormals must follow IEEE (no flush to zero), as on the CPU."""
+    w = W.random_case(211, 48, 64, 4, 8, 2, routing="dup", x_std=2e-38)
+    log(f"subnormal values quant={quant} out={out_kind}")
+    g = GpuRun(w, quant, out_kind).run_all().host()
+    o = oracle_run(w, quant, out_kind)
+    compare(w, quant, out_kind, g, o)
+
+
 def test_identity_k1_unit_weight():
     """k = 1, weight 1: combine returns the dequantised row exactly."""
     w = W.random_case(201, 64, 512, 1, 8, 2, zero_rows=2)
