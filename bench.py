@@ -10,8 +10,9 @@ Timing: W untimed warm-up steps, then K timed steps.  Before each step and
 between dispatch and combine a read-only pass over a 1 GiB buffer evicts the
 L2s and the 256 MB Infinity Cache, so x is read from HBM by dispatch and the
 receive buffer from HBM by combine (between the two, a real MoE layer runs its
-expert GEMMs).  HIP events recorded on the stream the kernels run on time each
-stage; flushes are outside the timed intervals.  ``ms_per_step`` is the mean
+expert GEMMs).  HIP events recorded on the stream the kernels run on (created without the
+system-scope fence, which only serves host visibility) time each stage;
+flushes are outside the timed intervals.  ``ms_per_step`` is the mean
 of layout+notify+dispatch+combine over the K steps and ``value`` is bs divided
 by it (tokens/s, whole pipeline).  The un-flushed back-to-back rate, a plain
 device copy and the CPU oracle are reported beside it, labelled.
@@ -46,6 +47,54 @@ KERNEL_SOURCES = {
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw HIP events (ctypes on the HIP runtime torch already loaded),
+    recorded on the stream the library's kernels run on.  By default they are
+    created with hipEventDisableSystemFence: the system-scope fence only
+    matters for host visibility of memory and adds dispatch latency to every
+    timed interval."""
+
+    FLAGS = {"nofence": 0x20000000, "default": 0x0}
+
+    def __init__(self, flags: str = "nofence"):
+        import ctypes
+
+        self.ct = ctypes
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.flags = self.FLAGS[flags]
+        self.events = []
+
+    def new(self):
+        ev = self.ct.c_void_p()
+        rc = self.lib.hipEventCreateWithFlags(self.ct.byref(ev), self.flags)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+        self.events.append(ev)
+        return ev
+
+    def record(self, ev, stream) -> None:
+        rc = self.lib.hipEventRecord(ev, self.ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def ms(self, a, b) -> float:
+        out = self.ct.c_float(0.0)
+        rc = self.lib.hipEventElapsedTime(self.ct.byref(out), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return out.value
+
+    def close(self) -> None:
+        for ev in self.events:
+            self.lib.hipEventDestroy(ev)
+        self.events = []
 
 
 def algorithmic_bytes(bs: int, h: int, k: int, quant: bool, out_bytes: int = 2):
@@ -115,6 +164,8 @@ def main(argv=None) -> int:
     ap.add_argument("--mode", default="int8", choices=["int8", "pass"])
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work (0: skip)")
     ap.add_argument("--flush-mib", type=int, default=1024)
+    ap.add_argument("--event-flags", default="nofence", choices=["nofence", "default"],
+                    help="HIP event creation flags for the stage timers")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, then WRITE_SIZE) of a bench "
                          "run into profiles/traffic_*.json and exit")
@@ -163,39 +214,40 @@ def main(argv=None) -> int:
 
     # timed steps
     log(f"timed x{args.steps}")
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    hev = HipEvents(args.event_flags)
+    ev = [[hev.new() for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     for i in range(args.steps):
         e = ev[i]
         do_flush()
-        e[0].record(stream)
+        hev.record(e[0], stream)
         buf.layout(idx)
         buf.notify()
-        e[1].record(stream)
+        hev.record(e[1], stream)
         buf.dispatch(x, idx)
-        e[2].record(stream)
+        hev.record(e[2], stream)
         do_flush()
-        e[3].record(stream)
+        hev.record(e[3], stream)
         buf.combine(idx, wts)
-        e[4].record(stream)
+        hev.record(e[4], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
-    lay_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    dis_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    com_ms = [e[3].elapsed_time(e[4]) for e in ev]
+    lay_ms = [hev.ms(e[0], e[1]) for e in ev]
+    dis_ms = [hev.ms(e[1], e[2]) for e in ev]
+    com_ms = [hev.ms(e[3], e[4]) for e in ev]
     step_ms = [a + b + c for a, b, c in zip(lay_ms, dis_ms, com_ms)]
     ms_per_step = sum(step_ms) / len(step_ms)
 
     # un-flushed back-to-back pipeline (labelled; combine may hit the Infinity Cache)
     log("un-flushed back-to-back")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
+    e0, e1 = hev.new(), hev.new()
+    hev.record(e0, stream)
     for _ in range(args.steps):
         buf.run(x, idx, wts)
-    e1.record(stream)
+    hev.record(e1, stream)
     torch.cuda.synchronize()
-    unflushed_ms = e0.elapsed_time(e1) / args.steps
+    unflushed_ms = hev.ms(e0, e1) / args.steps
 
     # plain device copy of 1 GiB (read + write) as the practical ceiling
     log("copy ceiling")
@@ -203,18 +255,16 @@ def main(argv=None) -> int:
     dst = torch.empty_like(src)
     for _ in range(2):
         torch.neg(src, out=dst)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0, c1 = hev.new(), hev.new()
     reps = 10
-    c0.record(stream)
+    hev.record(c0, stream)
     for _ in range(reps):
         torch.neg(src, out=dst)
-    c1.record(stream)
+    hev.record(c1, stream)
     torch.cuda.synchronize()
-    copy_gbps = 2 * src.numel() * 4 * reps / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    copy_gbps = 2 * src.numel() * 4 * reps / (hev.ms(c0, c1) * 1e-3) / 1e9
     del dst
-
-    # parity spot check of the timed buffers against the oracle on a sample
-    torch.cuda.synchronize()
+    hev.close()
 
     b_dis, b_com, b_lay = algorithmic_bytes(w.bs, w.hidden, w.topk, quant)
     dis_mean = statistics.mean(dis_ms)
@@ -252,6 +302,7 @@ def main(argv=None) -> int:
                    "dispatch": "int8" if quant else "passthrough", "out_dtype": "bf16",
                    "parallelism": "1 GPU, ranks are logical partitions of one receive buffer"},
         "step": "layout + notify + dispatch + combine, caches flushed before the step and before combine",
+        "timer": f"HIP events on the kernels' stream ({args.event_flags})",
         "dispatch_combine_tokens_per_s": w.bs / ((dis_mean + com_mean) * 1e-3),
         "dispatch_combine_hbm_gbps": dc_gbps,
         "dispatch_combine_hbm_frac": dc_gbps / HBM_PEAK_GBPS,

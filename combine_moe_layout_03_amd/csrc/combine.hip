@@ -1,12 +1,12 @@
 // Stage 4, combine ("UMDK/CAM communication acceleration library deep
 // analysis v2", section 2.6, moe_combine_normal_zb::ReadBufferAndWeightedSum).
 //
-// kWpt waves per token.  Each wave first resolves, in scalar registers, the
-// receive row, weight and (int8) inverse scale of each of the token's k
-// entries.  Then each lane walks chunks of kElems elements of the row with
-// 16-byte loads, software-pipelined: the k row loads of the next chunk are
-// issued before the current chunk is summed, so loads and arithmetic
-// overlap inside every wave.  The loaded values are folded into binary32
+// kWpt waves per token, each owning every kWpt-th group of 64 chunks of the
+// row.  Each wave first resolves the receive row, weight and (int8) inverse
+// scale of each of the token's k entries into scalar registers.  Then each
+// lane walks chunks of kElems elements, software-pipelined: the k row loads
+// of the next chunk are issued before the current chunk is summed, so loads
+// and arithmetic overlap inside every wave.  The loaded values are folded into binary32
 // accumulators in entry order j = 0..k-1, exactly as the page does:
 //   acc = +0; acc = acc + v_j * w_j  (v_j = float(row) or float(q) * inv)
 // with every multiply and add rounded separately (this file is compiled with
@@ -64,20 +64,31 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   }
 }
 
-template <Out kOut, int kElems>
+typedef uint32_t o32x4 __attribute__((ext_vector_type(4)));
+
+template <bool kNt>
+__device__ __forceinline__ void put16(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  if constexpr (kNt) {
+    __builtin_nontemporal_store(o32x4{a, b, c, d}, reinterpret_cast<o32x4*>(p));
+  } else {
+    *reinterpret_cast<uint4*>(p) = make_uint4(a, b, c, d);
+  }
+}
+
+template <Out kOut, int kElems, bool kNt>
 __device__ __forceinline__ void store_out(void* out, size_t elem_offset, const float (&acc)[kElems]) {
   if constexpr (kOut == Out::kF32) {
-    float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + elem_offset);
+    float* p = static_cast<float*>(out) + elem_offset;
 #pragma unroll
     for (int q = 0; q < kElems / 4; ++q)
-      p[q] = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+      put16<kNt>(p + 4 * q, __float_as_uint(acc[4 * q]), __float_as_uint(acc[4 * q + 1]),
+                 __float_as_uint(acc[4 * q + 2]), __float_as_uint(acc[4 * q + 3]));
   } else {
-    uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + elem_offset);
+    uint16_t* p = static_cast<uint16_t*>(out) + elem_offset;
 #pragma unroll
-    for (int q = 0; q < kElems / 8; ++q) {
-      p[q] = make_uint4(pack2<kOut>(acc[8 * q + 0], acc[8 * q + 1]), pack2<kOut>(acc[8 * q + 2], acc[8 * q + 3]),
-                        pack2<kOut>(acc[8 * q + 4], acc[8 * q + 5]), pack2<kOut>(acc[8 * q + 6], acc[8 * q + 7]));
-    }
+    for (int q = 0; q < kElems / 8; ++q)
+      put16<kNt>(p + 8 * q, pack2<kOut>(acc[8 * q + 0], acc[8 * q + 1]), pack2<kOut>(acc[8 * q + 2], acc[8 * q + 3]),
+                 pack2<kOut>(acc[8 * q + 4], acc[8 * q + 5]), pack2<kOut>(acc[8 * q + 6], acc[8 * q + 7]));
   }
 }
 
@@ -88,17 +99,19 @@ typedef const MOE_GLOBAL uint8_t* gbytes;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <Recv kRecv, int kElems>
+template <Recv kRecv, int kElems, bool kNt>
 __device__ __forceinline__ void load_chunk(Chunk<kRecv, kElems>& c, gbytes p) {
   constexpr int kWords = Chunk<kRecv, kElems>::kWords;
   if constexpr (kWords == 2) {
-    const u32x2 v = *reinterpret_cast<const MOE_GLOBAL u32x2*>(p);
+    const u32x2 v = kNt ? __builtin_nontemporal_load(reinterpret_cast<const MOE_GLOBAL u32x2*>(p))
+                        : *reinterpret_cast<const MOE_GLOBAL u32x2*>(p);
     c.w[0] = v.x;
     c.w[1] = v.y;
   } else {
 #pragma unroll
     for (int q = 0; q < kWords / 4; ++q) {
-      const u32x4 v = *reinterpret_cast<const MOE_GLOBAL u32x4*>(p + 16 * q);
+      const u32x4 v = kNt ? __builtin_nontemporal_load(reinterpret_cast<const MOE_GLOBAL u32x4*>(p + 16 * q))
+                          : *reinterpret_cast<const MOE_GLOBAL u32x4*>(p + 16 * q);
       c.w[4 * q + 0] = v.x;
       c.w[4 * q + 1] = v.y;
       c.w[4 * q + 2] = v.z;
@@ -109,16 +122,17 @@ __device__ __forceinline__ void load_chunk(Chunk<kRecv, kElems>& c, gbytes p) {
 
 // The chunk c of all kMaxK rows (entries that are not dispatched point at
 // row 0 and are skipped when summing): no branches, so no waits between.
-template <Recv kRecv, int kMaxK, int kElems>
+template <Recv kRecv, int kMaxK, int kElems, bool kNt>
 __device__ __forceinline__ void load_rows(Chunk<kRecv, kElems> (&raw)[kMaxK], gbytes base,
                                           const int64_t (&row_off)[kMaxK], int c) {
   constexpr int kChunkBytes = kElems * elem_bytes<kRecv>();
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) load_chunk(raw[j], base + row_off[j] + static_cast<int64_t>(c) * kChunkBytes);
+  for (int j = 0; j < kMaxK; ++j)
+    load_chunk<kRecv, kElems, kNt>(raw[j], base + row_off[j] + static_cast<int64_t>(c) * kChunkBytes);
 }
 
 // Weighted sum of one chunk in entry order, then the store.
-template <Recv kRecv, Out kOut, int kMaxK, int kElems>
+template <Recv kRecv, Out kOut, int kMaxK, int kElems, bool kNtStore>
 __device__ __forceinline__ void fold_and_store(const Chunk<kRecv, kElems> (&raw)[kMaxK],
                                                const bool (&valid)[kMaxK], const float (&wj)[kMaxK],
                                                const float (&invj)[kMaxK], void* out,
@@ -136,10 +150,11 @@ __device__ __forceinline__ void fold_and_store(const Chunk<kRecv, kElems> (&raw)
       acc[e] = acc[e] + p;
     }
   }
-  store_out<kOut, kElems>(out, elem_offset, acc);
+  store_out<kOut, kElems, kNtStore>(out, elem_offset, acc);
 }
 
-template <Recv kRecv, Out kOut, int kMaxK, int kElems, int kWpt>
+template <Recv kRecv, Out kOut, int kMaxK, int kElems, int kWpt, bool kNtLoad = false,
+          bool kNtStore = false>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(RouteArgs a,
                                                                   const uint8_t* __restrict__ recv,
                                                                   const float* __restrict__ topk_w,
@@ -182,43 +197,35 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(RouteArgs a,
   const size_t out_base = static_cast<size_t>(t) * a.hidden;
   int c = lane + part * kWave;
   C buf_a[kMaxK], buf_b[kMaxK];
-  load_rows<kRecv, kMaxK, kElems>(buf_a, base, row_off, min(c, chunks - 1));
+  load_rows<kRecv, kMaxK, kElems, kNtLoad>(buf_a, base, row_off, min(c, chunks - 1));
   for (int it = 0; it < iters; it += 2) {
-    load_rows<kRecv, kMaxK, kElems>(buf_b, base, row_off, min(c + kStride, chunks - 1));
+    load_rows<kRecv, kMaxK, kElems, kNtLoad>(buf_b, base, row_off, min(c + kStride, chunks - 1));
     if (c < chunks)
-      fold_and_store<kRecv, kOut, kMaxK, kElems>(buf_a, valid, wj, invj, out,
+      fold_and_store<kRecv, kOut, kMaxK, kElems, kNtStore>(buf_a, valid, wj, invj, out,
                                                  out_base + static_cast<size_t>(c) * kElems);
     c += kStride;
     if (it + 1 >= iters) break;
-    load_rows<kRecv, kMaxK, kElems>(buf_a, base, row_off, min(c + kStride, chunks - 1));
+    load_rows<kRecv, kMaxK, kElems, kNtLoad>(buf_a, base, row_off, min(c + kStride, chunks - 1));
     if (c < chunks)
-      fold_and_store<kRecv, kOut, kMaxK, kElems>(buf_b, valid, wj, invj, out,
+      fold_and_store<kRecv, kOut, kMaxK, kElems, kNtStore>(buf_b, valid, wj, invj, out,
                                                  out_base + static_cast<size_t>(c) * kElems);
     c += kStride;
   }
 }
 
-// Launch shape: one wave per token.
+// Launch shape (swept at h = 7168, k = 8 with caches flushed): four waves
+// per token, 8-element chunks; 16-bit rows are read with non-temporal loads
+// (streamed past the caches), int8 rows with ordinary loads.
 template <Recv kRecv, Out kOut, int kMaxK>
 hipError_t launch_shape(const RouteArgs& a, const uint8_t* recv, const float* w, void* out,
                         hipStream_t stream) {
-  constexpr int kWpt = 1;
+  constexpr int kWpt = 4;
+  constexpr bool kNtLoad = kRecv != Recv::kInt8;
   constexpr int kTokensPerBlock = kCombineThreads / kWave / kWpt;
-  // 16-element chunks (16-byte int8 loads; two 16-byte loads per 16-bit
-  // row) except for 16-bit rows with up to 32 entries, which use 8-element
-  // chunks so that two buffers of k chunks stay in registers.
-  constexpr bool kWide = kRecv == Recv::kInt8 || kMaxK <= 8;
   const dim3 block(kCombineThreads);
   const dim3 grid((a.bs + kTokensPerBlock - 1) / kTokensPerBlock);
-  if constexpr (kWide) {
-    if (a.hidden % 16 == 0) {
-      hipLaunchKernelGGL((combine_kernel<kRecv, kOut, kMaxK, 16, kWpt>), grid, block, 0, stream, a,
-                         recv, w, out);
-      return hipGetLastError();
-    }
-  }
-  hipLaunchKernelGGL((combine_kernel<kRecv, kOut, kMaxK, 8, kWpt>), grid, block, 0, stream, a, recv,
-                     w, out);
+  hipLaunchKernelGGL((combine_kernel<kRecv, kOut, kMaxK, 8, kWpt, kNtLoad, false>), grid, block, 0, stream,
+                     a, recv, w, out);
   return hipGetLastError();
 }
 

@@ -31,10 +31,20 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
   const int tile = blockIdx.x;
   for (int e = threadIdx.x; e <= num_experts; e += kLayoutThreads) hist[e] = 0;
   __syncthreads();
-  const int begin = tile * kLayoutTile;
-  const int end = min(n, begin + kLayoutTile);
-  for (int i = begin + threadIdx.x; i < end; i += kLayoutThreads) {
-    const int e = topk_idx[i];
+  // All of this thread's ids are loaded before the first LDS update, so the
+  // loads are in flight together.
+  constexpr int kPer = kLayoutTile / kLayoutThreads;
+  const int begin = tile * kLayoutTile + threadIdx.x;
+  int ids[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = begin + r * kLayoutThreads;
+    ids[r] = i < n ? topk_idx[i] : -2;
+  }
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    if (ids[r] == -2 && begin + r * kLayoutThreads >= n) continue;
+    const int e = ids[r];
     const int key = static_cast<unsigned>(e) < static_cast<unsigned>(num_experts) ? e : num_experts;
     atomicAdd(&hist[key], 1);
   }
@@ -86,12 +96,20 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
   const int seg_begin = tile * kLayoutTile + wave * kLayoutSegment;
   int local[kLayoutRounds];
   int key[kLayoutRounds];
+  int ids[kLayoutRounds];
   int my_bad = 0;
+  // All rounds' ids are loaded first (in flight together); the rounds then
+  // only touch LDS.
+#pragma unroll
+  for (int r = 0; r < kLayoutRounds; ++r) {
+    const int i = seg_begin + r * kWave + lane;
+    ids[r] = i < n ? topk_idx[i] : -1;
+  }
 #pragma unroll
   for (int r = 0; r < kLayoutRounds; ++r) {
     const int i = seg_begin + r * kWave + lane;
     const bool in_range = i < n;
-    const int e = in_range ? topk_idx[i] : -1;
+    const int e = ids[r];
     const bool valid = in_range && static_cast<unsigned>(e) < static_cast<unsigned>(num_experts);
     my_bad += (in_range && !valid) ? 1 : 0;
     uint64_t peers = __ballot(valid);
