@@ -10,19 +10,28 @@
 namespace moe {
 
 // ---- layout -------------------------------------------------------------------
-// Entries are processed in tiles of kLayoutTile flat (token, k) entries; a
-// tile is one 256-thread workgroup whose four waves each own a contiguous
-// quarter, walked in rounds of 64 entries.
-constexpr int kLayoutThreads = 256;
-constexpr int kLayoutRounds = 8;
-constexpr int kLayoutSegment = kLayoutRounds * 64;                    // entries per wave
-constexpr int kLayoutTile = (kLayoutThreads / 64) * kLayoutSegment;  // 2048
-
-inline int64_t layout_num_tiles(int64_t n) { return n <= 0 ? 1 : (n + kLayoutTile - 1) / kLayoutTile; }
+// The flat (token, k) entries are cut into tiles of 2048, one workgroup per
+// tile; a workgroup's waves each own a contiguous segment of its tile,
+// walked in rounds of 64 entries.  Up to 512 experts a workgroup has 16 waves
+// of 2 rounds, beyond that 4 waves of 8 rounds (the per-wave LDS counters,
+// waves x E ints, must fit).
+struct LayoutShape {
+  int waves, rounds;
+  int64_t tile() const { return static_cast<int64_t>(waves) * rounds * 64; }
+};
+constexpr int kLayoutBigGroupMaxExperts = 512;
+inline LayoutShape layout_shape(int64_t num_experts) {
+  return num_experts <= kLayoutBigGroupMaxExperts ? LayoutShape{16, 2} : LayoutShape{4, 8};
+}
+inline int64_t layout_num_tiles(int64_t n, int64_t num_experts) {
+  const int64_t tile = layout_shape(num_experts).tile();
+  return n <= 0 ? 1 : (n + tile - 1) / tile;
+}
 // Workspace: per-tile expert counts plus a bad-id count for every tile but
 // the last (the last tile's workgroup counts its own entries).
 inline size_t layout_workspace_bytes(int64_t n, int64_t num_experts) {
-  return static_cast<size_t>(layout_num_tiles(n) - 1) * static_cast<size_t>(num_experts + 1) * 4u;
+  return static_cast<size_t>(layout_num_tiles(n, num_experts) - 1) *
+         static_cast<size_t>(num_experts + 1) * 4u;
 }
 
 hipError_t launch_layout(const int32_t* topk_idx, int32_t n, int32_t num_experts, int32_t epr,

@@ -3,67 +3,79 @@
 // counts and the send slot of every (token, k) entry.
 //
 // The page counts in rounds with cross-core atomics and a SyncAll per round,
-// then computes send indices.  Here the flat entry list is cut into tiles of
-// kLayoutTile entries:
-//   layout_count_kernel  one workgroup per tile except the last: an LDS
-//                        histogram of the tile (order-free atomics), written
-//                        to the workspace;
+// then computes send indices.  Here the flat entry list is cut into tiles
+// (see LayoutShape):
+//   layout_count_kernel  one workgroup per tile except the last, only when
+//                        there are several tiles: an LDS histogram of the
+//                        tile (order-free atomics), written to the workspace;
 //   layout_rank_kernel   one workgroup per tile: the tile's starting count per
-//                        expert (sum over earlier tiles), then the stable rank
-//                        of every entry among equal ids, wave by wave, in flat
-//                        order.  The last tile's workgroup also writes the
-//                        totals.
+//                        expert (sum over earlier tiles' histograms), then the
+//                        stable rank of every entry among equal ids, wave by
+//                        wave, in flat order.  The last tile's workgroup also
+//                        writes the totals.
 // Inside a wave, lanes holding the same expert id find each other with one
 // ballot per id bit (a match-any built from ballots); a lane's rank in its
-// group is the number of group lanes below it.  A per-wave LDS counter per
-// expert carries the rank across rounds; a scan over the four waves and the
-// tile base turn it into the global slot.  No result depends on scheduling.
+// group is the number of group lanes below it.  The group's highest lane
+// adds the group size to a wave-private LDS counter of the expert with an
+// atomic that returns the old value; LDS executes one wave's operations in
+// order, so that value is the count of the expert in the wave's earlier
+// rounds.  Up to eight rounds' atomics are issued back to back before their
+// results are shuffled to the group members, so the rounds do not wait on
+// each other.  A scan over the waves and the tile base turn wave-local ranks
+// into global slots.  No result depends on scheduling.
 #include "device_util.h"
 #include "launch.h"
 
 namespace moe {
 namespace {
 
-__global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
+constexpr int kBatch = 8;  // rounds whose counter atomics are in flight together
+
+template <int kWaves, int kRounds>
+__global__ __launch_bounds__(kWaves * kWave) void layout_count_kernel(
     const int32_t* __restrict__ topk_idx, int32_t n, int32_t num_experts,
     int32_t* __restrict__ tile_count, int32_t* __restrict__ tile_bad) {
+  constexpr int kThreads = kWaves * kWave;
+  constexpr int kTile = kThreads * kRounds;
   extern __shared__ int32_t hist[];  // [E + 1]; hist[E] counts bad ids
   const int tile = blockIdx.x;
-  for (int e = threadIdx.x; e <= num_experts; e += kLayoutThreads) hist[e] = 0;
-  __syncthreads();
-  // All of this thread's ids are loaded before the first LDS update, so the
-  // loads are in flight together.
-  constexpr int kPer = kLayoutTile / kLayoutThreads;
-  const int begin = tile * kLayoutTile + threadIdx.x;
-  int ids[kPer];
+  // All of this thread's ids are loaded before the first LDS update.
+  const int64_t begin = static_cast<int64_t>(tile) * kTile + threadIdx.x;
+  int ids[kRounds];
 #pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int i = begin + r * kLayoutThreads;
-    ids[r] = i < n ? topk_idx[i] : -2;
+  for (int r = 0; r < kRounds; ++r) {
+    const int64_t i = begin + r * kThreads;
+    ids[r] = i < n ? topk_idx[i] : 0;
   }
+  for (int e = threadIdx.x; e <= num_experts; e += kThreads) hist[e] = 0;
+  __syncthreads();
 #pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    if (ids[r] == -2 && begin + r * kLayoutThreads >= n) continue;
+  for (int r = 0; r < kRounds; ++r) {
+    if (begin + r * kThreads >= n) continue;
     const int e = ids[r];
-    const int key = static_cast<unsigned>(e) < static_cast<unsigned>(num_experts) ? e : num_experts;
-    atomicAdd(&hist[key], 1);
+    atomicAdd(&hist[static_cast<unsigned>(e) < static_cast<unsigned>(num_experts) ? e : num_experts], 1);
   }
   __syncthreads();
   int32_t* row = tile_count + static_cast<size_t>(tile) * num_experts;
-  for (int e = threadIdx.x; e < num_experts; e += kLayoutThreads) row[e] = hist[e];
+  for (int e = threadIdx.x; e < num_experts; e += kThreads) row[e] = hist[e];
   if (threadIdx.x == 0) tile_bad[tile] = hist[num_experts];
 }
 
-__global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
+template <int kWaves, int kRounds>
+__global__ __launch_bounds__(kWaves * kWave) void layout_rank_kernel(
     const int32_t* __restrict__ topk_idx, int32_t n, int32_t num_experts, int32_t epr,
     int32_t ranks, int32_t id_bits, int32_t num_tiles, const int32_t* __restrict__ tile_count,
     const int32_t* __restrict__ tile_bad, int32_t* __restrict__ token_per_expert,
     int32_t* __restrict__ token_per_rank, int32_t* __restrict__ send_token_idx,
     int32_t* __restrict__ bad_count) {
+  constexpr int kThreads = kWaves * kWave;
+  constexpr int kSegment = kRounds * kWave;
+  constexpr int kTile = kWaves * kSegment;
+  constexpr int kB = kRounds < kBatch ? kRounds : kBatch;
+  static_assert(kRounds % kB == 0, "rounds come in batches");
   extern __shared__ int32_t lds[];
-  constexpr int kWaves = kLayoutThreads / kWave;
-  int32_t* wave_cnt = lds;                       // [kWaves][E]
-  int32_t* base = lds + kWaves * num_experts;    // [E]
+  int32_t* wave_cnt = lds;                     // [kWaves][E]
+  int32_t* base = lds + kWaves * num_experts;  // [E]
   __shared__ int32_t block_bad;
 
   const int tid = threadIdx.x;
@@ -71,9 +83,18 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
   const int wave = uniform(tid / kWave);
   const int tile = blockIdx.x;
 
-  // Starting count of every expert for this tile: the sum over earlier
-  // tiles, 16 independent loads in flight per thread per batch.
-  for (int e = tid; e < num_experts; e += kLayoutThreads) {
+  // This wave's ids, loaded first so they are in flight meanwhile.
+  const int64_t seg_begin = static_cast<int64_t>(tile) * kTile + static_cast<int64_t>(wave) * kSegment;
+  int ids[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int64_t i = seg_begin + r * kWave + lane;
+    ids[r] = i < n ? topk_idx[i] : -1;
+  }
+
+  // Starting count of every expert for this tile: the sum of the earlier
+  // tiles' histograms, 16 independent loads in flight per thread per batch.
+  for (int e = tid; e < num_experts; e += kThreads) {
     int s = 0;
     for (int t0 = 0; t0 < tile; t0 += 16) {
       int v[16];
@@ -91,48 +112,47 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
   __syncthreads();
 
   // Per wave: stable rank of each entry among earlier entries of this wave's
-  // segment with the same expert id.
+  // segment with the same expert id.  Invalid entries get rank -1.
   int32_t* my_cnt = wave_cnt + wave * num_experts;
-  const int seg_begin = tile * kLayoutTile + wave * kLayoutSegment;
-  int local[kLayoutRounds];
-  int key[kLayoutRounds];
-  int ids[kLayoutRounds];
+  int local[kRounds];
   int my_bad = 0;
-  // All rounds' ids are loaded first (in flight together); the rounds then
-  // only touch LDS.
 #pragma unroll
-  for (int r = 0; r < kLayoutRounds; ++r) {
-    const int i = seg_begin + r * kWave + lane;
-    ids[r] = i < n ? topk_idx[i] : -1;
-  }
+  for (int b0 = 0; b0 < kRounds; b0 += kB) {
+    int ret[kB];
+    int leader[kB];
+    int below[kB];
 #pragma unroll
-  for (int r = 0; r < kLayoutRounds; ++r) {
-    const int i = seg_begin + r * kWave + lane;
-    const bool in_range = i < n;
-    const int e = ids[r];
-    const bool valid = in_range && static_cast<unsigned>(e) < static_cast<unsigned>(num_experts);
-    my_bad += (in_range && !valid) ? 1 : 0;
-    uint64_t peers = __ballot(valid);
-    for (int b = 0; b < id_bits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t set = __ballot(bit);
-      peers &= bit ? set : ~set;
+    for (int u = 0; u < kB; ++u) {
+      const int r = b0 + u;
+      const int64_t i = seg_begin + r * kWave + lane;
+      const int e = ids[r];
+      const bool in_range = i < n;
+      const bool valid = in_range && static_cast<unsigned>(e) < static_cast<unsigned>(num_experts);
+      my_bad += (in_range && !valid) ? 1 : 0;
+      uint64_t peers = __ballot(valid);
+      for (int b = 0; b < id_bits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t set = __ballot(bit);
+        peers &= bit ? set : ~set;
+      }
+      // For a valid lane, `peers` is the set of valid lanes with the same id;
+      // its highest lane is the group's leader.
+      below[u] = valid ? lanes_below(peers) : -1;
+      leader[u] = valid ? 63 - __builtin_clzll(peers) : lane;
+      ret[u] = 0;
+      if (valid && leader[u] == lane) ret[u] = atomicAdd(&my_cnt[e], __popcll(peers));
     }
-    // For a valid lane, `peers` is the set of valid lanes with the same id.
-    const int below = lanes_below(peers);
-    const int group = __popcll(peers);
-    const int prev = valid ? my_cnt[e] : 0;
-    local[r] = prev + below;
-    key[r] = valid ? e : -1;
-    // The group's highest lane advances the counter; the wave's LDS reads of
-    // this round are issued before this write.
-    if (valid && below == group - 1) my_cnt[e] = prev + group;
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int start = __shfl(ret[u], leader[u], kWave);
+      local[b0 + u] = below[u] < 0 ? -1 : start + below[u];
+    }
   }
   if (my_bad) atomicAdd(&block_bad, my_bad);
   __syncthreads();
 
   // Exclusive scan over the waves, on top of the tile base.
-  for (int e = tid; e < num_experts; e += kLayoutThreads) {
+  for (int e = tid; e < num_experts; e += kThreads) {
     int s = base[e];
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
@@ -145,14 +165,14 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
   __syncthreads();
 
 #pragma unroll
-  for (int r = 0; r < kLayoutRounds; ++r) {
-    const int i = seg_begin + r * kWave + lane;
-    if (i < n) send_token_idx[i] = key[r] >= 0 ? my_cnt[key[r]] + local[r] : -1;
+  for (int r = 0; r < kRounds; ++r) {
+    const int64_t i = seg_begin + r * kWave + lane;
+    if (i < n) send_token_idx[i] = local[r] >= 0 ? my_cnt[ids[r]] + local[r] : -1;
   }
 
   if (tile == num_tiles - 1) {
-    for (int e = tid; e < num_experts; e += kLayoutThreads) token_per_expert[e] = base[e];
-    for (int r = tid; r < ranks; r += kLayoutThreads) {
+    for (int e = tid; e < num_experts; e += kThreads) token_per_expert[e] = base[e];
+    for (int r = tid; r < ranks; r += kThreads) {
       int s = 0;
       for (int j = 0; j < epr; ++j) s += base[r * epr + j];
       token_per_rank[r] = s;
@@ -165,30 +185,46 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
   }
 }
 
+template <int kWaves, int kRounds>
+hipError_t launch_shape(const int32_t* topk_idx, int32_t n, int32_t num_experts, int32_t epr,
+                        int32_t ranks, int32_t* token_per_expert, int32_t* token_per_rank,
+                        int32_t* send_token_idx, int32_t* bad_count, void* workspace,
+                        hipStream_t stream) {
+  constexpr int kThreads = kWaves * kWave;
+  constexpr int64_t kTile = static_cast<int64_t>(kThreads) * kRounds;
+  const int num_tiles = n <= 0 ? 1 : static_cast<int>((n + kTile - 1) / kTile);
+  int32_t* tile_count = static_cast<int32_t*>(workspace);
+  int32_t* tile_bad =
+      tile_count == nullptr ? nullptr : tile_count + static_cast<size_t>(num_tiles - 1) * num_experts;
+  if (num_tiles > 1) {
+    const size_t lds = static_cast<size_t>(num_experts + 1) * sizeof(int32_t);
+    hipLaunchKernelGGL((layout_count_kernel<kWaves, kRounds>), dim3(num_tiles - 1), dim3(kThreads), lds,
+                       stream, topk_idx, n, num_experts, tile_count, tile_bad);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  int id_bits = 0;
+  while ((1 << id_bits) < num_experts) ++id_bits;
+  const size_t lds = static_cast<size_t>(kWaves + 1) * num_experts * sizeof(int32_t);
+  hipLaunchKernelGGL((layout_rank_kernel<kWaves, kRounds>), dim3(num_tiles), dim3(kThreads), lds, stream,
+                     topk_idx, n, num_experts, epr, ranks, id_bits, num_tiles, tile_count, tile_bad,
+                     token_per_expert, token_per_rank, send_token_idx, bad_count);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_layout(const int32_t* topk_idx, int32_t n, int32_t num_experts, int32_t epr,
                          int32_t ranks, int32_t* token_per_expert, int32_t* token_per_rank,
                          int32_t* send_token_idx, int32_t* bad_count, void* workspace,
                          hipStream_t stream) {
-  const int num_tiles = static_cast<int>(layout_num_tiles(n));
-  int32_t* tile_count = static_cast<int32_t*>(workspace);
-  int32_t* tile_bad =
-      tile_count == nullptr ? nullptr : tile_count + static_cast<size_t>(num_tiles - 1) * num_experts;
-  if (num_tiles > 1) {
-    const size_t lds = static_cast<size_t>(num_experts + 1) * sizeof(int32_t);
-    hipLaunchKernelGGL(layout_count_kernel, dim3(num_tiles - 1), dim3(kLayoutThreads), lds, stream,
-                       topk_idx, n, num_experts, tile_count, tile_bad);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+  const LayoutShape shape = layout_shape(num_experts);
+  if (shape.waves == 16) {
+    return launch_shape<16, 2>(topk_idx, n, num_experts, epr, ranks, token_per_expert, token_per_rank,
+                               send_token_idx, bad_count, workspace, stream);
   }
-  int id_bits = 0;
-  while ((1 << id_bits) < num_experts) ++id_bits;
-  const size_t lds = static_cast<size_t>(kLayoutThreads / kWave + 1) * num_experts * sizeof(int32_t);
-  hipLaunchKernelGGL(layout_rank_kernel, dim3(num_tiles), dim3(kLayoutThreads), lds, stream,
-                     topk_idx, n, num_experts, epr, ranks, id_bits, num_tiles, tile_count, tile_bad,
-                     token_per_expert, token_per_rank, send_token_idx, bad_count);
-  return hipGetLastError();
+  return launch_shape<4, 8>(topk_idx, n, num_experts, epr, ranks, token_per_expert, token_per_rank,
+                            send_token_idx, bad_count, workspace, stream);
 }
 
 }  // namespace moe

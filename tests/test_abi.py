@@ -53,8 +53,11 @@ def test_recv_row_bytes_errors(M):
     assert M._lib.moe_recv_row_bytes(8, 0, None) == 1
 
 
+# Tiles hold 2048 entries; the workspace holds (tiles - 1) rows of E + 1
+# counts.
 @pytest.mark.parametrize("bs,k,e,expect", [(4096, 8, 256, 15 * 257 * 4), (0, 1, 1, 0), (256, 8, 16, 0),
-                                           (257, 8, 16, 17 * 4), (16384, 8, 256, 63 * 257 * 4)])
+                                           (257, 8, 16, 1 * 17 * 4), (16384, 8, 256, 63 * 257 * 4),
+                                           (5000, 8, 1024, 19 * 1025 * 4)])
 def test_layout_workspace_bytes(M, bs, k, e, expect):
     assert M.moe_layout_workspace_bytes(bs, k, e) == expect
 
@@ -69,19 +72,19 @@ P = 0x100000  # a non-NULL, 256-byte aligned stand-in pointer (never dereference
 
 
 def test_layout_rejects_on_host(M):
+    # every call below has an invalid argument, so it returns before any HIP call
     L = M._lib
-    ws = M.moe_layout_workspace_bytes(4096, 8, 256)
-    assert L.moe_layout(P, -1, 8, 16, 16, P, P, P, None, P, ws, None) == 2
-    assert L.moe_layout(P, 16, 0, 16, 16, P, P, P, None, P, ws, None) == 2
-    assert L.moe_layout(P, 16, 33, 16, 16, P, P, P, None, P, ws, None) == 7
-    assert L.moe_layout(P, 16, 8, 0, 16, P, P, P, None, P, ws, None) == 2
-    assert L.moe_layout(P, 16, 8, 2049, 1, P, P, P, None, P, ws, None) == 7
-    assert L.moe_layout(P, 16, 8, 16, 16, None, P, P, None, P, ws, None) == 1
-    assert L.moe_layout(None, 16, 8, 16, 16, P, P, P, None, P, ws, None) == 1
-    assert L.moe_layout(P, 4096, 8, 16, 16, P, P, P, None, P, ws - 4, None) == 5
-    assert L.moe_layout(P, 4096, 8, 16, 16, P, P, P, None, None, ws, None) == 1
-    assert L.moe_layout(P + 2, 16, 8, 16, 16, P, P, P, None, P, ws, None) == 3
-    assert L.moe_layout(P, 16, 8, 16, 16, P, P, P, P + 1, P, ws, None) == 3
+    assert L.moe_layout(P, -1, 8, 16, 16, P, P, P, None, None, 0, None) == 2
+    assert L.moe_layout(P, 16, 0, 16, 16, P, P, P, None, None, 0, None) == 2
+    assert L.moe_layout(P, 16, 33, 16, 16, P, P, P, None, None, 0, None) == 7
+    assert L.moe_layout(P, 16, 8, 0, 16, P, P, P, None, None, 0, None) == 2
+    assert L.moe_layout(P, 16, 8, 2049, 1, P, P, P, None, None, 0, None) == 7
+    assert L.moe_layout(P, 16, 8, 16, 16, None, P, P, None, None, 0, None) == 1
+    assert L.moe_layout(P, 16, 8, 16, 16, P, None, P, None, None, 0, None) == 1
+    assert L.moe_layout(None, 16, 8, 16, 16, P, P, P, None, None, 0, None) == 1
+    assert L.moe_layout(P, 16, 8, 16, 16, P, P, None, None, None, 0, None) == 1
+    assert L.moe_layout(P + 2, 16, 8, 16, 16, P, P, P, None, None, 0, None) == 3
+    assert L.moe_layout(P, 16, 8, 16, 16, P, P, P, P + 1, None, 0, None) == 3
 
 
 def test_notify_rejects_on_host(M):

@@ -129,10 +129,17 @@ RANDOM_CASES = [
     (108, 5, 16384, 3, 8, 2, "uniform", 0.0, "bf16", True),
     (109, 5, 16384, 3, 8, 2, "uniform", 0.0, "fp16", False),
     (110, 256, 96, 8, 32, 4, "zipf1.2", 0.0, "fp16", True),
-    (111, 257, 40, 8, 16, 4, "dup", 0.0, "bf16", True),      # n = 2056: one full tile + ragged
+    # layout tiles hold 2048 entries (16 waves x 2 rounds up to 512 experts,
+    # 4 waves x 8 rounds beyond)
+    (111, 257, 40, 8, 16, 4, "dup", 0.0, "bf16", True),      # n = 2056: a full tile + 8 entries
     (112, 512, 40, 4, 16, 4, "dup", 0.0, "bf16", False),     # n = 2048: exactly one tile
-    (113, 4100, 24, 8, 64, 8, "dup", 0.2, "bf16", True),     # 17 tiles, bad ids across tiles
+    (113, 4100, 24, 8, 64, 8, "dup", 0.2, "bf16", True),     # 17 tiles, bad ids in all of them
     (114, 33, 72, 5, 7, 7, "dup", 0.0, "fp16", True),
+    (115, 4096, 16, 8, 64, 8, "dup", 0.0, "bf16", False),    # n = 32768: 16 full tiles
+    (116, 600, 16, 8, 1024, 8, "dup", 0.05, "bf16", True),   # E > 512: 4-wave tiles, n = 4800
+    (117, 256, 16, 8, 513, 1, "hot", 0.0, "bf16", True),     # E = 513, every entry to expert 0
+    (118, 9000, 16, 8, 32, 4, "zipf1.2", 0.01, "bf16", True),  # n = 72000: 36 tiles
+    (119, 40000, 16, 8, 64, 8, "dup", 0.0, "bf16", False),   # n = 320000: 157 tiles
 ]
 
 
