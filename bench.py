@@ -42,6 +42,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "dispatch": os.path.join(ROOT, "combine_moe_layout_03_amd", "csrc", "dispatch.hip"),
     "combine": os.path.join(ROOT, "combine_moe_layout_03_amd", "csrc", "combine.hip"),
+    "fused": os.path.join(ROOT, "combine_moe_layout_03_amd", "csrc", "fused.hip"),
 }
 
 
@@ -166,6 +167,8 @@ def main(argv=None) -> int:
     ap.add_argument("--flush-mib", type=int, default=1024)
     ap.add_argument("--event-flags", default="nofence", choices=["nofence", "default"],
                     help="HIP event creation flags for the stage timers")
+    ap.add_argument("--path", default="separate", choices=["separate", "fused"],
+                    help="layout, notify and dispatch as three launches, or one fused launch")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, then WRITE_SIZE) of a bench "
                          "run into profiles/traffic_*.json and exit")
@@ -205,11 +208,24 @@ def main(argv=None) -> int:
     def do_flush():
         torch.sum(flush, dim=0, out=flush_out)
 
+    fused = args.path == "fused"
+    if fused and not M.moe_fused_supported(w.bs, w.hidden, w.topk, w.expert_num_per_rank, w.rank_size,
+                                           torch.bfloat16, quant):
+        log("the fused kernel does not apply to this shape; the fused entry point runs the three stages")
+
+    def first_stages():
+        if fused:
+            buf.layout_notify_dispatch(x, idx)
+        else:
+            buf.layout(idx)
+            buf.notify()
+            buf.dispatch(x, idx)
+
     # warm-up (also the first touch of every buffer)
     log(f"warm-up x{args.warmup}")
     for _ in range(args.warmup):
         do_flush()
-        buf.run(x, idx, wts)
+        buf.run(x, idx, wts, fused=fused)
     torch.cuda.synchronize()
 
     # timed steps
@@ -221,12 +237,19 @@ def main(argv=None) -> int:
     for i in range(args.steps):
         e = ev[i]
         do_flush()
-        hev.record(e[0], stream)
-        buf.layout(idx)
-        buf.notify()
-        hev.record(e[1], stream)
-        buf.dispatch(x, idx)
-        hev.record(e[2], stream)
+        if fused:
+            # one launch for layout + notify + dispatch: timed as one interval
+            hev.record(e[0], stream)
+            hev.record(e[1], stream)
+            first_stages()
+            hev.record(e[2], stream)
+        else:
+            hev.record(e[0], stream)
+            buf.layout(idx)
+            buf.notify()
+            hev.record(e[1], stream)
+            buf.dispatch(x, idx)
+            hev.record(e[2], stream)
         do_flush()
         hev.record(e[3], stream)
         buf.combine(idx, wts)
@@ -244,7 +267,7 @@ def main(argv=None) -> int:
     e0, e1 = hev.new(), hev.new()
     hev.record(e0, stream)
     for _ in range(args.steps):
-        buf.run(x, idx, wts)
+        buf.run(x, idx, wts, fused=fused)
     hev.record(e1, stream)
     torch.cuda.synchronize()
     unflushed_ms = hev.ms(e0, e1) / args.steps
@@ -269,13 +292,21 @@ def main(argv=None) -> int:
     b_dis, b_com, b_lay = algorithmic_bytes(w.bs, w.hidden, w.topk, quant)
     dis_mean = statistics.mean(dis_ms)
     com_mean = statistics.mean(com_ms)
-    dom = "dispatch" if dis_mean >= com_mean else "combine"
-    dom_ms = dis_mean if dom == "dispatch" else com_mean
-    dom_bytes = b_dis if dom == "dispatch" else b_com
+    # the launch that carries the dispatch: the dispatch kernel, or the fused
+    # kernel (which also reads the ids for the layout and writes the slots)
+    first = "fused" if fused else "dispatch"
+    b_first = b_dis + b_lay if fused else b_dis
+    dom = first if dis_mean >= com_mean else "combine"
+    dom_ms = dis_mean if dom == first else com_mean
+    dom_bytes = b_first if dom == first else b_com
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     mode_tag = "int8" if quant else "pass"
     traffic = load_traffic(dom, args.workload, mode_tag)
     dc_gbps = (b_dis + b_com) / ((dis_mean + com_mean) * 1e-3) / 1e9
+    if fused:
+        stages = (("layout+notify+dispatch", dis_ms), ("combine", com_ms))
+    else:
+        stages = (("layout+notify", lay_ms), ("dispatch", dis_ms), ("combine", com_ms))
 
     cpu = None
     if args.cpu_budget > 0:
@@ -302,6 +333,8 @@ def main(argv=None) -> int:
                    "dispatch": "int8" if quant else "passthrough", "out_dtype": "bf16",
                    "parallelism": "1 GPU, ranks are logical partitions of one receive buffer"},
         "step": "layout + notify + dispatch + combine, caches flushed before the step and before combine",
+        "path": ("layout+notify+dispatch fused in one launch, then combine" if fused
+                 else "four launches: layout, notify, dispatch, combine"),
         "timer": f"HIP events on the kernels' stream ({args.event_flags})",
         "dispatch_combine_tokens_per_s": w.bs / ((dis_mean + com_mean) * 1e-3),
         "dispatch_combine_hbm_gbps": dc_gbps,
@@ -309,9 +342,10 @@ def main(argv=None) -> int:
         "stages_us": {
             name: {"mean": statistics.mean(v) * 1e3, "p10": pct(v, 0.1) * 1e3,
                    "p50": pct(v, 0.5) * 1e3, "p90": pct(v, 0.9) * 1e3}
-            for name, v in (("layout+notify", lay_ms), ("dispatch", dis_ms), ("combine", com_ms))
+            for name, v in stages
         },
-        "algorithmic_bytes": {"dispatch": b_dis, "combine": b_com, "layout": b_lay},
+        "algorithmic_bytes": ({"fused": b_first, "combine": b_com} if fused else
+                              {"dispatch": b_dis, "combine": b_com, "layout": b_lay}),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
         "unflushed_ms_per_step": unflushed_ms,

@@ -26,7 +26,7 @@ __all__ = [
     "MOE_BF16", "MOE_FP16", "MOE_FP32", "MOE_INT8_ROWSCALE", "MoeEpError", "LIB_PATH",
     "moe_recv_row_bytes", "moe_layout_workspace_bytes", "moe_layout", "moe_notify",
     "moe_dispatch", "moe_combine", "moe_status_str", "moe_last_hip_error", "EpBuffers",
-    "dtype_code",
+    "dtype_code", "moe_fused_supported", "moe_layout_notify_dispatch",
 ]
 
 MOE_BF16, MOE_FP16, MOE_FP32, MOE_INT8_ROWSCALE = 0, 1, 2, 3
@@ -49,6 +49,9 @@ _SIGS = {
                      _INT),
     "moe_combine": ([_P, _INT, _SZ, _I32, _I32, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _INT, _P],
                     _INT),
+    "moe_fused_supported": ([_I32, _I32, _I32, _I32, _I32, _INT, _INT, ctypes.POINTER(_INT)], _INT),
+    "moe_layout_notify_dispatch": ([_P, _INT, _I32, _I32, _I32, _P, _I32, _I32, _INT, _P, _P, _P, _P, _P, _P,
+                                    _P, _P, _P, _SZ, _P, _SZ, _P], _INT),
     "moe_status_str": ([_INT], ctypes.c_char_p),
     "moe_last_hip_error": ([], _INT),
 }
@@ -195,6 +198,38 @@ def moe_combine(recv_x: torch.Tensor, recv_type: int, hidden: int, topk_idx: tor
         dtype_code(out.dtype), _stream(stream)))
 
 
+def moe_fused_supported(bs: int, hidden: int, topk: int, expert_num_per_rank: int, rank_size: int,
+                        x_dtype: torch.dtype, quant_int8: bool) -> bool:
+    out = _INT(0)
+    _check("moe_fused_supported", _lib.moe_fused_supported(
+        bs, hidden, topk, expert_num_per_rank, rank_size, dtype_code(x_dtype), 1 if quant_int8 else 0,
+        ctypes.byref(out)))
+    return bool(out.value)
+
+
+def moe_layout_notify_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, expert_num_per_rank: int,
+                               rank_size: int, quant_int8: bool, token_per_expert: torch.Tensor,
+                               token_per_rank: torch.Tensor, send_token_idx: torch.Tensor,
+                               bad_id_count: Optional[torch.Tensor], put_offset: torch.Tensor,
+                               recv_count: torch.Tensor, recv_base: torch.Tensor,
+                               recv_token_per_expert: torch.Tensor, recv_x: torch.Tensor,
+                               workspace: torch.Tensor, stream=None) -> None:
+    if x.dim() != 2 or topk_idx.dim() != 2:
+        raise ValueError("x must be [bs, hidden] and topk_idx [bs, topk]")
+    bs, hidden = x.shape
+    topk = topk_idx.shape[1]
+    i32 = torch.int32
+    _check("moe_layout_notify_dispatch", _lib.moe_layout_notify_dispatch(
+        _dev(x, "x"), dtype_code(x.dtype), bs, hidden, topk, _dev(topk_idx, "topk_idx", i32),
+        expert_num_per_rank, rank_size, 1 if quant_int8 else 0,
+        _dev(token_per_expert, "token_per_expert", i32), _dev(token_per_rank, "token_per_rank", i32),
+        _dev(send_token_idx, "send_token_idx", i32), _dev(bad_id_count, "bad_id_count", i32, optional=True),
+        _dev(put_offset, "put_offset", i32), _dev(recv_count, "recv_count", i32),
+        _dev(recv_base, "recv_base", i32), _dev(recv_token_per_expert, "recv_token_per_expert", i32),
+        _dev(recv_x, "recv_x"), recv_x.numel() * recv_x.element_size(), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 class EpBuffers:
     """Device buffers of one pipeline shape, allocated once through torch.
 
@@ -241,9 +276,18 @@ class EpBuffers:
         moe_combine(self.recv_x, self.recv_type, self.hidden, topk_idx, topk_w, self.send_token_idx,
                     self.put_offset, self.recv_base, self.epr, self.ranks, self.out, stream)
 
-    def run(self, x, topk_idx, topk_w, stream=None):
-        self.layout(topk_idx, stream)
-        self.notify(stream)
-        self.dispatch(x, topk_idx, stream)
+    def layout_notify_dispatch(self, x, topk_idx, stream=None):
+        moe_layout_notify_dispatch(x, topk_idx, self.epr, self.ranks, self.quant_int8, self.token_per_expert,
+                                   self.token_per_rank, self.send_token_idx, self.bad_id_count,
+                                   self.put_offset, self.recv_count, self.recv_base,
+                                   self.recv_token_per_expert, self.recv_x, self.workspace, stream)
+
+    def run(self, x, topk_idx, topk_w, stream=None, fused: bool = False):
+        if fused:
+            self.layout_notify_dispatch(x, topk_idx, stream)
+        else:
+            self.layout(topk_idx, stream)
+            self.notify(stream)
+            self.dispatch(x, topk_idx, stream)
         self.combine(topk_idx, topk_w, stream)
         return self.out

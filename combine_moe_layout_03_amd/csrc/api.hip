@@ -190,6 +190,123 @@ int moe_combine(const void* recv_x, moe_dtype recv_type, size_t recv_x_bytes, in
                                         static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+// Whether the one-kernel form applies (host logic only).
+bool fused_applies(int32_t bs, int32_t hidden, int32_t topk) {
+  return bs >= 1 && hidden <= moe::kFusedMaxHidden &&
+         static_cast<int64_t>(bs) * topk <= moe::kFusedMaxEntries;
+}
+
+// Tokens per workgroup and workgroups of the one kernel: one workgroup per
+// CU (fewer for small batches), more when the per-token LDS of a group would
+// exceed kFusedMaxLds.
+int fused_grid(int32_t bs, int32_t topk, int32_t num_experts, int cus, int32_t* tokens_per_group) {
+  const size_t fixed = moe::fused_lds_bytes(num_experts, 0, topk);
+  const size_t per_token = moe::fused_lds_bytes(num_experts, 1, topk) - fixed;
+  const int64_t t_max = static_cast<int64_t>((moe::kFusedMaxLds - fixed) / per_token);
+  int64_t groups = bs < cus ? bs : cus;
+  if (groups < 1) groups = 1;
+  int64_t tpg = (bs + groups - 1) / groups;
+  if (tpg > t_max) tpg = t_max;
+  groups = (bs + tpg - 1) / tpg;
+  *tokens_per_group = static_cast<int32_t>(tpg);
+  return static_cast<int>(groups);
+}
+
+}  // namespace
+
+int moe_fused_supported(int32_t bs, int32_t hidden, int32_t topk, int32_t expert_num_per_rank, int32_t ranks,
+                        moe_dtype x_type, int quant_int8, int* supported) {
+  if (!supported) return MOE_ERR_NULL_PTR;
+  int st = check_tokens(bs, topk);
+  if (st) return st;
+  if ((st = check_experts(expert_num_per_rank, ranks))) return st;
+  if ((st = check_hidden(hidden))) return st;
+  if (x_type != MOE_BF16 && x_type != MOE_FP16) return MOE_ERR_BAD_DTYPE;
+  if (quant_int8 != 0 && quant_int8 != 1) return MOE_ERR_BAD_DTYPE;
+  *supported = fused_applies(bs, hidden, topk) ? 1 : 0;
+  return MOE_OK;
+}
+
+int moe_layout_notify_dispatch(const void* x, moe_dtype x_type, int32_t bs, int32_t hidden, int32_t topk,
+                               const int32_t* topk_idx, int32_t epr, int32_t ranks, int quant_int8,
+                               int32_t* token_per_expert, int32_t* token_per_rank, int32_t* send_token_idx,
+                               int32_t* bad_id_count, int32_t* put_offset, int32_t* recv_count,
+                               int32_t* recv_base, int32_t* recv_token_per_expert, void* recv_x,
+                               size_t recv_x_bytes, void* workspace, size_t workspace_bytes, void* stream) {
+  if (x_type != MOE_BF16 && x_type != MOE_FP16) return MOE_ERR_BAD_DTYPE;
+  if (quant_int8 != 0 && quant_int8 != 1) return MOE_ERR_BAD_DTYPE;
+  const moe_dtype recv_type = quant_int8 ? MOE_INT8_ROWSCALE : x_type;
+  int st = check_tokens(bs, topk);
+  if (st) return st;
+  if ((st = check_experts(epr, ranks))) return st;
+  if ((st = check_hidden(hidden))) return st;
+  if (!token_per_expert || !token_per_rank || !put_offset || !recv_count || !recv_base ||
+      !recv_token_per_expert)
+    return MOE_ERR_NULL_PTR;
+  if (bs > 0 && (!x || !topk_idx || !send_token_idx || !recv_x)) return MOE_ERR_NULL_PTR;
+  const int64_t n = static_cast<int64_t>(bs) * topk;
+  const bool one_kernel = fused_applies(bs, hidden, topk);
+  if (!one_kernel) {
+    const size_t need_ws = moe::layout_workspace_bytes(n, epr * ranks);
+    if (workspace_bytes < need_ws) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (need_ws > 0 && !workspace) return MOE_ERR_NULL_PTR;
+  }
+  size_t rb = 0;
+  if ((st = row_bytes(hidden, recv_type, &rb))) return st;
+  if (recv_x_bytes < rb * static_cast<size_t>(bs) * static_cast<size_t>(topk)) return MOE_ERR_BUFFER_TOO_SMALL;
+  if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(topk_idx, 4) || !aligned(send_token_idx, 4) ||
+      !aligned(workspace, 4) || !aligned(token_per_expert, 4) || !aligned(token_per_rank, 4) ||
+      !aligned(bad_id_count, 4) || !aligned(put_offset, 4) || !aligned(recv_count, 4) ||
+      !aligned(recv_base, 4) || !aligned(recv_token_per_expert, 4))
+    return MOE_ERR_BAD_ALIGN;
+
+  if (!one_kernel) {
+    if ((st = moe_layout(topk_idx, bs, topk, epr, ranks, token_per_expert, token_per_rank, send_token_idx,
+                         bad_id_count, workspace, workspace_bytes, stream)))
+      return st;
+    if ((st = moe_notify(token_per_expert, epr, ranks, put_offset, recv_count, recv_base,
+                         recv_token_per_expert, stream)))
+      return st;
+    return moe_dispatch(x, x_type, bs, hidden, topk, topk_idx, send_token_idx, put_offset, recv_base, epr,
+                        ranks, quant_int8, recv_x, recv_x_bytes, stream);
+  }
+
+  int device = 0, cus = 0;
+  hipError_t err = hipGetDevice(&device);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (err != hipSuccess) return hip_status(err);
+  moe::FusedArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.topk_idx = topk_idx;
+  a.bs = bs;
+  a.hidden = hidden;
+  a.k = topk;
+  a.epr = epr;
+  a.ranks = ranks;
+  a.num_experts = epr * ranks;
+  int id_bits = 0;
+  while ((1 << id_bits) < a.num_experts) ++id_bits;
+  a.id_bits = id_bits;
+  const int groups = fused_grid(bs, topk, a.num_experts, cus, &a.tokens_per_group);
+  a.ids_aligned16 = aligned(topk_idx, 16) ? 1 : 0;
+  a.token_per_expert = token_per_expert;
+  a.token_per_rank = token_per_rank;
+  a.send_token_idx = send_token_idx;
+  a.bad_count = bad_id_count;
+  a.put_offset = put_offset;
+  a.recv_count = recv_count;
+  a.recv_base = recv_base;
+  a.recv_token_per_expert = recv_token_per_expert;
+  a.recv = static_cast<uint8_t*>(recv_x);
+  a.row_bytes = static_cast<int64_t>(rb);
+  a.cap_rows = static_cast<int64_t>(recv_x_bytes / rb);
+  a.scale_off = static_cast<int32_t>(align32(hidden));
+  const moe::Half xt = x_type == MOE_FP16 ? moe::Half::kFp16 : moe::Half::kBf16;
+  return hip_status(moe::launch_fused(a, xt, quant_int8 != 0, groups, static_cast<hipStream_t>(stream)));
+}
+
 const char* moe_status_str(int status) {
   switch (status) {
     case MOE_OK: return "ok";

@@ -1,0 +1,310 @@
+// Layout + notify + dispatch in one launch: the single-kernel, low-latency
+// form of the EP pipeline ("UMDK/CAM communication acceleration library deep
+// analysis v2", section 3.2, moe_dispatch_lowlatency_zb: local expert counts,
+// count exchange, global count matrix and prefix sum, then the token writes,
+// all inside one kernel), with the stage definitions of sections 2.3-2.5.
+// Results are identical to moe_layout, moe_notify and moe_dispatch called in
+// turn.
+//
+// The pages' kernel synchronises its cores between the phases.  On one
+// MI355X a grid-wide barrier costs more than the work it would save: every
+// workgroup's arrival is a device-scope atomic on one address, and 256-512 of
+// them serialise at the memory side, tens of microseconds.  Counting the ids
+// is cheap next to the rows, so here every workgroup counts all of them
+// itself and no workgroup waits on another:
+//   1. Each thread issues the loads of its first 32 ids, then each wave the
+//      loads of its first token's row; the row arrives while the rest runs.
+//   2. All bs*k ids are counted into two LDS histograms: the entries before
+//      this workgroup's first entry, and the rest.  Their sum is the layout
+//      stage's per-expert totals (with invalid ids in the last bin).
+//   3. An exclusive scan of the totals in LDS is the notify stage: the
+//      receive row of (expert e, slot s) is scan[e] + s.  Workgroup 0 writes
+//      the layout and notify outputs.
+//   4. Wave 0 ranks the workgroup's own entries in entry order: match-any
+//      ballots group equal ids, and the group leader adds the group's size
+//      to the expert's running count (seeded with the counts before the
+//      workgroup), so each entry's slot is its stable rank within its
+//      expert.  The slots go to LDS and to sendTokenIdx.
+//   5. Each wave quantises (or passes through) its tokens and writes every
+//      copy, as the dispatch kernel does.
+// The ids are read once per workgroup from L2 (bs*k*4 bytes each); with one
+// workgroup per CU that is the only redundant work.
+#include <hip/hip_runtime.h>
+
+#include "device_util.h"
+#include "launch.h"
+#include "quant.h"
+
+#pragma clang fp contract(off)
+
+namespace moe {
+namespace {
+
+constexpr int kWaves = kFusedWaves;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kQuads = 8;       // 16-byte id loads per thread in a whole batch
+constexpr int kBatch = kThreads * kQuads * 4;  // ids per whole batch
+constexpr int kTailLoads = 8;  // 4-byte id loads per thread in the rest
+
+// Row t into registers, 16 bytes (8 elements) per chunk, chunk lane + 64 i
+// in v[i].  Chunks past the row's end load its last chunk again (a duplicate
+// changes no maximum and is never stored), so every load is unconditional.
+template <int kVpl>
+__device__ __forceinline__ void load_row(uint4 (&v)[kVpl], const uint16_t* x, int t, int hidden, int lane) {
+  const uint32_t last = static_cast<uint32_t>(hidden >> 3) - 1u;
+  const uint4* src = reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * hidden);
+#pragma unroll
+  for (int i = 0; i < kVpl; ++i) {
+    const uint32_t c = static_cast<uint32_t>(lane + i * kWave);
+    v[i] = src[c < last ? c : last];
+  }
+}
+
+template <bool kFp16, bool kQuant, int kVpl>
+__global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
+  extern __shared__ int32_t lds[];
+  const int E = a.num_experts;
+  int32_t* pre = lds;                     // [E + 1] counts before this group; then running counts
+  int32_t* tot = pre + (E + 1);           // [E + 1] counts from this group on; then totals
+  int32_t* gsc = tot + (E + 1);           // [E + 1] exclusive scan of the totals (gsc[E]: all valid)
+  int32_t* ids_l = gsc + (E + 1);         // [T * k] own entries' ids
+  int32_t* slot_l = ids_l + a.tokens_per_group * a.k;  // [T * k] own entries' slots (-1: dropped)
+  __shared__ int32_t wave_sum[kWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = uniform(tid / kWave);
+  const int group = blockIdx.x;
+  const int n = a.bs * a.k;  // at most kFusedMaxEntries
+  const int t_begin = min(group * a.tokens_per_group, a.bs);
+  const int t_end = min(t_begin + a.tokens_per_group, a.bs);
+  const int e_begin = t_begin * a.k;
+  const int own = (t_end - t_begin) * a.k;
+
+  // 1-2. Histograms of all ids: before this group's first entry, and the
+  //      rest; the group's own ids are also kept in LDS.  Whole batches of
+  //      kQuads * 4 ids per thread are read with unguarded 16-byte loads off
+  //      one base (when the ids are 16-byte aligned), so they issue back to
+  //      back and need one address register; the first batch is issued
+  //      before the row loads, and since loads complete in order, counting
+  //      it waits for the ids only.  The rest of the ids (and all of them
+  //      when unaligned) are read kTailLoads per thread with clamped indices.
+  for (int e = tid; e <= E; e += kThreads) {
+    pre[e] = 0;
+    tot[e] = 0;
+  }
+  __syncthreads();
+  const int e_end = e_begin + own;
+  auto count_one = [&](int i, int e) {
+    const int bin = static_cast<unsigned>(e) < static_cast<unsigned>(E) ? e : E;
+    atomicAdd(i < e_begin ? &pre[bin] : &tot[bin], 1);
+    if (i >= e_begin && i < e_end) ids_l[i - e_begin] = e;
+  };
+  int4 quads[kQuads];
+  auto load_batch = [&](int b) {
+    const int4* src = reinterpret_cast<const int4*>(a.topk_idx + b);
+#pragma unroll
+    for (int u = 0; u < kQuads; ++u) quads[u] = src[u * kThreads + tid];
+  };
+  auto count_batch = [&](int b) {
+#pragma unroll
+    for (int u = 0; u < kQuads; ++u) {
+      const int i = b + 4 * (u * kThreads + tid);
+      count_one(i, quads[u].x);
+      count_one(i + 1, quads[u].y);
+      count_one(i + 2, quads[u].z);
+      count_one(i + 3, quads[u].w);
+    }
+  };
+  // The first token of this wave (waves past the group's last token load
+  // that token's row again and never use it): loaded early, used at the end.
+  uint4 v[kVpl];
+  const int t_first = t_begin + wave;
+  const int t_pre = t_first < t_end ? t_first : t_end - 1;
+  int b = 0;
+  const bool whole = a.ids_aligned16 && n >= kBatch;
+  if (whole) {
+    load_batch(0);
+    load_row<kVpl>(v, a.x, t_pre, a.hidden, lane);
+    count_batch(0);
+    for (b = kBatch; b + kBatch <= n; b += kBatch) {
+      load_batch(b);
+      count_batch(b);
+    }
+  }
+  for (; b < n; b += kThreads * kTailLoads) {
+    int ids[kTailLoads];
+#pragma unroll
+    for (int u = 0; u < kTailLoads; ++u) {
+      const int i = b + u * kThreads + tid;
+      ids[u] = a.topk_idx[i < n ? i : n - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kTailLoads; ++u) {
+      const int i = b + u * kThreads + tid;
+      if (i < n) count_one(i, ids[u]);
+    }
+  }
+  if (!whole) load_row<kVpl>(v, a.x, t_pre, a.hidden, lane);  // few ids: counted first
+  __syncthreads();
+
+  // 3. Totals and their exclusive scan (notify).  Thread t owns the
+  //    contiguous experts [t * per, (t + 1) * per).
+  {
+    const int per = (E + kThreads - 1) / kThreads;  // 1 or 2 (E <= 2048)
+    const int e0 = tid * per;
+    int c0 = 0, c1 = 0;
+    if (e0 < E) c0 = tot[e0] + pre[e0];
+    if (per > 1 && e0 + 1 < E) c1 = tot[e0 + 1] + pre[e0 + 1];
+    const int sum = c0 + c1;
+    const int incl = wave_inclusive_scan(sum, lane);
+    if (lane == kWave - 1) wave_sum[wave] = incl;
+    __syncthreads();
+    int off = 0;
+    for (int w = 0; w < wave; ++w) off += wave_sum[w];
+    const int excl = off + incl - sum;
+    if (e0 < E) {
+      tot[e0] = c0;
+      gsc[e0] = excl;
+    }
+    if (per > 1 && e0 + 1 < E) {
+      tot[e0 + 1] = c1;
+      gsc[e0 + 1] = excl + c0;
+    }
+    if (tid == 0) {
+      int total = 0;
+      for (int w = 0; w < kWaves; ++w) total += wave_sum[w];
+      gsc[E] = total;
+      tot[E] += pre[E];
+    }
+  }
+  __syncthreads();
+  if (group == 0) {
+    for (int e = tid; e < E; e += kThreads) {
+      const int first = (e / a.epr) * a.epr;
+      a.token_per_expert[e] = tot[e];
+      a.recv_token_per_expert[e] = tot[e];
+      a.put_offset[e] = gsc[e] - gsc[first];
+    }
+    for (int r = tid; r < a.ranks; r += kThreads) {
+      const int cnt = gsc[(r + 1) * a.epr] - gsc[r * a.epr];
+      a.recv_base[r] = gsc[r * a.epr];
+      a.recv_count[r] = cnt;
+      a.token_per_rank[r] = cnt;
+    }
+    if (tid == 0 && a.bad_count != nullptr) *a.bad_count = tot[E];
+  }
+
+  // 4. Slots of this group's own entries, in entry order, by wave 0 alone
+  //    (LDS atomics of one wave complete in issue order, which keeps the
+  //    ranks stable across rounds).
+  if (wave == 0) {
+    for (int r0 = 0; r0 < own; r0 += kWave) {
+      const int li = r0 + lane;
+      const bool in_range = li < own;
+      const int e = in_range ? ids_l[li] : -1;
+      const bool valid = in_range && static_cast<unsigned>(e) < static_cast<unsigned>(E);
+      uint64_t peers = __ballot(valid);
+      for (int bit = 0; bit < a.id_bits; ++bit) {
+        const bool on = (e >> bit) & 1;
+        const uint64_t set = __ballot(on);
+        peers &= on ? set : ~set;
+      }
+      const int below = valid ? lanes_below(peers) : 0;
+      const int leader = valid ? 63 - __builtin_clzll(peers) : lane;
+      int ret = 0;
+      if (valid && leader == lane) ret = atomicAdd(&pre[e], __popcll(peers));
+      const int start = __shfl(ret, leader, kWave);
+      if (in_range) {
+        const int slot = valid ? start + below : -1;
+        ids_l[li] = valid ? e : 0;
+        slot_l[li] = slot;
+        a.send_token_idx[e_begin + li] = slot;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 5. Dispatch of this group's tokens: wave w takes tokens w, w + 16, ...
+  const int chunks = a.hidden >> 3;
+  for (int t = t_first; t < t_end; t += kWaves) {
+    if (t != t_first) load_row<kVpl>(v, a.x, t, a.hidden, lane);
+    const int li0 = (t - t_begin) * a.k;
+    if constexpr (!kQuant) {
+      for (int j = 0; j < a.k; ++j) {
+        const int slot = slot_l[li0 + j];
+        if (slot < 0) continue;
+        const int64_t row = static_cast<int64_t>(gsc[ids_l[li0 + j]]) + slot;  // recvBase[rank] + putOffset[e]
+        if (row >= a.cap_rows) continue;
+        uint4* dst = reinterpret_cast<uint4*>(a.recv + row * a.row_bytes);
+#pragma unroll
+        for (int i = 0; i < kVpl; ++i) {
+          const int c = lane + i * kWave;
+          if (c < chunks) dst[c] = v[i];
+        }
+      }
+    } else {
+      u16x2 m2 = {0, 0};
+#pragma unroll
+      for (int i = 0; i < kVpl; ++i) m2 = max_magnitude(m2, v[i]);
+      const uint32_t m = wave_max_u32(m2.x > m2.y ? m2.x : m2.y);
+      float s, inv;
+      row_scale<kFp16>(m, s, inv);
+      uint2 q[kVpl];
+#pragma unroll
+      for (int i = 0; i < kVpl; ++i) q[i] = quantise_chunk<kFp16>(v[i], s);
+      for (int j = 0; j < a.k; ++j) {
+        const int slot = slot_l[li0 + j];
+        if (slot < 0) continue;
+        const int64_t row = static_cast<int64_t>(gsc[ids_l[li0 + j]]) + slot;
+        if (row >= a.cap_rows) continue;
+        uint8_t* base = a.recv + row * a.row_bytes;
+#pragma unroll
+        for (int i = 0; i < kVpl; ++i) {
+          const int c = lane + i * kWave;
+          if (c < chunks) reinterpret_cast<uint2*>(base)[c] = q[i];
+        }
+        if (lane == 0) *reinterpret_cast<float*>(base + a.scale_off) = inv;
+      }
+    }
+  }
+}
+
+template <bool kFp16, bool kQuant>
+const void* pick_kernel(int hidden) {
+  const int per_lane = (hidden / 8 + kWave - 1) / kWave;
+#define MOE_FUSED_CASE(V) \
+  if (per_lane <= V) return reinterpret_cast<const void*>(&fused_kernel<kFp16, kQuant, V>);
+  MOE_FUSED_CASE(1)
+  MOE_FUSED_CASE(2)
+  MOE_FUSED_CASE(4)
+  MOE_FUSED_CASE(8)
+  MOE_FUSED_CASE(12)
+  MOE_FUSED_CASE(14)
+  MOE_FUSED_CASE(16)
+#undef MOE_FUSED_CASE
+  return nullptr;
+}
+
+}  // namespace
+
+size_t fused_lds_bytes(int32_t num_experts, int32_t tokens_per_group, int32_t topk) {
+  return (static_cast<size_t>(3) * (num_experts + 1) + 2u * static_cast<size_t>(tokens_per_group) * topk) *
+         sizeof(int32_t);
+}
+
+hipError_t launch_fused(const FusedArgs& a, Half x_type, bool quant, int groups, hipStream_t stream) {
+  const void* f = nullptr;
+  if (x_type == Half::kFp16) {
+    f = quant ? pick_kernel<true, true>(a.hidden) : pick_kernel<true, false>(a.hidden);
+  } else {
+    f = quant ? pick_kernel<false, true>(a.hidden) : pick_kernel<false, false>(a.hidden);
+  }
+  if (f == nullptr || groups < 1) return hipErrorInvalidValue;
+  const size_t lds = fused_lds_bytes(a.num_experts, a.tokens_per_group, a.k);
+  FusedArgs copy = a;
+  void* args[] = {&copy};
+  return hipLaunchKernel(f, dim3(groups), dim3(kThreads), args, lds, stream);
+}
+
+}  // namespace moe

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "moe_ep.h"
+
 namespace moe {
 
 // ---- layout -------------------------------------------------------------------
@@ -68,5 +70,34 @@ hipError_t launch_dispatch(const RouteArgs& r, const void* x, Half x_type, bool 
 
 hipError_t launch_combine(const RouteArgs& r, const void* recv_x, Recv recv_type,
                           const float* topk_w, void* out, Out out_type, hipStream_t stream);
+
+// ---- fused layout + notify + dispatch ------------------------------------------
+constexpr int kFusedWaves = 16;                 // waves per workgroup
+constexpr int kFusedMaxHidden = 16 * 64 * 8;    // row held in registers: 16 chunks per lane
+constexpr int64_t kFusedMaxEntries = 1 << 19;   // bs * k: every workgroup counts all ids
+constexpr size_t kFusedMaxLds = 64 * 1024;
+static_assert(MOE_MAX_EXPERTS <= 2 * kFusedWaves * 64, "the fused scan gives each thread two experts");
+
+struct FusedArgs {
+  const uint16_t* x;
+  const int32_t* topk_idx;
+  int32_t bs, hidden, k, epr, ranks, num_experts, id_bits;
+  int32_t tokens_per_group;  // T: workgroup g owns tokens [g*T, (g+1)*T)
+  int32_t ids_aligned16;     // topk_idx is 16-byte aligned
+  int32_t* token_per_expert;
+  int32_t* token_per_rank;
+  int32_t* send_token_idx;
+  int32_t* bad_count;
+  int32_t* put_offset;
+  int32_t* recv_count;
+  int32_t* recv_base;
+  int32_t* recv_token_per_expert;
+  uint8_t* recv;
+  int64_t row_bytes, cap_rows;
+  int32_t scale_off;
+};
+
+size_t fused_lds_bytes(int32_t num_experts, int32_t tokens_per_group, int32_t topk);
+hipError_t launch_fused(const FusedArgs& a, Half x_type, bool quant, int groups, hipStream_t stream);
 
 }  // namespace moe

@@ -24,7 +24,7 @@
  * Conventions for every entry point:
  *  - Pointers named as device pointers must point to device memory (or to
  *    memory the device can address); the library never allocates, frees or
- *    keeps device memory, and keeps no state between calls.
+ *    keeps device memory, and keeps no state of its own between calls.
  *  - Arrays are dense, row-major, in the element types given below.
  *  - Work is only enqueued on `stream` (a hipStream_t; NULL means the null
  *    stream) and the call returns without waiting.  Stage order on one stream
@@ -162,6 +162,37 @@ int moe_combine(const void* recvX, moe_dtype recvType, size_t recvXBytes, int32_
                 const int32_t* sendTokenIdx, const int32_t* putOffset, const int32_t* recvBase,
                 int32_t expertNumPerRank, int32_t rankSize, void* out, moe_dtype outType,
                 void* stream);
+
+/* ---- Fused layout + notify + dispatch ------------------------------------ */
+
+/* *supported = 1 if moe_layout_notify_dispatch runs as one kernel for this
+ * shape, 0 if it runs the three stages one after another (bs == 0, hidden
+ * above 8192, or bs * topk above 2^19: every workgroup of the one kernel
+ * reads all bs * topk ids).  Host only; the answer does not depend on the
+ * device. */
+int moe_fused_supported(int32_t bs, int32_t hidden, int32_t topk, int32_t expertNumPerRank,
+                        int32_t rankSize, moe_dtype xType, int quantInt8, int* supported);
+
+/* Stages 1-3 in one launch: the single-kernel low-latency form of the
+ * pipeline ("UMDK/CAM communication acceleration library deep analysis v2",
+ * section 3.2, moe_dispatch_lowlatency_zb: local expert counts, count
+ * exchange, global count matrix and prefix sum, then the token writes in one
+ * kernel).  Every output is identical to moe_layout, moe_notify and
+ * moe_dispatch called in turn with the same arguments, which is also what
+ * this call does when the one kernel does not apply (moe_fused_supported).
+ * Arguments as in those three calls; workspace and workspaceBytes are
+ * moe_layout's (moe_layout_workspace_bytes) and are used only by the
+ * three-stage form.
+ * The one kernel needs no inter-workgroup synchronisation: each workgroup
+ * counts all ids itself, ranks its own tokens' entries and writes their
+ * rows; workgroup 0 writes the layout and notify outputs. */
+int moe_layout_notify_dispatch(const void* x, moe_dtype xType, int32_t bs, int32_t hidden,
+                               int32_t topk, const int32_t* topkIdx, int32_t expertNumPerRank,
+                               int32_t rankSize, int quantInt8, int32_t* tokenPerExpert,
+                               int32_t* tokenPerRank, int32_t* sendTokenIdx, int32_t* badIdCount,
+                               int32_t* putOffset, int32_t* recvCount, int32_t* recvBase,
+                               int32_t* recvTokenPerExpert, void* recvX, size_t recvXBytes,
+                               void* workspace, size_t workspaceBytes, void* stream);
 
 /* Text for a status code (static storage). */
 const char* moe_status_str(int status);

@@ -106,7 +106,10 @@ class GpuRun:
         self.buf.combine(self.idx, self.wts)
         return self
 
-    def run_all(self):
+    def run_all(self, fused: bool = False):
+        if fused:
+            self.buf.layout_notify_dispatch(self.x, self.idx)
+            return self.combine()
         return self.layout().notify().dispatch().combine()
 
     def host(self) -> Dict[str, object]:

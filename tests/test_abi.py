@@ -136,6 +136,57 @@ def test_combine_rejects_on_host(M):
     assert L.moe_combine(*args(bs=0, recv=None, out=None, w=None, cap=0)) == 0
 
 
+def test_fused_supported_is_host_logic(M):
+    # one kernel unless bs == 0, hidden > 8192 or bs * topk > 2^19; any expert count up to the maximum
+    import torch
+
+    bf16 = torch.bfloat16
+    assert M.moe_fused_supported(4096, 7168, 8, 16, 16, bf16, True)
+    assert M.moe_fused_supported(16384, 7168, 8, 4, 64, bf16, True)
+    assert M.moe_fused_supported(64, 128, 4, 1024, 2, bf16, True)
+    assert M.moe_fused_supported(1, 8192, 1, 1, 1, torch.float16, False)
+    assert not M.moe_fused_supported(0, 128, 4, 8, 2, bf16, True)
+    assert not M.moe_fused_supported(16, 8200, 4, 8, 2, bf16, True)
+    assert M.moe_fused_supported(65536, 16, 8, 8, 2, bf16, True)        # 2^19 entries
+    assert not M.moe_fused_supported(65537, 16, 8, 8, 2, bf16, True)
+
+
+def test_fused_rejects_on_host(M):
+    # every call below has an invalid argument, so it returns before any HIP call
+    L = M._lib
+    rb = M.moe_recv_row_bytes(7168, 3)
+    cap = 4096 * 8 * rb
+    big = 70000  # bs * 8 above 2^19: the three-stage form, which needs moe_layout's workspace
+    ws_big = M.moe_layout_workspace_bytes(big, 8, 256)
+    cap_big = big * 8 * rb
+
+    def call(**kw):
+        a = dict(x=P, xt=0, bs=4096, h=7168, k=8, idx=P, epr=16, r=16, q=1, tpe=P, tpr=P, slot=P, bad=None,
+                 put=P, cnt=P, base=P, rtpe=P, recv=P, cap=cap, ws=P, wsb=0)
+        a.update(kw)
+        return L.moe_layout_notify_dispatch(a["x"], a["xt"], a["bs"], a["h"], a["k"], a["idx"], a["epr"], a["r"],
+                                            a["q"], a["tpe"], a["tpr"], a["slot"], a["bad"], a["put"], a["cnt"],
+                                            a["base"], a["rtpe"], a["recv"], a["cap"], a["ws"], a["wsb"], None)
+    assert ws_big > 0
+    assert call(xt=2) == 4
+    assert call(q=3) == 4
+    assert call(h=7160 + 4) == 7
+    assert call(k=0) == 2
+    assert call(epr=4096, r=1) == 7
+    assert call(bs=big, cap=cap_big, ws=None, wsb=ws_big) == 1
+    assert call(bs=big, cap=cap_big, wsb=ws_big - 4) == 5
+    assert call(cap=cap - 1) == 6
+    assert call(x=None) == 1
+    assert call(tpe=None) == 1
+    assert call(recv=P + 8) == 3
+    assert call(ws=P + 2) == 3
+    assert call(put=P + 2) == 3
+    out = ctypes.c_int(5)
+    assert L.moe_fused_supported(16, 8, 2, 4, 2, 2, 1, ctypes.byref(out)) == 4   # fp32 input
+    assert L.moe_fused_supported(16, 12, 2, 4, 2, 0, 1, ctypes.byref(out)) == 7  # hidden % 8
+    assert L.moe_fused_supported(16, 8, 2, 4, 2, 0, 2, ctypes.byref(out)) == 4   # quant flag
+
+
 def test_binding_rejects_host_tensors(M):
     import torch
 
