@@ -167,7 +167,7 @@ def main(argv=None) -> int:
     ap.add_argument("--flush-mib", type=int, default=1024)
     ap.add_argument("--event-flags", default="nofence", choices=["nofence", "default"],
                     help="HIP event creation flags for the stage timers")
-    ap.add_argument("--path", default="separate", choices=["separate", "fused"],
+    ap.add_argument("--path", default="fused", choices=["separate", "fused"],
                     help="layout, notify and dispatch as three launches, or one fused launch")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, then WRITE_SIZE) of a bench "
@@ -374,18 +374,20 @@ def _read_counter_csv(path: str):
 
 
 def ingest_pmc(args, fetch_csv: str, write_csv: str) -> int:
-    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dispatch and
-    combine kernels by what the same counters read for the bench's plain copy
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dispatch,
+    combine and fused kernels (those the run launched) by what the same counters read for the bench's plain copy
     kernel (torch.neg over the 1 GiB flush buffer: 1 GiB read, 1 GiB written),
     and store bytes per launch with the kernel source hash."""
     fetch = _read_counter_csv(fetch_csv)
     write = _read_counter_csv(write_csv)
     copy_bytes = args.flush_mib * (1 << 20)
 
-    def pick(table, key):
+    def pick(table, key, required=True):
         cands = [(n, v) for n, v in table.items() if key in n]
         if not cands:
-            raise SystemExit(f"no kernel matching {key!r} in counters")
+            if required:
+                raise SystemExit(f"no kernel matching {key!r} in counters")
+            return None, None
         n, v = max(cands, key=lambda nv: len(nv[1]))
         return n, statistics.median(v)
 
@@ -398,10 +400,12 @@ def ingest_pmc(args, fetch_csv: str, write_csv: str) -> int:
     import workloads as W
 
     c = W.CONFIGS[args.workload]
-    b_dis, b_com, _ = algorithmic_bytes(c["bs"], c["hidden"], c["topk"], quant)
-    for kernel, alg in (("dispatch", b_dis), ("combine", b_com)):
-        kname, f = pick(fetch, f"{kernel}_kernel")
-        _, wr = pick(write, f"{kernel}_kernel")
+    b_dis, b_com, b_lay = algorithmic_bytes(c["bs"], c["hidden"], c["topk"], quant)
+    for kernel, alg in (("dispatch", b_dis), ("combine", b_com), ("fused", b_dis + b_lay)):
+        kname, f = pick(fetch, f"{kernel}_kernel", required=False)
+        _, wr = pick(write, f"{kernel}_kernel", required=False)
+        if f is None or wr is None:
+            continue  # not launched in this run
         traffic = f * 1024.0 * f_scale + wr * 1024.0 * w_scale
         rec = {
             "kernel": kname, "workload": args.workload, "mode": args.mode,

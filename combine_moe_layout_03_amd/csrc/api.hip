@@ -198,12 +198,16 @@ bool fused_applies(int32_t bs, int32_t hidden, int32_t topk) {
          static_cast<int64_t>(bs) * topk <= moe::kFusedMaxEntries;
 }
 
-// Tokens per workgroup and workgroups of the one kernel: one workgroup per
-// CU (fewer for small batches), more when the per-token LDS of a group would
-// exceed kFusedMaxLds.
-int fused_grid(int32_t bs, int32_t topk, int32_t num_experts, int cus, int32_t* tokens_per_group) {
-  const size_t fixed = moe::fused_lds_bytes(num_experts, 0, topk);
-  const size_t per_token = moe::fused_lds_bytes(num_experts, 1, topk) - fixed;
+// Tokens per workgroup, LDS histogram copies and workgroups of the one
+// kernel: one workgroup per CU (fewer for small batches); as many histogram
+// copies (up to 8) as leave room in kFusedMaxLds for 8 KiB of per-token
+// state; more workgroups when the per-token state of one would not fit.
+int fused_grid(int32_t bs, int32_t topk, int32_t num_experts, int cus, int32_t* tokens_per_group,
+               int32_t* copies_log2) {
+  int lg = moe::kFusedMaxCopiesLog2;
+  while (lg > 0 && moe::fused_lds_bytes(num_experts, 0, topk, 1 << lg) + 8192 > moe::kFusedMaxLds) --lg;
+  const size_t fixed = moe::fused_lds_bytes(num_experts, 0, topk, 1 << lg);
+  const size_t per_token = moe::fused_lds_bytes(num_experts, 1, topk, 1 << lg) - fixed;
   const int64_t t_max = static_cast<int64_t>((moe::kFusedMaxLds - fixed) / per_token);
   int64_t groups = bs < cus ? bs : cus;
   if (groups < 1) groups = 1;
@@ -211,6 +215,7 @@ int fused_grid(int32_t bs, int32_t topk, int32_t num_experts, int cus, int32_t* 
   if (tpg > t_max) tpg = t_max;
   groups = (bs + tpg - 1) / tpg;
   *tokens_per_group = static_cast<int32_t>(tpg);
+  *copies_log2 = lg;
   return static_cast<int>(groups);
 }
 
@@ -289,7 +294,7 @@ int moe_layout_notify_dispatch(const void* x, moe_dtype x_type, int32_t bs, int3
   int id_bits = 0;
   while ((1 << id_bits) < a.num_experts) ++id_bits;
   a.id_bits = id_bits;
-  const int groups = fused_grid(bs, topk, a.num_experts, cus, &a.tokens_per_group);
+  const int groups = fused_grid(bs, topk, a.num_experts, cus, &a.tokens_per_group, &a.copies_log2);
   a.ids_aligned16 = aligned(topk_idx, 16) ? 1 : 0;
   a.token_per_expert = token_per_expert;
   a.token_per_rank = token_per_rank;

@@ -74,8 +74,9 @@ hipError_t launch_combine(const RouteArgs& r, const void* recv_x, Recv recv_type
 // ---- fused layout + notify + dispatch ------------------------------------------
 constexpr int kFusedWaves = 16;                 // waves per workgroup
 constexpr int kFusedMaxHidden = 16 * 64 * 8;    // row held in registers: 16 chunks per lane
-constexpr int64_t kFusedMaxEntries = 1 << 19;   // bs * k: every workgroup counts all ids
+constexpr int64_t kFusedMaxEntries = 1 << 16;   // bs * k: every workgroup counts all ids
 constexpr size_t kFusedMaxLds = 64 * 1024;
+constexpr int kFusedMaxCopiesLog2 = 3;          // up to 8 copies of each LDS histogram
 static_assert(MOE_MAX_EXPERTS <= 2 * kFusedWaves * 64, "the fused scan gives each thread two experts");
 
 struct FusedArgs {
@@ -84,6 +85,7 @@ struct FusedArgs {
   int32_t bs, hidden, k, epr, ranks, num_experts, id_bits;
   int32_t tokens_per_group;  // T: workgroup g owns tokens [g*T, (g+1)*T)
   int32_t ids_aligned16;     // topk_idx is 16-byte aligned
+  int32_t copies_log2;       // log2 of the LDS histogram copies
   int32_t* token_per_expert;
   int32_t* token_per_rank;
   int32_t* send_token_idx;
@@ -97,7 +99,7 @@ struct FusedArgs {
   int32_t scale_off;
 };
 
-size_t fused_lds_bytes(int32_t num_experts, int32_t tokens_per_group, int32_t topk);
+size_t fused_lds_bytes(int32_t num_experts, int32_t tokens_per_group, int32_t topk, int32_t copies);
 hipError_t launch_fused(const FusedArgs& a, Half x_type, bool quant, int groups, hipStream_t stream);
 
 }  // namespace moe

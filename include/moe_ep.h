@@ -167,7 +167,7 @@ int moe_combine(const void* recvX, moe_dtype recvType, size_t recvXBytes, int32_
 
 /* *supported = 1 if moe_layout_notify_dispatch runs as one kernel for this
  * shape, 0 if it runs the three stages one after another (bs == 0, hidden
- * above 8192, or bs * topk above 2^19: every workgroup of the one kernel
+ * above 8192, or bs * topk above 2^16: every workgroup of the one kernel
  * reads all bs * topk ids).  Host only; the answer does not depend on the
  * device. */
 int moe_fused_supported(int32_t bs, int32_t hidden, int32_t topk, int32_t expertNumPerRank,

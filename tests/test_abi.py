@@ -137,18 +137,18 @@ def test_combine_rejects_on_host(M):
 
 
 def test_fused_supported_is_host_logic(M):
-    # one kernel unless bs == 0, hidden > 8192 or bs * topk > 2^19; any expert count up to the maximum
+    # one kernel unless bs == 0, hidden > 8192 or bs * topk > 2^16; any expert count up to the maximum
     import torch
 
     bf16 = torch.bfloat16
     assert M.moe_fused_supported(4096, 7168, 8, 16, 16, bf16, True)
-    assert M.moe_fused_supported(16384, 7168, 8, 4, 64, bf16, True)
+    assert not M.moe_fused_supported(16384, 7168, 8, 4, 64, bf16, True)
     assert M.moe_fused_supported(64, 128, 4, 1024, 2, bf16, True)
     assert M.moe_fused_supported(1, 8192, 1, 1, 1, torch.float16, False)
     assert not M.moe_fused_supported(0, 128, 4, 8, 2, bf16, True)
     assert not M.moe_fused_supported(16, 8200, 4, 8, 2, bf16, True)
-    assert M.moe_fused_supported(65536, 16, 8, 8, 2, bf16, True)        # 2^19 entries
-    assert not M.moe_fused_supported(65537, 16, 8, 8, 2, bf16, True)
+    assert M.moe_fused_supported(8192, 16, 8, 8, 2, bf16, True)         # 2^16 entries
+    assert not M.moe_fused_supported(8193, 16, 8, 8, 2, bf16, True)
 
 
 def test_fused_rejects_on_host(M):
@@ -156,7 +156,7 @@ def test_fused_rejects_on_host(M):
     L = M._lib
     rb = M.moe_recv_row_bytes(7168, 3)
     cap = 4096 * 8 * rb
-    big = 70000  # bs * 8 above 2^19: the three-stage form, which needs moe_layout's workspace
+    big = 70000  # bs * 8 above 2^16: the three-stage form, which needs moe_layout's workspace
     ws_big = M.moe_layout_workspace_bytes(big, 8, 256)
     cap_big = big * 8 * rb
 

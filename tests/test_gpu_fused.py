@@ -45,6 +45,9 @@ FUSED_RANDOM = [
     (312, 100, 32, 8, 1024, 8, "dup", 0.0, "fp16", False),
     (313, 255, 40, 5, 3, 3, "hot", 0.3, "bf16", True),
     (314, 257, 7168, 8, 256, 16, "zipf1.2", 0.0, "bf16", True),
+    (315, 4096, 512, 8, 256, 16, "hot", 0.0, "bf16", True),
+    (316, 8192, 64, 8, 256, 16, "hot", 0.01, "bf16", True),
+    (317, 2000, 24, 8, 2048, 64, "hot", 0.0, "fp16", True),
 ]
 
 
@@ -80,8 +83,8 @@ def test_fused_repeated_calls():
         np.testing.assert_array_equal(raw[:total, :h].view(np.int8), ref["dispatch"]["codes"][:total])
 
 
-@pytest.mark.parametrize("seed,bs,h,k,e,r", [(330, 200, 8704, 4, 64, 8), (331, 65600, 8, 8, 32, 4)],
-                         ids=["hidden_above_8192", "entries_above_2^19"])
+@pytest.mark.parametrize("seed,bs,h,k,e,r", [(330, 200, 8704, 4, 64, 8), (331, 8193, 16, 8, 32, 4)],
+                         ids=["hidden_above_8192", "entries_above_2^16"])
 def test_fused_fallback_shape_matches(seed, bs, h, k, e, r):
     """Shapes the one kernel does not take run the three stages through the
     same entry point."""
