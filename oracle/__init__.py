@@ -41,6 +41,7 @@ _SIGS = {
     "oracle_f32_to_f16": [_P, _P, _I64],
     "oracle_layout": [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P],
     "oracle_notify": [_P, _I64, _I64, _P, _P, _P, _P],
+    "oracle_notify_multi": [_P, _I64, _I64, _I64, _P, _P, _P, _P],
     "oracle_quant_row": [_P, _INT, _I64, _P, _P, _P],
     "oracle_dispatch": [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _I64, _I64, _INT, _I64,
                         _P, _P, _P],
@@ -137,6 +138,25 @@ class Oracle:
                                     _ptr(cnt), _ptr(base), _ptr(rtpe)), "notify")
         return dict(put_offset=put, recv_count=cnt, recv_base=base, recv_token_per_expert=rtpe)
 
+    def notify_multi(self, token_per_expert: np.ndarray, expert_num_per_rank: int,
+                     rank_size: int) -> Dict[str, np.ndarray]:
+        """Stage 2 over the count matrix of several sources: token_per_expert
+        [S, E] -> putOffset [E, S], recvCount [R], recvBase [R],
+        recvTokenPerExpert [E]."""
+        tpe = np.ascontiguousarray(token_per_expert, dtype=np.int32)
+        e = expert_num_per_rank * rank_size
+        if tpe.ndim != 2 or tpe.shape[1] != e:
+            raise ValueError("token_per_expert must be [S, E]")
+        num_src = tpe.shape[0]
+        put = np.zeros((e, num_src), np.int32)
+        cnt = np.zeros(rank_size, np.int32)
+        base = np.zeros(rank_size, np.int32)
+        rtpe = np.zeros(e, np.int32)
+        _check(self.L.oracle_notify_multi(_ptr(tpe), num_src, expert_num_per_rank, rank_size,
+                                          _ptr(put), _ptr(cnt), _ptr(base), _ptr(rtpe)),
+               "notify_multi")
+        return dict(put_offset=put, recv_count=cnt, recv_base=base, recv_token_per_expert=rtpe)
+
     def quant_row(self, x_bits: np.ndarray, x_kind: str = "bf16"):
         """QuantProcess on one row: (codes int8 [h], inv float32, scale float32)."""
         x = np.ascontiguousarray(x_bits, dtype=np.uint16).reshape(-1)
@@ -149,8 +169,11 @@ class Oracle:
 
     def dispatch(self, x_bits: np.ndarray, x_kind: str, topk_idx: np.ndarray,
                  send_token_idx: np.ndarray, put_offset: np.ndarray, recv_base: np.ndarray,
-                 expert_num_per_rank: int, rank_size: int, quant: bool) -> Dict[str, np.ndarray]:
-        """Stage 3: scatter rows (optionally quantised) into a [bs*k]-row buffer."""
+                 expert_num_per_rank: int, rank_size: int, quant: bool,
+                 into: Optional[Dict[str, np.ndarray]] = None) -> Dict[str, np.ndarray]:
+        """Stage 3: scatter rows (optionally quantised) into a [bs*k]-row
+        buffer, or into the rows of ``into`` (a buffer shared by several
+        sources, as returned by an earlier call)."""
         x = np.ascontiguousarray(x_bits, dtype=np.uint16)
         bs, h = x.shape
         idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
@@ -158,13 +181,25 @@ class Oracle:
         slot = np.ascontiguousarray(send_token_idx, dtype=np.int32)
         put = np.ascontiguousarray(put_offset, dtype=np.int32)
         base = np.ascontiguousarray(recv_base, dtype=np.int32)
-        rows = bs * k
         recv = codes = inv = None
-        if quant:
-            codes = np.zeros((rows, h), np.int8)
-            inv = np.zeros(rows, np.float32)
+        if into is not None:
+            if quant:
+                codes, inv = into["codes"], into["inv"]
+                rows = codes.shape[0]
+                if codes.dtype != np.int8 or inv.dtype != np.float32 or not codes.flags.c_contiguous:
+                    raise ValueError("into: int8 codes [rows, h] and float32 inv [rows]")
+            else:
+                recv = into["rows"]
+                rows = recv.shape[0]
+                if recv.dtype != np.uint16 or not recv.flags.c_contiguous:
+                    raise ValueError("into: uint16 rows [rows, h]")
         else:
-            recv = np.zeros((rows, h), np.uint16)
+            rows = bs * k
+            if quant:
+                codes = np.zeros((rows, h), np.int8)
+                inv = np.zeros(rows, np.float32)
+            else:
+                recv = np.zeros((rows, h), np.uint16)
         _check(self.L.oracle_dispatch(_ptr(x), _KIND[x_kind], bs, h, k, _ptr(idx), _ptr(slot),
                                       _ptr(put), _ptr(base), expert_num_per_rank, rank_size,
                                       1 if quant else 0, rows, _ptr(recv), _ptr(codes),
@@ -215,6 +250,32 @@ class Oracle:
                            expert_num_per_rank, rank_size, out_kind)
         return dict(layout=lay, notify=no, dispatch=dis, out=out)
 
+    def pipeline_multi(self, xs, x_kind: str, idxs, ws, expert_num_per_rank: int,
+                       rank_size: int, quant: bool, out_kind: Optional[str] = None
+                       ) -> Dict[str, object]:
+        """All four stages with several source ranks sharing one receive
+        buffer: a layout per source, notify over the [S, E] count matrix,
+        each source's dispatch with its column of putOffset, then each
+        source's combine.  Returns every intermediate; ``outs`` per source."""
+        lays = [self.layout(idx, expert_num_per_rank, rank_size) for idx in idxs]
+        counts = np.stack([l["token_per_expert"] for l in lays]) if lays else None
+        no = self.notify_multi(counts, expert_num_per_rank, rank_size)
+        h = xs[0].shape[1]
+        rows = sum(int(np.asarray(i).shape[0]) * int(np.asarray(i).shape[1]) for i in idxs)
+        if quant:
+            buf = dict(codes=np.zeros((rows, h), np.int8), inv=np.zeros(rows, np.float32))
+        else:
+            buf = dict(rows=np.zeros((rows, h), np.uint16))
+        for src, (x, idx, lay) in enumerate(zip(xs, idxs, lays)):
+            self.dispatch(x, x_kind, idx, lay["send_token_idx"], no["put_offset"][:, src],
+                          no["recv_base"], expert_num_per_rank, rank_size, quant, into=buf)
+        out_kind = out_kind or x_kind
+        outs = [self.combine(buf, "int8" if quant else x_kind, idx, w, lay["send_token_idx"],
+                             no["put_offset"][:, src], no["recv_base"], expert_num_per_rank,
+                             rank_size, out_kind)
+                for src, (idx, w, lay) in enumerate(zip(idxs, ws, lays))]
+        return dict(layouts=lays, counts=counts, notify=no, dispatch=buf, outs=outs)
+
 
 _default: Optional[Oracle] = None
 
@@ -251,6 +312,14 @@ def layout(*a, **kw):
 
 def notify(*a, **kw):
     return default().notify(*a, **kw)
+
+
+def notify_multi(*a, **kw):
+    return default().notify_multi(*a, **kw)
+
+
+def pipeline_multi(*a, **kw):
+    return default().pipeline_multi(*a, **kw)
 
 
 def quant_row(*a, **kw):

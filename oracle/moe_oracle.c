@@ -13,7 +13,8 @@
  *   2.1  the four stages and their order,
  *   2.2.1 comm_args.h (UB_ALIGN_SIZE = 32 bytes; the CommArgs scalars),
  *   2.3  moe_dispatch_layout_zb (per-expert counts, per-(token,k) send index),
- *   2.4  moe_notify_dispatch_zb (prefix sums: putOffset, receive counts),
+ *   2.4  moe_notify_dispatch_zb (prefix sums: putOffset, receive counts; with
+ *        several source ranks, over the all-gathered count matrix),
  *   2.5  moe_dispatch_normal_zb / QuantProcess (row scatter, dynamic int8),
  *   2.6  moe_combine_normal_zb / ReadBufferAndWeightedSum (weighted gather),
  *   2.8  the per-rank zero-buffer layout (token region read by combine).
@@ -31,7 +32,8 @@
  *    reads one row per entry;
  *  - on one device the logical ranks' receive regions are concatenated in
  *    rank order with no gaps, and inside a rank the experts' rows are
- *    contiguous in expert order;
+ *    contiguous in expert order; with several sources, an expert's rows are
+ *    ordered by source rank, then by send slot;
  *  - the quantiser stores the inverse scale 1/s; combine dequantises with
  *    (float)q * inv before the weight multiply;
  *  - combine sums j = 0..k-1 from +0.0f, multiply then add, each rounded;
@@ -225,6 +227,45 @@ int oracle_notify(const int32_t *token_per_expert, int64_t epr, int64_t ranks,
       put_offset[e] = acc;
       acc += token_per_expert[e];
       recv_token_per_expert[e] = token_per_expert[e];
+    }
+    recv_count[r] = acc;
+    recv_base[r] = base;
+    base += acc;
+  }
+  return ORACLE_OK;
+}
+
+/* Stage 2 with several source ranks (page section 2.4: every rank's
+ * tokenPerExpert is all-gathered, then prefix sums give the write offsets;
+ * section 2.6 reads the offset of (expert e, source s) at index
+ * e * epWorldSize + s).  Input: token_per_expert[s][e] for num_src sources.
+ * Inside destination rank r the rows are ordered by expert, then by source:
+ *   for r: acc = 0
+ *     for e of r ascending, for s = 0 .. num_src-1:
+ *       put_offset[e][s] = acc; acc += count[s][e]
+ *     recv_count[r] = acc
+ * recv_base[r] concatenates the ranks' regions in rank order, and
+ * recv_token_per_expert[e] = sum over s of count[s][e].  With one source this
+ * is oracle_notify. */
+int oracle_notify_multi(const int32_t *token_per_expert, int64_t num_src, int64_t epr,
+                        int64_t ranks, int32_t *put_offset, int32_t *recv_count,
+                        int32_t *recv_base, int32_t *recv_token_per_expert) {
+  if (num_src < 1 || epr < 1 || ranks < 1) return ORACLE_BAD_ARG;
+  if (!token_per_expert || !put_offset || !recv_count || !recv_base || !recv_token_per_expert)
+    return ORACLE_BAD_ARG;
+  int64_t num_experts = epr * ranks;
+  int32_t base = 0;
+  for (int64_t r = 0; r < ranks; ++r) {
+    int32_t acc = 0;
+    for (int64_t e = r * epr; e < (r + 1) * epr; ++e) {
+      int32_t sum = 0;
+      for (int64_t src = 0; src < num_src; ++src) {
+        int32_t c = token_per_expert[src * num_experts + e];
+        put_offset[e * num_src + src] = acc;
+        acc += c;
+        sum += c;
+      }
+      recv_token_per_expert[e] = sum;
     }
     recv_count[r] = acc;
     recv_base[r] = base;

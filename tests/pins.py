@@ -264,6 +264,95 @@ def check_notify(orc, tpe: np.ndarray, epr: int, ranks: int) -> None:
     assert int(got["recv_base"][-1]) + int(got["recv_count"][-1]) == total
 
 
+def check_notify_multi_golden(orc) -> None:
+    """Hand-worked count matrices of several sources (golden/notify_multi.json)."""
+    g = load_golden("notify_multi.json")
+    for c in g["cases"]:
+        got = orc.notify_multi(np.array(c["counts"], np.int32), c["epr"], c["ranks"])
+        for key in ("put_offset", "recv_count", "recv_base", "recv_token_per_expert"):
+            assert np.array_equal(got[key], np.array(c[key], np.int32)), (c["name"], key)
+
+
+def check_notify_multi_single_source(orc, tpe: np.ndarray, epr: int, ranks: int) -> None:
+    """With one source the multi-source notify is the single-source one
+    (itself pinned against numpy cumsum)."""
+    one = orc.notify(tpe, epr, ranks)
+    multi = orc.notify_multi(np.asarray(tpe, np.int32).reshape(1, -1), epr, ranks)
+    assert np.array_equal(multi["put_offset"][:, 0], one["put_offset"])
+    for key in ("recv_count", "recv_base", "recv_token_per_expert"):
+        assert np.array_equal(multi[key], one[key]), key
+
+
+def multi_rows(idxs, layouts, no, epr: int):
+    """Receive row of every valid entry of every source, from the oracle's
+    outputs: recvBase[e / EPR] + putOffset[e][s] + slot_s[t, j]."""
+    out = []
+    for src, (idx, lay) in enumerate(zip(idxs, layouts)):
+        idx = np.asarray(idx, np.int64)
+        e_num = no["put_offset"].shape[0]
+        valid = (idx >= 0) & (idx < e_num)
+        ec = np.where(valid, idx, 0)
+        rows = no["recv_base"][ec // epr].astype(np.int64) + no["put_offset"][ec, src] + \
+            lay["send_token_idx"].astype(np.int64)
+        out.append(np.where(valid, rows, -1))
+    return out
+
+
+def check_multi_receive_order(orc, idxs, epr: int, ranks: int) -> None:
+    """Library-routine pin of the multi-source layout: sorting every valid
+    (source, token, k) entry by the key (expert, source, token, k) with
+    numpy's lexsort gives each entry's receive row (its position), and the
+    rows tile [0, total) exactly once."""
+    lays = [orc.layout(idx, epr, ranks) for idx in idxs]
+    no = orc.notify_multi(np.stack([l["token_per_expert"] for l in lays]), epr, ranks)
+    rows = multi_rows(idxs, lays, no, epr)
+    e_num = epr * ranks
+    keys_e, keys_s, keys_f, got = [], [], [], []
+    for src, (idx, r) in enumerate(zip(idxs, rows)):
+        flat = np.asarray(idx, np.int64).reshape(-1)
+        valid = (flat >= 0) & (flat < e_num)
+        keys_e.append(flat[valid])
+        keys_s.append(np.full(int(valid.sum()), src, np.int64))
+        keys_f.append(np.nonzero(valid)[0])
+        got.append(r.reshape(-1)[valid])
+    ke, ks, kf, got = (np.concatenate(a) for a in (keys_e, keys_s, keys_f, got))
+    order = np.lexsort((kf, ks, ke))  # last key is the primary one
+    expect = np.empty_like(order)
+    expect[order] = np.arange(order.size)
+    assert np.array_equal(got, expect), "multi-source receive rows = lexsort position"
+    total = int(order.size)
+    assert int(no["recv_base"][-1]) + int(no["recv_count"][-1]) == total
+    counts = np.stack([l["token_per_expert"] for l in lays]).astype(np.int64)
+    assert np.array_equal(no["recv_token_per_expert"], counts.sum(0)), "recvTokenPerExpert"
+    assert np.array_equal(no["recv_count"], counts.sum(0).reshape(ranks, epr).sum(1)), "recvCount"
+
+
+def check_pipeline_multi_vs_single(orc, xs, x_kind: str, idxs, ws, epr: int, ranks: int,
+                                   quant: bool) -> None:
+    """Closed form of the whole multi-source pipeline: each source's combine
+    output equals that source's single-source pipeline (the rows it reads are
+    the rows it wrote, wherever they sit), bit for bit; and every valid
+    entry's receive row holds that source's token (passthrough) or its
+    quantised copy (int8)."""
+    m = orc.pipeline_multi(xs, x_kind, idxs, ws, epr, ranks, quant)
+    rows = multi_rows(idxs, m["layouts"], m["notify"], epr)
+    for src, (x, idx, w) in enumerate(zip(xs, idxs, ws)):
+        single = orc.pipeline(x, x_kind, idx, w, epr, ranks, quant)
+        assert np.array_equal(m["outs"][src], single["out"]), f"source {src} output"
+        r = rows[src]
+        t_of = np.broadcast_to(np.arange(idx.shape[0])[:, None], idx.shape)
+        sel = r >= 0
+        if quant:
+            srow = single["dispatch"]["codes"]
+            srows = multi_rows([idx], [single["layout"]],
+                               dict(put_offset=single["notify"]["put_offset"][:, None],
+                                    recv_base=single["notify"]["recv_base"]), epr)[0]
+            assert np.array_equal(m["dispatch"]["codes"][r[sel]], srow[srows[sel]]), f"source {src} codes"
+            assert np.array_equal(m["dispatch"]["inv"][r[sel]], single["dispatch"]["inv"][srows[sel]])
+        else:
+            assert np.array_equal(m["dispatch"]["rows"][r[sel]], np.asarray(x)[t_of[sel]]), f"source {src} rows"
+
+
 # --------------------------------------------------------------------------
 # dispatch (stage 3)
 # --------------------------------------------------------------------------

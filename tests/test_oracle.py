@@ -152,3 +152,41 @@ def test_passthrough_round_trip_unit_weights(orc):
     wsum = w.topk_w.astype(np.float64).sum(axis=1, keepdims=True)
     err = np.abs(res["out"] - x * wsum)
     assert np.all(err <= 2 * w.topk * 2.0 ** -24 * np.abs(x) * wsum + 1e-38)
+
+
+# --------------------------------------------------------------------------
+# several source ranks sharing one receive buffer
+# --------------------------------------------------------------------------
+
+def _sources(seed, sizes, h, k, e, r, routing="dup", bad=0.0, kind="bf16"):
+    cases = [W.random_case(seed + i, bs, h, k, e, r, x_dtype=kind, routing=routing, bad_frac=bad)
+             for i, bs in enumerate(sizes)]
+    return ([c.x for c in cases], [c.topk_idx for c in cases], [c.topk_w for c in cases])
+
+
+def test_notify_multi_golden(orc):
+    pins.check_notify_multi_golden(orc)
+
+
+@pytest.mark.parametrize("epr,ranks,seed", [(1, 1, 11), (4, 2, 12), (16, 16, 13), (7, 3, 14)])
+def test_notify_multi_single_source(orc, epr, ranks, seed):
+    tpe = (W.u64(seed, 0, epr * ranks) % np.uint64(50)).astype(np.int32)
+    pins.check_notify_multi_single_source(orc, tpe, epr, ranks)
+
+
+@pytest.mark.parametrize("seed,sizes,k,e,r,routing,bad", [
+    (401, (5, 3), 2, 4, 2, "dup", 0.0),
+    (402, (40, 0, 17, 33), 4, 12, 3, "dup", 0.1),
+    (403, (64,) * 8, 8, 64, 8, "uniform", 0.0),
+    (404, (100, 1, 250), 8, 256, 16, "zipf1.2", 0.02),
+    (405, (30, 30), 3, 2, 1, "hot", 0.0),
+])
+def test_multi_receive_order_lexsort(orc, seed, sizes, k, e, r, routing, bad):
+    _, idxs, _ = _sources(seed, sizes, 8, k, e, r, routing, bad)
+    pins.check_multi_receive_order(orc, idxs, e // r, r)
+
+
+@pytest.mark.parametrize("quant,kind", [(False, "bf16"), (True, "bf16"), (True, "fp16")])
+def test_pipeline_multi_equals_each_single_source(orc, quant, kind):
+    xs, idxs, ws = _sources(410, (24, 0, 9, 31), 40, 4, 16, 4, "dup", 0.05, kind)
+    pins.check_pipeline_multi_vs_single(orc, xs, kind, idxs, ws, 4, 4, quant)

@@ -32,6 +32,21 @@ MUTANTS = {
         "      put_offset[e] = acc;\n      acc += token_per_expert[e];",
         "      acc += token_per_expert[e];\n      put_offset[e] = acc;",
         "notify"),
+    # multi-source notify: sources in descending order inside an expert
+    "multi_source_descending": (
+        "for (int64_t src = 0; src < num_src; ++src) {",
+        "for (int64_t src = num_src - 1; src >= 0; --src) {",
+        "notify_multi"),
+    # multi-source notify: count matrix read transposed
+    "multi_count_transposed": (
+        "token_per_expert[src * num_experts + e]",
+        "token_per_expert[e * num_src + src]",
+        "notify_multi"),
+    # multi-source notify: offsets stored source-major
+    "multi_put_source_major": (
+        "put_offset[e * num_src + src] = acc;",
+        "put_offset[src * num_experts + e] = acc;",
+        "notify_multi"),
     # dispatch: destination rank taken modulo instead of divided
     "dest_rank_modulo": (
         "return (int64_t)recv_base[e / epr] + put_offset[e] + slot;",
@@ -116,6 +131,11 @@ def _run_pin(orc, which):
         w = W.make_workload("small")
         lay = orc.layout(w.topk_idx, w.expert_num_per_rank, w.rank_size)
         pins.check_notify(orc, lay["token_per_expert"], w.expert_num_per_rank, w.rank_size)
+    elif which == "notify_multi":
+        pins.check_notify_multi_golden(orc)
+        idxs = [W.random_case(450 + i, bs, 8, 4, 12, 3, routing="dup").topk_idx
+                for i, bs in enumerate((20, 7, 13))]
+        pins.check_multi_receive_order(orc, idxs, 4, 3)
     elif which == "dispatch":
         w = W.make_workload("small")
         pins.check_dispatch_passthrough(orc, w.x, "bf16", w.topk_idx, w.expert_num_per_rank,
