@@ -169,6 +169,9 @@ def main(argv=None) -> int:
                     help="HIP event creation flags for the stage timers")
     ap.add_argument("--path", default="fused", choices=["separate", "fused"],
                     help="layout, notify and dispatch as three launches, or one fused launch")
+    ap.add_argument("--sources", type=int, default=1,
+                    help="split the workload's tokens into this many source ranks sharing one receive "
+                         "buffer (multi-source notify, per-source dispatch and combine)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, then WRITE_SIZE) of a bench "
                          "run into profiles/traffic_*.json and exit")
@@ -207,6 +210,10 @@ def main(argv=None) -> int:
 
     def do_flush():
         torch.sum(flush, dim=0, out=flush_out)
+
+    if args.sources > 1:
+        del buf
+        return bench_sources(args, M, torch, w, x, idx, wts, quant, do_flush, stream)
 
     fused = args.path == "fused"
     if fused and not M.moe_fused_supported(w.bs, w.hidden, w.topk, w.expert_num_per_rank, w.rank_size,
@@ -353,6 +360,111 @@ def main(argv=None) -> int:
         "unflushed_tokens_per_s": w.bs / (unflushed_ms * 1e-3),
         "copy_ceiling_gbps": copy_gbps,
         "wall_ms_per_step_incl_flush": wall / args.steps * 1e3,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_sources(args, M, torch, w, x, idx, wts, quant: bool, do_flush, stream) -> int:
+    """The workload's tokens split evenly into ``--sources`` source ranks
+    sharing one receive buffer: a step is every source's layout, one notify
+    over the [S, E] count matrix, every source's dispatch, then every
+    source's combine (all on one stream; the caches are flushed before the
+    step and before the combines)."""
+    n_src = args.sources
+    if w.bs % n_src:
+        print(f"--sources must divide bs = {w.bs}", file=sys.stderr)
+        return 2
+    per = w.bs // n_src
+    xs = [x[s * per:(s + 1) * per] for s in range(n_src)]
+    idxs = [idx[s * per:(s + 1) * per] for s in range(n_src)]
+    wss = [wts[s * per:(s + 1) * per] for s in range(n_src)]
+    buf = M.EpMultiBuffers([per] * n_src, w.hidden, w.topk, w.expert_num_per_rank, w.rank_size,
+                           x_dtype=torch.bfloat16, quant_int8=quant, out_dtype=torch.bfloat16)
+    log(f"{n_src} sources of {per} tokens: warm-up x{args.warmup}")
+    for _ in range(args.warmup):
+        do_flush()
+        buf.run(xs, idxs, wss)
+    torch.cuda.synchronize()
+    log(f"timed x{args.steps}")
+    hev = HipEvents(args.event_flags)
+    ev = [[hev.new() for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        e = ev[i]
+        do_flush()
+        hev.record(e[0], stream)
+        for s in range(n_src):
+            buf.layout(s, idxs[s])
+        buf.notify()
+        hev.record(e[1], stream)
+        for s in range(n_src):
+            buf.dispatch(s, xs[s], idxs[s])
+        hev.record(e[2], stream)
+        do_flush()
+        hev.record(e[3], stream)
+        for s in range(n_src):
+            buf.combine(s, idxs[s], wss[s])
+        hev.record(e[4], stream)
+    torch.cuda.synchronize()
+    lay_ms = [hev.ms(e[0], e[1]) for e in ev]
+    dis_ms = [hev.ms(e[1], e[2]) for e in ev]
+    com_ms = [hev.ms(e[3], e[4]) for e in ev]
+    ms_per_step = statistics.mean([a + b + c for a, b, c in zip(lay_ms, dis_ms, com_ms)])
+    log("un-flushed back-to-back")
+    e0, e1 = hev.new(), hev.new()
+    hev.record(e0, stream)
+    for _ in range(args.steps):
+        buf.run(xs, idxs, wss)
+    hev.record(e1, stream)
+    torch.cuda.synchronize()
+    unflushed_ms = hev.ms(e0, e1) / args.steps
+    hev.close()
+    b_dis, b_com, b_lay = algorithmic_bytes(w.bs, w.hidden, w.topk, quant)
+    dis_mean, com_mean = statistics.mean(dis_ms), statistics.mean(com_ms)
+    dom = "dispatch" if dis_mean >= com_mean else "combine"
+    dom_ms, dom_bytes = (dis_mean, b_dis) if dom == "dispatch" else (com_mean, b_com)
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    dc_gbps = (b_dis + b_com) / ((dis_mean + com_mean) * 1e-3) / 1e9
+    cpu = cpu_baseline(w, quant, args.cpu_budget) if args.cpu_budget > 0 else None
+    line = {
+        "metric": METRIC,
+        "value": w.bs / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "payload": ("bf16 rows in, int8 codes + fp32 inverse scale per row on the wire, bf16 out"
+                    if quant else "bf16 rows in and on the wire, bf16 out"),
+        "data": "synthetic",
+        "config": {"workload": args.workload, "bs": w.bs, "hidden": w.hidden, "topk": w.topk,
+                   "num_experts": w.num_experts, "rank_size": w.rank_size, "x_dtype": "bf16",
+                   "dispatch": "int8" if quant else "passthrough", "out_dtype": "bf16",
+                   "sources": n_src, "tokens_per_source": per,
+                   "parallelism": "1 GPU, source and destination ranks are logical partitions"},
+        "step": (f"{n_src} layouts + notify over the [{n_src}, E] counts, {n_src} dispatches, {n_src} "
+                 "combines; caches flushed before the step and before the combines"),
+        "path": "multi-source (one stream; each source's launches cover 1/S of the tokens)",
+        "timer": f"HIP events on the kernels' stream ({args.event_flags})",
+        "dispatch_combine_tokens_per_s": w.bs / ((dis_mean + com_mean) * 1e-3),
+        "dispatch_combine_hbm_gbps": dc_gbps,
+        "dispatch_combine_hbm_frac": dc_gbps / HBM_PEAK_GBPS,
+        "stages_us": {
+            name: {"mean": statistics.mean(v) * 1e3, "p10": pct(v, 0.1) * 1e3,
+                   "p50": pct(v, 0.5) * 1e3, "p90": pct(v, 0.9) * 1e3}
+            for name, v in (("layouts+notify", lay_ms), ("dispatches", dis_ms), ("combines", com_ms))
+        },
+        "algorithmic_bytes": {"dispatch": b_dis, "combine": b_com, "layout": b_lay},
+        "roofline": {"bound": "hbm", "kernel": dom + " (all sources' launches)", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None},
+        "unflushed_ms_per_step": unflushed_ms,
+        "unflushed_tokens_per_s": w.bs / (unflushed_ms * 1e-3),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -26,11 +26,12 @@ __all__ = [
     "MOE_BF16", "MOE_FP16", "MOE_FP32", "MOE_INT8_ROWSCALE", "MoeEpError", "LIB_PATH",
     "moe_recv_row_bytes", "moe_layout_workspace_bytes", "moe_layout", "moe_notify",
     "moe_dispatch", "moe_combine", "moe_status_str", "moe_last_hip_error", "EpBuffers",
-    "dtype_code", "moe_fused_supported", "moe_layout_notify_dispatch",
+    "dtype_code", "moe_fused_supported", "moe_layout_notify_dispatch", "moe_notify_multi",
+    "moe_dispatch_src", "moe_combine_src", "EpMultiBuffers", "MOE_MAX_SOURCES",
 ]
 
 MOE_BF16, MOE_FP16, MOE_FP32, MOE_INT8_ROWSCALE = 0, 1, 2, 3
-MOE_MAX_EXPERTS, MOE_MAX_HIDDEN, MOE_MAX_TOPK = 2048, 16384, 32
+MOE_MAX_EXPERTS, MOE_MAX_HIDDEN, MOE_MAX_TOPK, MOE_MAX_SOURCES = 2048, 16384, 32, 384
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_ep.so")
 
@@ -49,6 +50,11 @@ _SIGS = {
                      _INT),
     "moe_combine": ([_P, _INT, _SZ, _I32, _I32, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _INT, _P],
                     _INT),
+    "moe_notify_multi": ([_P, _I32, _I32, _I32, _P, _P, _P, _P, _P], _INT),
+    "moe_dispatch_src": ([_P, _INT, _I32, _I32, _I32, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _INT, _P,
+                          _SZ, _P], _INT),
+    "moe_combine_src": ([_P, _INT, _SZ, _I32, _I32, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P,
+                         _INT, _P], _INT),
     "moe_fused_supported": ([_I32, _I32, _I32, _I32, _I32, _INT, _INT, ctypes.POINTER(_INT)], _INT),
     "moe_layout_notify_dispatch": ([_P, _INT, _I32, _I32, _I32, _P, _I32, _I32, _INT, _P, _P, _P, _P, _P, _P,
                                     _P, _P, _P, _SZ, _P, _SZ, _P], _INT),
@@ -198,6 +204,57 @@ def moe_combine(recv_x: torch.Tensor, recv_type: int, hidden: int, topk_idx: tor
         dtype_code(out.dtype), _stream(stream)))
 
 
+def moe_notify_multi(token_per_expert: torch.Tensor, expert_num_per_rank: int, rank_size: int,
+                     put_offset: torch.Tensor, recv_count: torch.Tensor, recv_base: torch.Tensor,
+                     recv_token_per_expert: torch.Tensor, stream=None) -> None:
+    """token_per_expert [S, E] -> put_offset [E, S] and the per-rank arrays."""
+    if token_per_expert.dim() != 2:
+        raise ValueError("token_per_expert must be [num_src, E]")
+    num_src, e = token_per_expert.shape
+    if tuple(put_offset.shape) != (e, num_src):
+        raise ValueError("put_offset must be [E, num_src]")
+    _check("moe_notify_multi", _lib.moe_notify_multi(
+        _dev(token_per_expert, "token_per_expert", torch.int32), num_src, expert_num_per_rank,
+        rank_size, _dev(put_offset, "put_offset", torch.int32),
+        _dev(recv_count, "recv_count", torch.int32), _dev(recv_base, "recv_base", torch.int32),
+        _dev(recv_token_per_expert, "recv_token_per_expert", torch.int32), _stream(stream)))
+
+
+def moe_dispatch_src(x: torch.Tensor, topk_idx: torch.Tensor, send_token_idx: torch.Tensor,
+                     put_offset: torch.Tensor, recv_base: torch.Tensor, expert_num_per_rank: int,
+                     rank_size: int, src_rank: int, quant_int8: bool, recv_x: torch.Tensor,
+                     stream=None) -> None:
+    """Dispatch of source ``src_rank``; put_offset is [E, num_src]."""
+    if x.dim() != 2 or topk_idx.dim() != 2 or put_offset.dim() != 2:
+        raise ValueError("x must be [bs, hidden], topk_idx [bs, topk], put_offset [E, num_src]")
+    bs, hidden = x.shape
+    topk = topk_idx.shape[1]
+    _check("moe_dispatch_src", _lib.moe_dispatch_src(
+        _dev(x, "x"), dtype_code(x.dtype), bs, hidden, topk,
+        _dev(topk_idx, "topk_idx", torch.int32), _dev(send_token_idx, "send_token_idx", torch.int32),
+        _dev(put_offset, "put_offset", torch.int32), _dev(recv_base, "recv_base", torch.int32),
+        expert_num_per_rank, rank_size, put_offset.shape[1], src_rank, 1 if quant_int8 else 0,
+        _dev(recv_x, "recv_x"), recv_x.numel() * recv_x.element_size(), _stream(stream)))
+
+
+def moe_combine_src(recv_x: torch.Tensor, recv_type: int, hidden: int, topk_idx: torch.Tensor,
+                    topk_weights: torch.Tensor, send_token_idx: torch.Tensor, put_offset: torch.Tensor,
+                    recv_base: torch.Tensor, expert_num_per_rank: int, rank_size: int, src_rank: int,
+                    out: torch.Tensor, stream=None) -> None:
+    """Combine of source ``src_rank``; put_offset is [E, num_src]."""
+    if topk_idx.dim() != 2 or put_offset.dim() != 2:
+        raise ValueError("topk_idx must be [bs, topk] and put_offset [E, num_src]")
+    bs, topk = topk_idx.shape
+    if out.dim() != 2 or tuple(out.shape) != (bs, hidden):
+        raise ValueError("out must be [bs, hidden]")
+    _check("moe_combine_src", _lib.moe_combine_src(
+        _dev(recv_x, "recv_x"), recv_type, recv_x.numel() * recv_x.element_size(), bs, hidden, topk,
+        _dev(topk_idx, "topk_idx", torch.int32), _dev(topk_weights, "topk_weights", torch.float32),
+        _dev(send_token_idx, "send_token_idx", torch.int32), _dev(put_offset, "put_offset", torch.int32),
+        _dev(recv_base, "recv_base", torch.int32), expert_num_per_rank, rank_size, put_offset.shape[1],
+        src_rank, _dev(out, "out"), dtype_code(out.dtype), _stream(stream)))
+
+
 def moe_fused_supported(bs: int, hidden: int, topk: int, expert_num_per_rank: int, rank_size: int,
                         x_dtype: torch.dtype, quant_int8: bool) -> bool:
     out = _INT(0)
@@ -290,4 +347,69 @@ class EpBuffers:
             self.notify(stream)
             self.dispatch(x, topk_idx, stream)
         self.combine(topk_idx, topk_w, stream)
+        return self.out
+
+
+class EpMultiBuffers:
+    """Device buffers for several source ranks sharing one receive buffer
+    (one GPU standing in for the sources of an expert-parallel group).
+
+    Source s has ``sizes[s]`` tokens; each source keeps its own layout
+    outputs and combine output, the notify outputs and the receive buffer
+    (sum of the sources' bs * topk rows) are shared.  ``run`` enqueues every
+    source's layout, one notify over the [S, E] count matrix, every source's
+    dispatch, then every source's combine, on one stream."""
+
+    def __init__(self, sizes, hidden: int, topk: int, expert_num_per_rank: int, rank_size: int,
+                 x_dtype: torch.dtype = torch.bfloat16, quant_int8: bool = True,
+                 out_dtype: Optional[torch.dtype] = None, device="cuda"):
+        sizes = [int(b) for b in sizes]
+        if not sizes:
+            raise ValueError("at least one source")
+        e = expert_num_per_rank * rank_size
+        self.sizes, self.hidden, self.topk = sizes, hidden, topk
+        self.num_src = len(sizes)
+        self.epr, self.ranks, self.num_experts = expert_num_per_rank, rank_size, e
+        self.quant_int8 = quant_int8
+        self.recv_type = MOE_INT8_ROWSCALE if quant_int8 else dtype_code(x_dtype)
+        self.row_bytes = moe_recv_row_bytes(hidden, self.recv_type)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.token_per_expert = torch.zeros((self.num_src, e), **i32)
+        self.token_per_rank = torch.zeros((self.num_src, rank_size), **i32)
+        self.send_token_idx = [torch.zeros((b, topk), **i32) for b in sizes]
+        self.bad_id_count = torch.zeros(self.num_src, **i32)
+        ws = max(moe_layout_workspace_bytes(b, topk, e) for b in sizes)
+        self.workspace = torch.zeros(max(ws, 4) // 4, **i32)
+        self.put_offset = torch.zeros((e, self.num_src), **i32)
+        self.recv_count = torch.zeros(rank_size, **i32)
+        self.recv_base = torch.zeros(rank_size, **i32)
+        self.recv_token_per_expert = torch.zeros(e, **i32)
+        self.total_rows = sum(sizes) * topk
+        self.recv_x = torch.zeros(self.total_rows * self.row_bytes, dtype=torch.uint8, device=device)
+        self.out = [torch.zeros((b, hidden), dtype=out_dtype or x_dtype, device=device) for b in sizes]
+
+    def layout(self, src: int, topk_idx, stream=None):
+        moe_layout(topk_idx, self.epr, self.ranks, self.token_per_expert[src], self.token_per_rank[src],
+                   self.send_token_idx[src], self.bad_id_count[src:src + 1], self.workspace, stream)
+
+    def notify(self, stream=None):
+        moe_notify_multi(self.token_per_expert, self.epr, self.ranks, self.put_offset, self.recv_count,
+                         self.recv_base, self.recv_token_per_expert, stream)
+
+    def dispatch(self, src: int, x, topk_idx, stream=None):
+        moe_dispatch_src(x, topk_idx, self.send_token_idx[src], self.put_offset, self.recv_base, self.epr,
+                         self.ranks, src, self.quant_int8, self.recv_x, stream)
+
+    def combine(self, src: int, topk_idx, topk_w, stream=None):
+        moe_combine_src(self.recv_x, self.recv_type, self.hidden, topk_idx, topk_w, self.send_token_idx[src],
+                        self.put_offset, self.recv_base, self.epr, self.ranks, src, self.out[src], stream)
+
+    def run(self, xs, idxs, ws, stream=None):
+        for src in range(self.num_src):
+            self.layout(src, idxs[src], stream)
+        self.notify(stream)
+        for src in range(self.num_src):
+            self.dispatch(src, xs[src], idxs[src], stream)
+        for src in range(self.num_src):
+            self.combine(src, idxs[src], ws[src], stream)
         return self.out

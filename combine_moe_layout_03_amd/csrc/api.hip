@@ -58,14 +58,23 @@ int row_bytes(int32_t hidden, moe_dtype recv, size_t* bytes) {
   }
 }
 
-// Routing arguments common to dispatch and combine.
+// Source count and index of a multi-source call.
+int check_sources(int32_t num_src, int32_t src_rank) {
+  if (num_src < 1 || src_rank < 0 || src_rank >= num_src) return MOE_ERR_BAD_SHAPE;
+  if (num_src > MOE_MAX_SOURCES) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Routing arguments common to dispatch and combine; source src_rank of
+// num_src reads column src_rank of putOffset [E][num_src].
 int make_route(int32_t bs, int32_t hidden, int32_t topk, const int32_t* topk_idx,
                const int32_t* send_token_idx, const int32_t* put_offset, const int32_t* recv_base,
-               int32_t epr, int32_t ranks, moe_dtype recv_type, size_t recv_bytes,
-               moe::RouteArgs* r) {
+               int32_t epr, int32_t ranks, int32_t num_src, int32_t src_rank, moe_dtype recv_type,
+               size_t recv_bytes, moe::RouteArgs* r) {
   int st = check_tokens(bs, topk);
   if (st) return st;
   if ((st = check_experts(epr, ranks))) return st;
+  if ((st = check_sources(num_src, src_rank))) return st;
   if ((st = check_hidden(hidden))) return st;
   size_t rb = 0;
   if ((st = row_bytes(hidden, recv_type, &rb))) return st;
@@ -78,7 +87,8 @@ int make_route(int32_t bs, int32_t hidden, int32_t topk, const int32_t* topk_idx
   if (recv_bytes < need) return MOE_ERR_BUFFER_TOO_SMALL;
   r->topk_idx = topk_idx;
   r->send_token_idx = send_token_idx;
-  r->put_offset = put_offset;
+  r->put_offset = put_offset + src_rank;
+  r->put_stride = num_src;
   r->recv_base = recv_base;
   r->bs = bs;
   r->hidden = hidden;
@@ -148,16 +158,40 @@ int moe_notify(const int32_t* token_per_expert, int32_t epr, int32_t ranks, int3
                                        static_cast<hipStream_t>(stream)));
 }
 
+int moe_notify_multi(const int32_t* token_per_expert, int32_t num_src, int32_t epr, int32_t ranks,
+                     int32_t* put_offset, int32_t* recv_count, int32_t* recv_base,
+                     int32_t* recv_token_per_expert, void* stream) {
+  int st = check_experts(epr, ranks);
+  if (st) return st;
+  if ((st = check_sources(num_src, 0))) return st;
+  if (!token_per_expert || !put_offset || !recv_count || !recv_base || !recv_token_per_expert)
+    return MOE_ERR_NULL_PTR;
+  if (!aligned(token_per_expert, 4) || !aligned(put_offset, 4) || !aligned(recv_count, 4) ||
+      !aligned(recv_base, 4) || !aligned(recv_token_per_expert, 4))
+    return MOE_ERR_BAD_ALIGN;
+  return hip_status(moe::launch_notify_multi(token_per_expert, num_src, epr, ranks, put_offset,
+                                             recv_count, recv_base, recv_token_per_expert,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int moe_dispatch(const void* x, moe_dtype x_type, int32_t bs, int32_t hidden, int32_t topk,
                  const int32_t* topk_idx, const int32_t* send_token_idx, const int32_t* put_offset,
                  const int32_t* recv_base, int32_t epr, int32_t ranks, int quant_int8,
                  void* recv_x, size_t recv_x_bytes, void* stream) {
+  return moe_dispatch_src(x, x_type, bs, hidden, topk, topk_idx, send_token_idx, put_offset, recv_base,
+                          epr, ranks, 1, 0, quant_int8, recv_x, recv_x_bytes, stream);
+}
+
+int moe_dispatch_src(const void* x, moe_dtype x_type, int32_t bs, int32_t hidden, int32_t topk,
+                     const int32_t* topk_idx, const int32_t* send_token_idx, const int32_t* put_offset,
+                     const int32_t* recv_base, int32_t epr, int32_t ranks, int32_t num_src,
+                     int32_t src_rank, int quant_int8, void* recv_x, size_t recv_x_bytes, void* stream) {
   if (x_type != MOE_BF16 && x_type != MOE_FP16) return MOE_ERR_BAD_DTYPE;
   if (quant_int8 != 0 && quant_int8 != 1) return MOE_ERR_BAD_DTYPE;
   const moe_dtype recv_type = quant_int8 ? MOE_INT8_ROWSCALE : x_type;
   moe::RouteArgs r{};
   int st = make_route(bs, hidden, topk, topk_idx, send_token_idx, put_offset, recv_base, epr, ranks,
-                      recv_type, recv_x_bytes, &r);
+                      num_src, src_rank, recv_type, recv_x_bytes, &r);
   if (st) return st;
   if (bs == 0) return MOE_OK;
   if (!x || !recv_x) return MOE_ERR_NULL_PTR;
@@ -170,12 +204,21 @@ int moe_combine(const void* recv_x, moe_dtype recv_type, size_t recv_x_bytes, in
                 int32_t hidden, int32_t topk, const int32_t* topk_idx, const float* topk_weights,
                 const int32_t* send_token_idx, const int32_t* put_offset, const int32_t* recv_base,
                 int32_t epr, int32_t ranks, void* out, moe_dtype out_type, void* stream) {
+  return moe_combine_src(recv_x, recv_type, recv_x_bytes, bs, hidden, topk, topk_idx, topk_weights,
+                         send_token_idx, put_offset, recv_base, epr, ranks, 1, 0, out, out_type, stream);
+}
+
+int moe_combine_src(const void* recv_x, moe_dtype recv_type, size_t recv_x_bytes, int32_t bs,
+                    int32_t hidden, int32_t topk, const int32_t* topk_idx, const float* topk_weights,
+                    const int32_t* send_token_idx, const int32_t* put_offset, const int32_t* recv_base,
+                    int32_t epr, int32_t ranks, int32_t num_src, int32_t src_rank, void* out,
+                    moe_dtype out_type, void* stream) {
   if (recv_type != MOE_BF16 && recv_type != MOE_FP16 && recv_type != MOE_INT8_ROWSCALE)
     return MOE_ERR_BAD_DTYPE;
   if (out_type != MOE_BF16 && out_type != MOE_FP16 && out_type != MOE_FP32) return MOE_ERR_BAD_DTYPE;
   moe::RouteArgs r{};
   int st = make_route(bs, hidden, topk, topk_idx, send_token_idx, put_offset, recv_base, epr, ranks,
-                      recv_type, recv_x_bytes, &r);
+                      num_src, src_rank, recv_type, recv_x_bytes, &r);
   if (st) return st;
   if (bs == 0) return MOE_OK;
   if (!recv_x || !out || !topk_weights) return MOE_ERR_NULL_PTR;

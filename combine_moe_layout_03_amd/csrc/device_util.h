@@ -68,7 +68,9 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Receive rows of kN (<= 64) consecutive entries j0 .. j0+kN-1 of token t.
-// Entry j goes to row recvBase[e / EPR] + putOffset[e] + sendTokenIdx[t, j];
+// Entry j goes to row recvBase[e / EPR] + putOffset[e] + sendTokenIdx[t, j]
+// (putOffset[e] is this source's column of the [E][S] offsets with S
+// sources: put_offset[e * put_stride]);
 // an entry that is past topk, has an id outside [0, E) or a negative slot,
 // or whose row falls outside the buffer, is not dispatched (valid = false,
 // offset 0).  Lane j resolves entry j0 + j with vector loads (one load
@@ -88,7 +90,7 @@ __device__ __forceinline__ void resolve_rows(const Route& a, int t, int j0, int 
   const int slot = a.send_token_idx[i];
   const int ec = min(max(e, 0), a.num_experts - 1);
   const int rank = static_cast<int>((static_cast<uint64_t>(ec) * a.epr_magic) >> 32);
-  const int64_t row = static_cast<int64_t>(a.recv_base[rank]) + a.put_offset[ec] + slot;
+  const int64_t row = static_cast<int64_t>(a.recv_base[rank]) + a.put_offset[ec * a.put_stride] + slot;
   const bool ok = (j0 + j < a.k) && static_cast<unsigned>(e) < static_cast<unsigned>(a.num_experts) &&
                   slot >= 0 && row >= 0 && row < a.cap_rows;
   const int64_t off = ok ? row * a.row_bytes : 0;

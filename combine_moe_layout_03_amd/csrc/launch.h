@@ -45,14 +45,19 @@ hipError_t launch_layout(const int32_t* topk_idx, int32_t n, int32_t num_experts
 hipError_t launch_notify(const int32_t* token_per_expert, int32_t epr, int32_t ranks,
                          int32_t* put_offset, int32_t* recv_count, int32_t* recv_base,
                          int32_t* recv_token_per_expert, hipStream_t stream);
+hipError_t launch_notify_multi(const int32_t* token_per_expert, int32_t num_src, int32_t epr,
+                               int32_t ranks, int32_t* put_offset, int32_t* recv_count,
+                               int32_t* recv_base, int32_t* recv_token_per_expert,
+                               hipStream_t stream);
 
 // ---- dispatch / combine ---------------------------------------------------------
 struct RouteArgs {
   const int32_t* topk_idx;        // [bs, k]
   const int32_t* send_token_idx;  // [bs, k]
-  const int32_t* put_offset;      // [E]
+  const int32_t* put_offset;      // column of [E][put_stride]: putOffset[e] at put_offset[e * put_stride]
   const int32_t* recv_base;       // [R]
   int32_t bs, hidden, k, epr, num_experts;
+  int32_t put_stride;  // number of source ranks (1: a single source)
   int64_t row_bytes;   // bytes per receive row
   int64_t cap_rows;    // rows that fit in the receive buffer
   int32_t scale_off;   // byte offset of the inverse scale in an int8 row

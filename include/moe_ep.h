@@ -71,6 +71,8 @@ enum {
 #define MOE_MAX_EXPERTS 2048   /* E = R * EPR */
 #define MOE_MAX_HIDDEN 16384   /* h */
 #define MOE_MAX_TOPK 32        /* k */
+#define MOE_MAX_SOURCES 384    /* source ranks sharing one receive buffer (the
+                                  page's CAM_MAX_RANK_SIZE) */
 
 /* Bytes of one receive-buffer row for hidden size `hidden` and receive type
  * `recv` (page 2.5 and 2.2.1):
@@ -162,6 +164,51 @@ int moe_combine(const void* recvX, moe_dtype recvType, size_t recvXBytes, int32_
                 const int32_t* sendTokenIdx, const int32_t* putOffset, const int32_t* recvBase,
                 int32_t expertNumPerRank, int32_t rankSize, void* out, moe_dtype outType,
                 void* stream);
+
+/* ---- Several source ranks sharing one receive buffer -------------------- */
+
+/* Stage 2 with S = numSrc source ranks (page 2.4: every rank's
+ * tokenPerExpert is all-gathered before the prefix sums; page 2.6: combine
+ * reads the base of (expert, source) at index expertId * epWorldSize +
+ * srcRank).  Inside destination rank r the rows are ordered by expert
+ * (ascending), then by source (ascending), then by send slot; the ranks'
+ * regions are concatenated in rank order.
+ * In:  tokenPerExpert     device int32 [S][E]: row s is source s's
+ *                         moe_layout output.
+ * Out: putOffset          device int32 [E][S]: start of the rows of
+ *                         (expert e, source s) inside e's rank region.
+ *      recvCount          device int32 [R]: rows in rank r's region.
+ *      recvBase           device int32 [R]: first row of rank r's region.
+ *      recvTokenPerExpert device int32 [E]: rows expert e receives from all
+ *                         sources.
+ * Requires 1 <= numSrc <= MOE_MAX_SOURCES; the total row count must fit in
+ * int32.  With numSrc == 1 the outputs equal moe_notify's. */
+int moe_notify_multi(const int32_t* tokenPerExpert, int32_t numSrc, int32_t expertNumPerRank,
+                     int32_t rankSize, int32_t* putOffset, int32_t* recvCount, int32_t* recvBase,
+                     int32_t* recvTokenPerExpert, void* stream);
+
+/* moe_dispatch for source srcRank of numSrc: entry (t, j) with a valid id e
+ * and slot s >= 0 writes to receive row
+ *     recvBase[e / EPR] + putOffset[e][srcRank] + s
+ * with putOffset [E][numSrc] and recvBase from moe_notify_multi.  The
+ * receive buffer is shared by all sources; it must hold at least this
+ * source's bs * topk rows (the sum over sources for all rows to land; rows
+ * past recvXBytes are skipped).  Other arguments as moe_dispatch.  Calls for
+ * different sources write disjoint rows and may run concurrently. */
+int moe_dispatch_src(const void* x, moe_dtype xType, int32_t bs, int32_t hidden, int32_t topk,
+                     const int32_t* topkIdx, const int32_t* sendTokenIdx, const int32_t* putOffset,
+                     const int32_t* recvBase, int32_t expertNumPerRank, int32_t rankSize,
+                     int32_t numSrc, int32_t srcRank, int quantInt8, void* recvX,
+                     size_t recvXBytes, void* stream);
+
+/* moe_combine for source srcRank of numSrc: reads the rows moe_dispatch_src
+ * wrote for that source (same row formula), with the same arithmetic and
+ * bit-exactness as moe_combine.  Other arguments as moe_combine. */
+int moe_combine_src(const void* recvX, moe_dtype recvType, size_t recvXBytes, int32_t bs,
+                    int32_t hidden, int32_t topk, const int32_t* topkIdx, const float* topkWeights,
+                    const int32_t* sendTokenIdx, const int32_t* putOffset, const int32_t* recvBase,
+                    int32_t expertNumPerRank, int32_t rankSize, int32_t numSrc, int32_t srcRank,
+                    void* out, moe_dtype outType, void* stream);
 
 /* ---- Fused layout + notify + dispatch ------------------------------------ */
 

@@ -35,7 +35,7 @@ def test_header_symbols_exported(M):
 
 def test_header_constants_match_binding(M):
     text = open(HEADER).read()
-    for name in ("MOE_MAX_EXPERTS", "MOE_MAX_HIDDEN", "MOE_MAX_TOPK"):
+    for name in ("MOE_MAX_EXPERTS", "MOE_MAX_HIDDEN", "MOE_MAX_TOPK", "MOE_MAX_SOURCES"):
         val = int(re.search(rf"#define {name} (\d+)", text).group(1))
         assert getattr(M, name) == val
 
@@ -134,6 +134,38 @@ def test_combine_rejects_on_host(M):
     assert L.moe_combine(*args(out=P + 2)) == 3
     assert L.moe_combine(*args(h=12)) == 7
     assert L.moe_combine(*args(bs=0, recv=None, out=None, w=None, cap=0)) == 0
+
+
+def test_multi_source_rejects_on_host(M):
+    # every call below has an invalid argument, so it returns before any HIP call
+    L = M._lib
+    assert L.moe_notify_multi(P, 0, 4, 4, P, P, P, P, None) == 2          # no source
+    assert L.moe_notify_multi(P, 385, 4, 4, P, P, P, P, None) == 7        # above MOE_MAX_SOURCES
+    assert L.moe_notify_multi(P, 4, 0, 4, P, P, P, P, None) == 2
+    assert L.moe_notify_multi(P, 4, 4, 1024, P, P, P, P, None) == 7       # E above the maximum
+    assert L.moe_notify_multi(None, 4, 4, 4, P, P, P, P, None) == 1
+    assert L.moe_notify_multi(P, 4, 4, 4, P, P, P, None, None) == 1
+    assert L.moe_notify_multi(P, 4, 4, 4, P + 2, P, P, P, None) == 3
+    rb = M.moe_recv_row_bytes(7168, 3)
+    cap = 4096 * 8 * rb
+
+    def dis(**kw):
+        return L.moe_dispatch_src(kw.get("x", P), 0, kw.get("bs", 4096), 7168, 8, P, P, P, P, 16, 16,
+                                  kw.get("ns", 4), kw.get("src", 0), 1, P, kw.get("cap", cap), None)
+
+    def com(**kw):
+        return L.moe_combine_src(P, 3, kw.get("cap", cap), kw.get("bs", 4096), 7168, 8, P,
+                                 kw.get("w", P), P, P, P, 16, 16, kw.get("ns", 4), kw.get("src", 0),
+                                 kw.get("out", P), 0, None)
+    for f in (dis, com):
+        assert f(src=-1) == 2
+        assert f(src=4) == 2
+        assert f(ns=0) == 2
+        assert f(ns=385, src=1) == 7
+        assert f(src=3, cap=cap - 1) == 6
+    assert dis(src=2, x=None) == 1
+    assert com(src=2, w=None) == 1
+    assert com(src=1, out=P + 2) == 3
 
 
 def test_fused_supported_is_host_logic(M):
