@@ -189,23 +189,29 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(RouteArgs a,
 
   // Software pipeline over this lane's chunks c, c + S, c + 2S, ...: the k
   // loads of the next chunk are issued before the current one is summed.
-  // Chunk indices past the row's end are clamped for the loads (the data is
-  // not used), so every load is issued unconditionally.
+  // `iters` counts the rounds in which this wave has at least one chunk (a
+  // wave-uniform bound, so no load is issued for a round the wave does not
+  // sum); lanes past the row's end inside such a round load its last chunk
+  // (clamped index, data unused), so the loads of a round need no branches.
   const int chunks = a.hidden / kElems;
   constexpr int kStride = kWave * kWpt;
-  const int iters = (chunks + kStride - 1) / kStride;
+  const int first = part * kWave;
+  const int iters = chunks > first ? (chunks - first + kStride - 1) / kStride : 0;
   const size_t out_base = static_cast<size_t>(t) * a.hidden;
-  int c = lane + part * kWave;
+  int c = lane + first;
+  if (iters == 0) return;
   C buf_a[kMaxK], buf_b[kMaxK];
   load_rows<kRecv, kMaxK, kElems, kNtLoad>(buf_a, base, row_off, min(c, chunks - 1));
   for (int it = 0; it < iters; it += 2) {
-    load_rows<kRecv, kMaxK, kElems, kNtLoad>(buf_b, base, row_off, min(c + kStride, chunks - 1));
+    if (it + 1 < iters)
+      load_rows<kRecv, kMaxK, kElems, kNtLoad>(buf_b, base, row_off, min(c + kStride, chunks - 1));
     if (c < chunks)
       fold_and_store<kRecv, kOut, kMaxK, kElems, kNtStore>(buf_a, valid, wj, invj, out,
                                                  out_base + static_cast<size_t>(c) * kElems);
     c += kStride;
     if (it + 1 >= iters) break;
-    load_rows<kRecv, kMaxK, kElems, kNtLoad>(buf_a, base, row_off, min(c + kStride, chunks - 1));
+    if (it + 2 < iters)
+      load_rows<kRecv, kMaxK, kElems, kNtLoad>(buf_a, base, row_off, min(c + kStride, chunks - 1));
     if (c < chunks)
       fold_and_store<kRecv, kOut, kMaxK, kElems, kNtStore>(buf_b, valid, wj, invj, out,
                                                  out_base + static_cast<size_t>(c) * kElems);
