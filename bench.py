@@ -163,6 +163,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large", choices=["tiny", "small", "mid", "large", "stress"])
     ap.add_argument("--mode", default="int8", choices=["int8", "pass"])
+    ap.add_argument("--x-dtype", default="bf16", choices=["bf16", "fp16"],
+                    help="element type of x (and of the combine output)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work (0: skip)")
     ap.add_argument("--flush-mib", type=int, default=1024)
     ap.add_argument("--event-flags", default="nofence", choices=["nofence", "default"],
@@ -198,12 +200,13 @@ def main(argv=None) -> int:
     quant = args.mode == "int8"
 
     log(f"generating workload {args.workload}")
-    w = W.make_workload(args.workload)
-    x = torch.from_numpy(w.x.view("int16")).to(dev).view(torch.bfloat16)
+    w = W.make_workload(args.workload, args.x_dtype)
+    xt = torch.float16 if args.x_dtype == "fp16" else torch.bfloat16
+    x = torch.from_numpy(w.x.view("int16")).to(dev).view(xt)
     idx = torch.from_numpy(w.topk_idx).to(dev)
     wts = torch.from_numpy(w.topk_w).to(dev)
     buf = M.EpBuffers(w.bs, w.hidden, w.topk, w.expert_num_per_rank, w.rank_size,
-                      x_dtype=torch.bfloat16, quant_int8=quant, out_dtype=torch.bfloat16)
+                      x_dtype=xt, quant_int8=quant, out_dtype=xt)
     flush = torch.ones(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
     flush_out = torch.zeros((), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -217,7 +220,7 @@ def main(argv=None) -> int:
 
     fused = args.path == "fused"
     if fused and not M.moe_fused_supported(w.bs, w.hidden, w.topk, w.expert_num_per_rank, w.rank_size,
-                                           torch.bfloat16, quant):
+                                           xt, quant):
         log("the fused kernel does not apply to this shape; the fused entry point runs the three stages")
 
     def first_stages():
@@ -333,12 +336,13 @@ def main(argv=None) -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp32",
-        "payload": ("bf16 rows in, int8 codes + fp32 inverse scale per row on the wire, bf16 out"
-                    if quant else "bf16 rows in and on the wire, bf16 out"),
+        "payload": (f"{args.x_dtype} rows in, int8 codes + fp32 inverse scale per row on the wire, "
+                    f"{args.x_dtype} out" if quant
+                    else f"{args.x_dtype} rows in and on the wire, {args.x_dtype} out"),
         "data": "synthetic",
         "config": {"workload": args.workload, "bs": w.bs, "hidden": w.hidden, "topk": w.topk,
-                   "num_experts": w.num_experts, "rank_size": w.rank_size, "x_dtype": "bf16",
-                   "dispatch": "int8" if quant else "passthrough", "out_dtype": "bf16",
+                   "num_experts": w.num_experts, "rank_size": w.rank_size, "x_dtype": args.x_dtype,
+                   "dispatch": "int8" if quant else "passthrough", "out_dtype": args.x_dtype,
                    "parallelism": "1 GPU, ranks are logical partitions of one receive buffer"},
         "step": "layout + notify + dispatch + combine, caches flushed before the step and before combine",
         "path": ("layout+notify+dispatch fused in one launch, then combine" if fused
@@ -381,7 +385,7 @@ def bench_sources(args, M, torch, w, x, idx, wts, quant: bool, do_flush, stream)
     idxs = [idx[s * per:(s + 1) * per] for s in range(n_src)]
     wss = [wts[s * per:(s + 1) * per] for s in range(n_src)]
     buf = M.EpMultiBuffers([per] * n_src, w.hidden, w.topk, w.expert_num_per_rank, w.rank_size,
-                           x_dtype=torch.bfloat16, quant_int8=quant, out_dtype=torch.bfloat16)
+                           x_dtype=x.dtype, quant_int8=quant, out_dtype=x.dtype)
     log(f"{n_src} sources of {per} tokens: warm-up x{args.warmup}")
     for _ in range(args.warmup):
         do_flush()
@@ -439,12 +443,13 @@ def bench_sources(args, M, torch, w, x, idx, wts, quant: bool, do_flush, stream)
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp32",
-        "payload": ("bf16 rows in, int8 codes + fp32 inverse scale per row on the wire, bf16 out"
-                    if quant else "bf16 rows in and on the wire, bf16 out"),
+        "payload": (f"{args.x_dtype} rows in, int8 codes + fp32 inverse scale per row on the wire, "
+                    f"{args.x_dtype} out" if quant
+                    else f"{args.x_dtype} rows in and on the wire, {args.x_dtype} out"),
         "data": "synthetic",
         "config": {"workload": args.workload, "bs": w.bs, "hidden": w.hidden, "topk": w.topk,
-                   "num_experts": w.num_experts, "rank_size": w.rank_size, "x_dtype": "bf16",
-                   "dispatch": "int8" if quant else "passthrough", "out_dtype": "bf16",
+                   "num_experts": w.num_experts, "rank_size": w.rank_size, "x_dtype": args.x_dtype,
+                   "dispatch": "int8" if quant else "passthrough", "out_dtype": args.x_dtype,
                    "sources": n_src, "tokens_per_source": per,
                    "parallelism": "1 GPU, source and destination ranks are logical partitions"},
         "step": (f"{n_src} layouts + notify over the [{n_src}, E] counts, {n_src} dispatches, {n_src} "

@@ -46,6 +46,8 @@
 namespace moe {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kWaves = kFusedWaves;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kQuads = 8;       // 16-byte id loads per thread in a whole batch
@@ -129,10 +131,15 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   const int t_first = t_begin + wave;
   const int t_pre = t_first < t_end ? t_first : t_end - 1;
   int b = 0;
+  // The row is loaded during the count when it fits in registers beside a
+  // whole batch of ids (up to 14 chunks per lane, h <= 7168); a longer row
+  // would spill, so it is loaded after the count.
+  constexpr bool kRowDuringCount = kVpl <= 14;
   const bool whole = a.ids_aligned16 && n >= kBatch;
+  const bool row_early = whole && kRowDuringCount;
   if (whole) {
     load_batch(0);
-    load_row<kVpl>(v, a.x, t_pre, a.hidden, lane);
+    if (row_early) load_row<kVpl>(v, a.x, t_pre, a.hidden, lane);
     count_batch(0);
     for (b = kBatch; b + kBatch <= n; b += kBatch) {
       load_batch(b);
@@ -152,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
       if (i < n) count_one(i, ids[u]);
     }
   }
-  if (!whole) load_row<kVpl>(v, a.x, t_pre, a.hidden, lane);  // few ids: counted first
+  if (!row_early) load_row<kVpl>(v, a.x, t_pre, a.hidden, lane);  // few ids, or a long row: counted first
   __syncthreads();
   for (int e = tid; e <= E; e += kThreads) {
     int sp = 0, st = 0;
@@ -253,11 +260,14 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
         if (slot < 0) continue;
         const int64_t row = static_cast<int64_t>(gsc[ids_l[li0 + j]]) + slot;  // recvBase[rank] + putOffset[e]
         if (row >= a.cap_rows) continue;
-        uint4* dst = reinterpret_cast<uint4*>(a.recv + row * a.row_bytes);
+        u32x4* dst = reinterpret_cast<u32x4*>(a.recv + row * a.row_bytes);
+        // Element-wise vector stores: a whole-struct uint4 copy here is a
+        // 16-byte memcpy out of v, which kept v in scratch memory (240 bytes
+        // per lane at h = 7168) and doubled the passthrough time.
 #pragma unroll
         for (int i = 0; i < kVpl; ++i) {
           const int c = lane + i * kWave;
-          if (c < chunks) dst[c] = v[i];
+          if (c < chunks) dst[c] = u32x4{v[i].x, v[i].y, v[i].z, v[i].w};
         }
       }
     } else {
