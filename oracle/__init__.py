@@ -47,6 +47,9 @@ _SIGS = {
                         _P, _P, _P],
     "oracle_combine": [_P, _P, _P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _I64,
                        _I64, _P, _INT, _P],
+    "oracle_exp_f32": [_P, _P, _I64],
+    "oracle_swiglu_quant_row": [_P, _I64, _P, ctypes.c_float, _P, _P, _P],
+    "oracle_swiglu_quant": [_P, _I64, _I64, _P, _P, _I64, _P, _P],
 }
 
 
@@ -166,6 +169,48 @@ class Oracle:
         _check(self.L.oracle_quant_row(_ptr(x), _KIND[x_kind], x.size, _ptr(codes),
                                        ctypes.addressof(inv), ctypes.addressof(s)), "quant_row")
         return codes, np.float32(inv.value), np.float32(s.value)
+
+    def exp_f32(self, x: np.ndarray) -> np.ndarray:
+        """The oracle's binary32 e^x (Cody-Waite reduction, degree-7 Taylor)."""
+        xs = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.zeros_like(xs)
+        _check(self.L.oracle_exp_f32(_ptr(xs), _ptr(out), xs.size), "exp_f32")
+        return out
+
+    def swiglu_quant_row(self, acc: np.ndarray, weight_scale: np.ndarray, token_scale: float):
+        """Epilogue of one row (acc int32 [2n]): (codes int8 [n], inv float32,
+        activations float32 [n] before quantisation)."""
+        a = np.ascontiguousarray(acc, dtype=np.int32).reshape(-1)
+        ws = np.ascontiguousarray(weight_scale, dtype=np.float32).reshape(-1)
+        if a.size % 2 or ws.size != a.size:
+            raise ValueError("acc and weight_scale: 2n values each")
+        n = a.size // 2
+        codes = np.zeros(n, np.int8)
+        act = np.zeros(n, np.float32)
+        inv = ctypes.c_float(0.0)
+        _check(self.L.oracle_swiglu_quant_row(_ptr(a), n, _ptr(ws), float(np.float32(token_scale)),
+                                              _ptr(codes), ctypes.addressof(inv), _ptr(act)),
+               "swiglu_quant_row")
+        return codes, np.float32(inv.value), act
+
+    def swiglu_quant(self, acc: np.ndarray, weight_scale: np.ndarray,
+                     token_scale: np.ndarray) -> Dict[str, np.ndarray]:
+        """Epilogue of every row: acc int32 [rows, 2n], weight_scale float32
+        [2n], token_scale float32 [rows] -> codes int8 [rows, n], inv [rows]."""
+        a = np.ascontiguousarray(acc, dtype=np.int32)
+        rows, n2 = a.shape
+        if n2 % 2:
+            raise ValueError("acc: [rows, 2n]")
+        n = n2 // 2
+        ws = np.ascontiguousarray(weight_scale, dtype=np.float32).reshape(-1)
+        ts = np.ascontiguousarray(token_scale, dtype=np.float32).reshape(-1)
+        if ws.size != n2 or ts.size != rows:
+            raise ValueError("weight_scale [2n], token_scale [rows]")
+        codes = np.zeros((rows, n), np.int8)
+        inv = np.zeros(rows, np.float32)
+        _check(self.L.oracle_swiglu_quant(_ptr(a), rows, n, _ptr(ws), _ptr(ts), 1, _ptr(codes),
+                                          _ptr(inv)), "swiglu_quant")
+        return dict(codes=codes, inv=inv)
 
     def dispatch(self, x_bits: np.ndarray, x_kind: str, topk_idx: np.ndarray,
                  send_token_idx: np.ndarray, put_offset: np.ndarray, recv_base: np.ndarray,
@@ -336,3 +381,15 @@ def combine(*a, **kw):
 
 def pipeline(*a, **kw):
     return default().pipeline(*a, **kw)
+
+
+def exp_f32(*a, **kw):
+    return default().exp_f32(*a, **kw)
+
+
+def swiglu_quant_row(*a, **kw):
+    return default().swiglu_quant_row(*a, **kw)
+
+
+def swiglu_quant(*a, **kw):
+    return default().swiglu_quant(*a, **kw)

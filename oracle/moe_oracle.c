@@ -18,6 +18,9 @@
  *   2.5  moe_dispatch_normal_zb / QuantProcess (row scatter, dynamic int8),
  *   2.6  moe_combine_normal_zb / ReadBufferAndWeightedSum (weighted gather),
  *   2.8  the per-rank zero-buffer layout (token region read by combine).
+ * and, for the expert-side epilogue between dispatch and combine, section 4
+ * "Fused Deep MoE": 4.3 (stage 2, DeqSwigluQuant) and 4.8.1 (the GMM1
+ * epilogue PerTokenDequantSwiGLU).
  *
  * Everything here is the plain definition, in the order the page gives,
  * single-threaded, in IEEE binary32 where the page fixes float (the quantiser
@@ -38,7 +41,12 @@
  *    (float)q * inv before the weight multiply;
  *  - combine sums j = 0..k-1 from +0.0f, multiply then add, each rounded;
  *  - expert ids outside [0, E) are counted as bad, get slot -1, are not
- *    dispatched and add nothing in combine.
+ *    dispatched and add nothing in combine;
+ *  - the epilogue's SwiGLU is Swish(gate) * up with the gate in the first
+ *    half of the accumulator row (the page shows x*sigmoid(x) on the left
+ *    half and the right half passed through, but not the product), and its
+ *    output row is quantised like a dispatched row; e^x is computed by a
+ *    named published method, written out (exp_cw).
  *
  * Parity pins live in tests/ (brute force, stable-sort and prefix-sum
  * equivalence, hand-worked quantiser rows, order-sensitive combine rows,
@@ -413,6 +421,123 @@ int oracle_combine(const uint16_t *recv_rows, const int8_t *codes, const float *
         ((uint16_t *)out)[t * h + i] = f32_to_f16(acc[i]);
       }
     }
+  }
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Expert-side epilogue between dispatch and combine: dequantise the int32   */
+/* accumulators of the first expert GEMM, SwiGLU, requantise to int8 (the    */
+/* same page, section 4 "Fused Deep MoE": section 4.3 stage 2,               */
+/* DeqSwigluQuant, and section 4.8.1, the GMM1 epilogue PerTokenDequantSwiGLU).*/
+/* ------------------------------------------------------------------------ */
+
+/* e^x in binary32 by a named published method, written out step by step so
+ * that it can be reproduced exactly: Cody and Waite's argument reduction
+ * (W. J. Cody, W. Waite, "Software Manual for the Elementary Functions",
+ * 1980), x = k ln2 + r with ln 2 split as C1 + C2, C1 = 355/512 exact in nine
+ * bits (so k*C1 is exact for |k| < 2^15) and C2 = ln 2 - C1 rounded to
+ * binary32; then e^r by its Taylor series to degree 7 in Horner form
+ * (|r| <= ln2/2, truncation below 2^-27 relative); then the scale by 2^k.
+ *   k  = round-half-even(x * log2(e))          (log2(e) rounded to binary32)
+ *   r  = (x - k*C1) - k*C2                     (each operation rounded)
+ *   p  = 1 + r(1 + r(1/2 + r(1/6 + r(1/24 + r(1/120 + r(1/720 + r/5040))))))
+ *        (each coefficient 1/n! rounded to binary32; multiply, then add)
+ *   result = p * 2^k, as p * 2^127 * 2 for k = 128 and as (p * 2^(k+64)) * 2^-64
+ *   for k < -126 (a subnormal result, rounded once by the last multiply).
+ * Inputs above 89 give +inf and below -104 give +0 (e^89 exceeds the largest
+ * binary32 and e^-104 is below half the smallest subnormal); NaN stays NaN. */
+static float pow2i(int k) { /* 2^k for -126 <= k <= 127 */
+  return bits_to_f32((uint32_t)(k + 127) << 23);
+}
+
+static float exp_cw(float x) {
+  if (x != x) return x;
+  if (x > 89.0f) return INFINITY;
+  if (x < -104.0f) return 0.0f;
+  const float log2e = 1.44269502162933349609375f; /* 0x3FB8AA3B */
+  const float c1 = 0.693359375f;                  /* 355/512 */
+  const float c2 = -2.12194440e-4f;               /* ln 2 - 355/512 */
+  float kf = nearbyintf(x * log2e);
+  int k = (int)kf;
+  float r = x - kf * c1;
+  r = r - kf * c2;
+  float p = 1.0f / 5040.0f;
+  p = p * r + 1.0f / 720.0f;
+  p = p * r + 1.0f / 120.0f;
+  p = p * r + 1.0f / 24.0f;
+  p = p * r + 1.0f / 6.0f;
+  p = p * r + 0.5f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  if (k > 127) return (p * pow2i(127)) * 2.0f;
+  if (k < -126) return (p * pow2i(k + 64)) * pow2i(-64);
+  return p * pow2i(k);
+}
+
+int oracle_exp_f32(const float *in, float *out, int64_t n) {
+  if ((n && (!in || !out)) || n < 0) return ORACLE_BAD_ARG;
+  for (int64_t i = 0; i < n; ++i) out[i] = exp_cw(in[i]);
+  return ORACLE_OK;
+}
+
+/* One row of the first expert GEMM's output: acc[0 .. 2n), the gate half
+ * (columns 0 .. n-1) followed by the up half (columns n .. 2n-1).
+ *   v_c   = (float(acc_c) * weight_scale[c]) * token_scale
+ *           (page 4.8.1 steps 4-6: int32 -> fp32 round-half-even, times the
+ *           column's weight scale, times the token's scale; each rounded)
+ *   act_i = (g / (1 + e^-g)) * u,   g = v_i, u = v_(n+i)
+ *           (steps 7: -g, Exp, +1, Div on the gate half; the up half passes
+ *           through; the two are multiplied, SwiGLU = Swish(gate) * up)
+ *   then the row act[0 .. n) is quantised exactly like a dispatched row:
+ *   amax = max |act_i|, s = 127 / (amax + 1e-12f), q_i = rint(act_i * s),
+ *   inv = 1 / s   (section 4.3 stage 2: "Quantize FP32 -> INT8").
+ * act_out (optional) receives the binary32 activations before quantisation. */
+static float swiglu_act(const int32_t *acc, int64_t n, const float *weight_scale,
+                        float token_scale, int64_t i) {
+  float g = (float)acc[i] * weight_scale[i];
+  g = g * token_scale;
+  float u = (float)acc[n + i] * weight_scale[n + i];
+  u = u * token_scale;
+  float e = exp_cw(-g);
+  float d = e + 1.0f;
+  float y = g / d;
+  return y * u;
+}
+
+int oracle_swiglu_quant_row(const int32_t *acc, int64_t n, const float *weight_scale,
+                            float token_scale, int8_t *codes, float *inv, float *act_out) {
+  if (!acc || !weight_scale || !codes || !inv || n < 1) return ORACLE_BAD_ARG;
+  float amax = 0.0f;
+  for (int64_t i = 0; i < n; ++i) {
+    float a = swiglu_act(acc, n, weight_scale, token_scale, i);
+    if (act_out) act_out[i] = a;
+    float m = fabsf(a);
+    if (m > amax) amax = m;
+  }
+  float den = amax + 1e-12f;
+  float s = 127.0f / den;
+  for (int64_t i = 0; i < n; ++i) {
+    float a = swiglu_act(acc, n, weight_scale, token_scale, i);
+    float r = nearbyintf(a * s);
+    if (!(r <= 127.0f && r >= -127.0f)) return ORACLE_INTERNAL;
+    codes[i] = (int8_t)(int32_t)r;
+  }
+  inv[0] = 1.0f / s;
+  return ORACLE_OK;
+}
+
+/* All rows: acc [rows][2n], token scale of row m at
+ * token_scale[m * ts_stride] (in floats), codes [rows][n], inv [rows]. */
+int oracle_swiglu_quant(const int32_t *acc, int64_t rows, int64_t n, const float *weight_scale,
+                        const float *token_scale, int64_t ts_stride, int8_t *codes, float *inv) {
+  if (rows < 0 || n < 1 || ts_stride < 1) return ORACLE_BAD_ARG;
+  if (rows == 0) return ORACLE_OK;
+  if (!acc || !weight_scale || !token_scale || !codes || !inv) return ORACLE_BAD_ARG;
+  for (int64_t m = 0; m < rows; ++m) {
+    int rc = oracle_swiglu_quant_row(acc + m * 2 * n, n, weight_scale, token_scale[m * ts_stride],
+                                     codes + m * n, &inv[m], NULL);
+    if (rc) return rc;
   }
   return ORACLE_OK;
 }

@@ -587,3 +587,137 @@ def check_combine_random_rows(orc, seed: int = 5) -> None:
         recv = random_receive_buffer(seed + 1, w.bs * w.topk, 24, kind)
         check_combine_bound(orc, recv, kind, w.topk_idx, w.topk_w, lay["send_token_idx"],
                             no["put_offset"], no["recv_base"], 4, 3)
+
+
+# --------------------------------------------------------------------------
+# expert-side epilogue: dequantise, SwiGLU, requantise
+# --------------------------------------------------------------------------
+
+def ulp32(ref: np.ndarray) -> np.ndarray:
+    """binary32 ulp at |ref| (float64), with the subnormal spacing below 2^-126."""
+    a = np.abs(np.asarray(ref, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return 2.0 ** (e - 23)
+
+
+def exp_probe_values() -> np.ndarray:
+    """A dense grid over the finite range, random bit patterns inside it, and
+    edges: zeros, tiny arguments, the overflow and underflow boundaries, and
+    arguments whose result is subnormal."""
+    grid = np.linspace(-104.0, 89.0, 400001).astype(np.float32)
+    rng = np.random.default_rng(2024)
+    pats = rng.integers(0, 2 ** 32, 400000, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    pats = pats[np.isfinite(pats) & (pats > -104.0) & (pats < 89.0)]
+    edges = np.float32([0.0, -0.0, 1e-30, -1e-30, 2.0 ** -25, -(2.0 ** -25), 0.5, -0.5, 1.0, -1.0,
+                        88.72283, 88.7228, 88.72284, -87.33654, -87.3366, -100.0, -103.27893,
+                        -103.97207, -103.9721, 17.0, 16.0, -17.0, 0.34657359, -0.34657359])
+    return np.concatenate([grid, pats, edges]).astype(np.float32)
+
+
+def check_exp(orc) -> None:
+    """The oracle's binary32 e^x against float64 exp (a library routine):
+    within 1.25 ulp everywhere it is finite and nonzero, subnormal results
+    within one subnormal step, exact at 0, monotone over the grid, +inf
+    above ln(max float) and +0 far below the subnormal range, NaN kept."""
+    x = exp_probe_values()
+    y = orc.exp_f32(x).astype(np.float64)
+    ref = np.exp(x.astype(np.float64))
+    big = ref >= 3.4028235677973366e38  # rounds to +inf in binary32
+    assert np.all(np.isinf(y[big])), "overflow to +inf"
+    fin = ~big
+    err = np.abs(y[fin] - ref[fin]) / ulp32(ref[fin])
+    assert err.max() <= 1.25, f"exp error {err.max():.3f} ulp at x = {x[fin][np.argmax(err)]!r}"
+    assert orc.exp_f32(np.float32([0.0, -0.0])).tolist() == [1.0, 1.0]
+    grid = orc.exp_f32(np.linspace(-104.0, 88.7, 200001).astype(np.float32))
+    assert np.all(np.diff(grid.astype(np.float64)) >= 0), "exp not monotone"
+    far = orc.exp_f32(np.float32([89.5, 100.0, 1e30, -104.5, -200.0, -1e30, np.inf, -np.inf]))
+    assert far[:3].tolist() == [np.inf] * 3 and np.isinf(far[6]) and far[7] == 0.0
+    assert np.all(far[3:6] == 0.0)
+    assert np.isnan(orc.exp_f32(np.float32([np.nan]))[0])
+
+
+def quant_f32_expected(acts: np.ndarray) -> Tuple[np.ndarray, np.float32]:
+    """The dispatch quantiser applied to a binary32 row, in exact rational
+    arithmetic with a binary32 rounding after each operation."""
+    a = np.asarray(acts, dtype=np.float32).astype(np.float64)
+    amax = Fraction(float(np.max(np.abs(a)))) if a.size else Fraction(0)
+    denom = round_f32(amax + frac(np.float32(1e-12)))
+    s = round_f32(Fraction(127) / denom)
+    codes = np.array([round_int_even(round_f32(Fraction(float(v)) * s)) for v in a], dtype=np.int64)
+    inv = round_f32(Fraction(1) / s)
+    return codes.astype(np.int8), np.float32(float(inv))
+
+
+def check_swiglu_golden(orc) -> None:
+    g = load_golden("swiglu_rows.json")
+    for case in g["cases"]:
+        codes, inv, _ = orc.swiglu_quant_row(np.array(case["acc"], np.int32),
+                                             np.array(case["weight_scale"], np.float32),
+                                             case["token_scale"])
+        assert codes.tolist() == case["codes"], case["name"]
+        assert f32_bits(inv) == int(case["inv_hex"], 16), case["name"] + " inverse scale"
+
+
+def swiglu_exact_case(seed: int, n: int):
+    """A row whose dequantisation is exact: |acc| < 2^24 and power-of-two
+    scales, so the gate and up values are known exactly in float64."""
+    rng = np.random.default_rng(seed)
+    acc = rng.integers(-(2 ** 23), 2 ** 23, 2 * n).astype(np.int32)
+    ws = (2.0 ** -rng.integers(18, 24, 2 * n)).astype(np.float32)
+    ts = np.float32(2.0 ** -int(rng.integers(0, 4)))
+    # a few gates pushed to the extremes: exp overflow, exp underflow, near 0
+    k = max(1, n // 16)
+    pos = rng.choice(n, size=3 * k, replace=False)
+    acc[pos[:k]] = -(2 ** 23) + 1
+    ws[pos[:k]] = np.float32(2.0 ** -15)  # gate about -256: e^-g overflows
+    acc[pos[k:2 * k]] = 2 ** 23 - 1
+    ws[pos[k:2 * k]] = np.float32(2.0 ** -15)  # gate about +256: e^-g underflows
+    acc[pos[2 * k:]] = rng.integers(-3, 4, k)
+    g = acc[:n].astype(np.float64) * ws[:n] * float(ts)
+    u = acc[n:].astype(np.float64) * ws[n:] * float(ts)
+    return acc, ws, ts, g, u
+
+
+def check_swiglu_bound(orc, seeds=(1, 2, 3), n: int = 200) -> None:
+    """Activations within 4 binary32 roundings (relative) of the float64
+    g / (1 + e^-g) * u on rows with exact dequantisation (e^x within 1.25 ulp,
+    then add, divide, multiply); codes and inverse scale exactly the
+    quantiser of those activations in rational arithmetic."""
+    for seed in seeds:
+        acc, ws, ts, g, u = swiglu_exact_case(seed, n)
+        codes, inv, act = orc.swiglu_quant_row(acc, ws, ts)
+        with np.errstate(over="ignore"):
+            ref = g / (1.0 + np.exp(-g)) * u
+        tol = 4.5 * 2.0 ** -24 * np.abs(ref) + 2.0 ** -149
+        assert np.all(np.abs(act.astype(np.float64) - ref) <= tol), f"activation bound, seed {seed}"
+        exp_codes, exp_inv = quant_f32_expected(act)
+        assert np.array_equal(codes, exp_codes), f"codes, seed {seed}"
+        assert f32_bits(inv) == f32_bits(exp_inv), f"inverse scale, seed {seed}"
+
+
+def check_swiglu_dequant_exact(orc, seed: int = 9, n: int = 64) -> None:
+    """Rows whose gates are all >= 17 after dequantisation (e^-g below half an
+    ulp of 1, so SwiGLU reduces to g * u exactly), with accumulators beyond
+    2^24 and scales that are not powers of two: every activation must equal
+    fl(fl(fl(fl(acc_g) * ws_g) * ts) * fl(fl(fl(acc_u) * ws_u) * ts)),
+    evaluated in rational arithmetic (int32 -> binary32 rounds half-even)."""
+    rng = np.random.default_rng(seed)
+    for trial in range(4):
+        ws = rng.uniform(0.5, 2.0, 2 * n).astype(np.float32) * np.float32(2.0 ** -22)
+        ts = np.float32(rng.uniform(0.9, 1.1))
+        acc = np.empty(2 * n, np.int64)
+        acc[:n] = rng.integers(2 ** 28, 2 ** 31 - 1, n)  # gate >= 2^28 * 2^-23 * 0.9 > 17
+        acc[n:] = rng.integers(-(2 ** 31), 2 ** 31 - 1, n)
+        acc[n] = 2 ** 24 + 1  # ties in the int32 -> binary32 cast
+        acc[n + 1] = 2 ** 24 + 3
+        acc = acc.astype(np.int32)
+        codes, inv, act = orc.swiglu_quant_row(acc, ws, ts)
+        tsf = frac(ts)
+        for i in range(n):
+            gq = round_f32(round_f32(round_f32(Fraction(int(acc[i]))) * frac(ws[i])) * tsf)
+            assert gq >= 17, "fixture: gate below 17"
+            uq = round_f32(round_f32(round_f32(Fraction(int(acc[n + i]))) * frac(ws[n + i])) * tsf)
+            a = round_f32(gq * uq)
+            assert f32_bits(act[i]) == f32_bits(np.float32(float(a))), (trial, i)
+        exp_codes, exp_inv = quant_f32_expected(act)
+        assert np.array_equal(codes, exp_codes) and f32_bits(inv) == f32_bits(exp_inv), trial

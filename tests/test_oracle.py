@@ -190,3 +190,36 @@ def test_multi_receive_order_lexsort(orc, seed, sizes, k, e, r, routing, bad):
 def test_pipeline_multi_equals_each_single_source(orc, quant, kind):
     xs, idxs, ws = _sources(410, (24, 0, 9, 31), 40, 4, 16, 4, "dup", 0.05, kind)
     pins.check_pipeline_multi_vs_single(orc, xs, kind, idxs, ws, 4, 4, quant)
+
+
+# ---- expert-side epilogue (dequantise, SwiGLU, requantise) ----------------
+
+def test_exp_against_float64(orc):
+    pins.check_exp(orc)
+
+
+def test_swiglu_golden_rows(orc):
+    pins.check_swiglu_golden(orc)
+
+
+def test_swiglu_bound_and_exact_quantiser(orc):
+    pins.check_swiglu_bound(orc, seeds=(1, 2, 3, 4, 5), n=300)
+
+
+def test_swiglu_dequant_rounding_exact(orc):
+    pins.check_swiglu_dequant_exact(orc)
+
+
+def test_swiglu_rows_equal_row_by_row(orc):
+    rng = np.random.default_rng(77)
+    rows, n = 9, 40
+    acc = rng.integers(-(2 ** 31), 2 ** 31 - 1, (rows, 2 * n)).astype(np.int32)
+    ws = rng.uniform(0.5, 2, 2 * n).astype(np.float32) * np.float32(2 ** -26)
+    ts = rng.uniform(0.01, 0.1, rows).astype(np.float32)
+    got = orc.swiglu_quant(acc, ws, ts)
+    for m in range(rows):
+        codes, inv, _ = orc.swiglu_quant_row(acc[m], ws, ts[m])
+        assert np.array_equal(got["codes"][m], codes)
+        assert pins.f32_bits(got["inv"][m]) == pins.f32_bits(inv)
+    empty = orc.swiglu_quant(np.zeros((0, 2 * n), np.int32), ws, np.zeros(0, np.float32))
+    assert empty["codes"].shape == (0, n)

@@ -75,6 +75,38 @@ MUTANTS = {
     "dequant_reassociated": ("v = (float)codes[dst * h + i] * inv[dst];\n        } else {\n          v = to_f32(recv_rows[dst * h + i], recv_kind);\n        }\n        float p = v * w;",
                              "v = (float)codes[dst * h + i];\n          v = v * (inv[dst] * w);\n        } else {\n          v = to_f32(recv_rows[dst * h + i], recv_kind) * w;\n        }\n        float p = v;",
                              "combine_int8_exact"),
+    # epilogue: gate and up halves swapped
+    "swiglu_halves_swapped": (
+        "float g = (float)acc[i] * weight_scale[i];\n  g = g * token_scale;\n  float u = (float)acc[n + i] * weight_scale[n + i];",
+        "float g = (float)acc[n + i] * weight_scale[n + i];\n  g = g * token_scale;\n  float u = (float)acc[i] * weight_scale[i];",
+        "swiglu"),
+    # epilogue: sigmoid instead of x * sigmoid(x)
+    "sigmoid_not_silu": ("float y = g / d;", "float y = 1.0f / d;", "swiglu"),
+    # epilogue: e^g instead of e^-g
+    "exp_sign": ("float e = exp_cw(-g);", "float e = exp_cw(g);", "swiglu"),
+    # epilogue: the +1 of the denominator dropped
+    "no_plus_one": ("float d = e + 1.0f;", "float d = e;", "swiglu"),
+    # epilogue: the token scale not applied to the gate
+    "no_token_scale": ("  g = g * token_scale;", "  (void)0;", "swiglu"),
+    # epilogue: the up half dequantised with the gate column's scale
+    "up_scale_column": ("float u = (float)acc[n + i] * weight_scale[n + i];",
+                        "float u = (float)acc[n + i] * weight_scale[i];", "swiglu"),
+    # epilogue: the two scales multiplied together first
+    "dequant_scales_first": ("float g = (float)acc[i] * weight_scale[i];\n  g = g * token_scale;",
+                             "float g = (float)acc[i] * (weight_scale[i] * token_scale);",
+                             "swiglu_dequant"),
+    # epilogue: the scale stored instead of its inverse
+    "swiglu_store_scale": ("inv[0] = 1.0f / s;", "inv[0] = s;", "swiglu"),
+    # exp: Taylor series cut at degree 6
+    "exp_degree6": ("float p = 1.0f / 5040.0f;\n  p = p * r + 1.0f / 720.0f;",
+                    "float p = 1.0f / 720.0f;", "exp"),
+    # exp: the low part of ln 2 dropped from the reduction
+    "exp_no_c2": ("r = r - kf * c2;", "(void)c2;", "exp"),
+    # exp: k truncated instead of rounded (|r| up to ln 2)
+    "exp_trunc_k": ("float kf = nearbyintf(x * log2e);", "float kf = truncf(x * log2e);", "exp"),
+    # exp: subnormal results flushed to zero
+    "exp_flush_subnormal": ("if (k < -126) return (p * pow2i(k + 64)) * pow2i(-64);",
+                            "if (k < -126) return 0.0f;", "exp"),
     # conversions: bf16 narrowing by truncation
     "bf16_truncate": ("if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;",
                       "(void)lower;", "conversions"),
@@ -158,6 +190,13 @@ def _run_pin(orc, which):
         pins.check_combine_random_rows(orc)
     elif which == "combine_int8_exact":
         _combine_int8_exact(orc)
+    elif which == "swiglu":
+        pins.check_swiglu_golden(orc)
+        pins.check_swiglu_bound(orc)
+    elif which == "swiglu_dequant":
+        pins.check_swiglu_dequant_exact(orc)
+    elif which == "exp":
+        pins.check_exp(orc)
     elif which == "conversions":
         pins.check_conversions(orc)
     else:
