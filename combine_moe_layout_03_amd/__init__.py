@@ -18,7 +18,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional
+from typing import Optional, Tuple
 
 import torch
 
@@ -28,10 +28,12 @@ __all__ = [
     "moe_dispatch", "moe_combine", "moe_status_str", "moe_last_hip_error", "EpBuffers",
     "dtype_code", "moe_fused_supported", "moe_layout_notify_dispatch", "moe_notify_multi",
     "moe_dispatch_src", "moe_combine_src", "EpMultiBuffers", "MOE_MAX_SOURCES",
+    "moe_deq_swiglu_quant", "token_scales_of", "MOE_EPILOGUE_MAX_N",
 ]
 
 MOE_BF16, MOE_FP16, MOE_FP32, MOE_INT8_ROWSCALE = 0, 1, 2, 3
 MOE_MAX_EXPERTS, MOE_MAX_HIDDEN, MOE_MAX_TOPK, MOE_MAX_SOURCES = 2048, 16384, 32, 384
+MOE_EPILOGUE_MAX_N = 4096
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_ep.so")
 
@@ -58,6 +60,7 @@ _SIGS = {
     "moe_fused_supported": ([_I32, _I32, _I32, _I32, _I32, _INT, _INT, ctypes.POINTER(_INT)], _INT),
     "moe_layout_notify_dispatch": ([_P, _INT, _I32, _I32, _I32, _P, _I32, _I32, _INT, _P, _P, _P, _P, _P, _P,
                                     _P, _P, _P, _SZ, _P, _SZ, _P], _INT),
+    "moe_deq_swiglu_quant": ([_P, _I32, _I32, _P, _P, ctypes.c_int64, _P, _SZ, _P], _INT),
     "moe_status_str": ([_INT], ctypes.c_char_p),
     "moe_last_hip_error": ([], _INT),
 }
@@ -285,6 +288,37 @@ def moe_layout_notify_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, expert_n
         _dev(recv_base, "recv_base", i32), _dev(recv_token_per_expert, "recv_token_per_expert", i32),
         _dev(recv_x, "recv_x"), recv_x.numel() * recv_x.element_size(), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_deq_swiglu_quant(acc: torch.Tensor, weight_scale: torch.Tensor, token_scale: torch.Tensor,
+                         out: torch.Tensor, token_scale_stride: int = 4, rows: Optional[int] = None,
+                         stream=None) -> None:
+    """Expert-side epilogue: acc int32 [rows, 2n], weight_scale float32 [2n];
+    the float scale of row m is read at byte m * token_scale_stride of
+    ``token_scale`` (a float32 [rows] tensor with stride 4, or the int8
+    receive buffer at its inverse-scale byte, see ``token_scales_of``); out is
+    a uint8 buffer of at least rows * moe_recv_row_bytes(n, MOE_INT8_ROWSCALE)
+    bytes, written as int8 rows (codes, inverse scale at byte align32(n))."""
+    if acc.dim() != 2 or acc.shape[1] % 2:
+        raise ValueError("acc must be [rows, 2n]")
+    n_rows = acc.shape[0] if rows is None else rows
+    n = acc.shape[1] // 2
+    if weight_scale.numel() != 2 * n:
+        raise ValueError("weight_scale must hold 2n floats")
+    if not token_scale.is_cuda:
+        raise ValueError("token_scale must be a device tensor")
+    _check("moe_deq_swiglu_quant", _lib.moe_deq_swiglu_quant(
+        _dev(acc, "acc", torch.int32), n_rows, n, _dev(weight_scale, "weight_scale", torch.float32),
+        token_scale.data_ptr(), token_scale_stride, _dev(out, "out"), out.numel() * out.element_size(),
+        _stream(stream)))
+
+
+def token_scales_of(recv_x: torch.Tensor, hidden: int) -> Tuple[torch.Tensor, int]:
+    """(base tensor view, byte stride) that addresses the inverse scales of an
+    int8 receive buffer in place, for ``moe_deq_swiglu_quant``."""
+    rb = moe_recv_row_bytes(hidden, MOE_INT8_ROWSCALE)
+    off = (hidden + 31) // 32 * 32
+    return recv_x[off:], rb
 
 
 class EpBuffers:

@@ -355,6 +355,32 @@ int moe_layout_notify_dispatch(const void* x, moe_dtype x_type, int32_t bs, int3
   return hip_status(moe::launch_fused(a, xt, quant_int8 != 0, groups, static_cast<hipStream_t>(stream)));
 }
 
+int moe_deq_swiglu_quant(const int32_t* acc, int32_t rows, int32_t n, const float* weight_scale,
+                         const void* token_scale, int64_t token_scale_stride, void* out, size_t out_bytes,
+                         void* stream) {
+  if (rows < 0 || n < 1 || token_scale_stride < 4 || token_scale_stride % 4 != 0) return MOE_ERR_BAD_SHAPE;
+  if (n % 4 != 0 || n > moe::kEpilogueMaxN) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!acc || !weight_scale || !token_scale || !out) return MOE_ERR_NULL_PTR;
+  if (!aligned(acc, 16) || !aligned(weight_scale, 16) || !aligned(out, 16) || !aligned(token_scale, 4))
+    return MOE_ERR_BAD_ALIGN;
+  size_t rb = 0;
+  int st = row_bytes(n, MOE_INT8_ROWSCALE, &rb);
+  if (st) return st;
+  if (out_bytes / rb < static_cast<size_t>(rows)) return MOE_ERR_BUFFER_TOO_SMALL;
+  moe::EpilogueArgs a{};
+  a.acc = acc;
+  a.weight_scale = weight_scale;
+  a.token_scale = token_scale;
+  a.rows = rows;
+  a.ts_stride = token_scale_stride;
+  a.n = n;
+  a.out = static_cast<uint8_t*>(out);
+  a.out_row_bytes = static_cast<int64_t>(rb);
+  a.scale_off = static_cast<int32_t>(align32(n));
+  return hip_status(moe::launch_deq_swiglu_quant(a, static_cast<hipStream_t>(stream)));
+}
+
 const char* moe_status_str(int status) {
   switch (status) {
     case MOE_OK: return "ok";

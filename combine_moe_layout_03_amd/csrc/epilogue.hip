@@ -1,0 +1,175 @@
+// Expert-side epilogue between dispatch and combine: dequantise the int32
+// output of the first expert GEMM, SwiGLU, requantise to int8
+// ("UMDK/CAM communication acceleration library deep analysis v2", section
+// 4.3, stage 2 DeqSwigluQuant, and section 4.8.1, the GMM1 epilogue
+// PerTokenDequantSwiGLU).
+//
+// Each row is one wave's work (up to n = 1024) or two or four waves' (up to
+// 2048, 4096); lanes own 4-column chunks of the n output columns.  For each
+// column i:
+//   g = (float(acc[i])     * ws[i])     * ts      gate (int32 -> binary32 RNE)
+//   u = (float(acc[n + i]) * ws[n + i]) * ts      up
+//   a = (g / (1 + e^-g)) * u                      Swish(gate) * up
+// each operation rounded on its own (this file is compiled with contraction
+// off, and binary32 division is correctly rounded).  The row's activations
+// stay in registers; the wave reduces their largest magnitude, and the row
+// is quantised exactly as dispatch quantises a token row, into the same
+// int8 row format (codes, then the inverse scale at byte align32(n)).
+//
+// e^x: Cody and Waite's reduction (Software Manual for the Elementary
+// Functions, 1980) with ln 2 = C1 + C2, C1 = 355/512, then the degree-7
+// Taylor polynomial of e^r in Horner form, then the scale by 2^k, all in
+// binary32.  The scale 2^k is applied as (p * 2^k1) * 2^k2 with the first
+// product exact, so the one rounding (into the subnormal range, or the
+// overflow to infinity) happens in the last multiply whatever k is.
+#include "device_util.h"
+#include "launch.h"
+#include "quant.h"
+
+#pragma clang fp contract(off)
+
+namespace moe {
+namespace {
+
+constexpr int kEpiThreads = 256;
+constexpr int kEpiRows = kEpiThreads / kWave;  // rows per workgroup
+
+#define MOE_GLOBAL __attribute__((address_space(1)))
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float pow2(int k) {  // 2^k, -126 <= k <= 127
+  return __uint_as_float(static_cast<uint32_t>(k + 127) << 23);
+}
+
+__device__ __forceinline__ float exp_cw(float x) {
+  const float xc = fminf(fmaxf(x, -104.0f), 89.0f);
+  const float kf = __builtin_rintf(xc * 1.44269502162933349609375f);  // x log2(e)
+  const int k = static_cast<int>(kf);
+  float r = xc - kf * 0.693359375f;     // C1 = 355/512: k * C1 is exact
+  r = r - kf * -2.12194440e-4f;         // C2 = ln 2 - C1
+  float p = 1.0f / 5040.0f;
+  p = p * r + 1.0f / 720.0f;
+  p = p * r + 1.0f / 120.0f;
+  p = p * r + 1.0f / 24.0f;
+  p = p * r + 1.0f / 6.0f;
+  p = p * r + 0.5f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  const int k1 = k > 127 ? 127 : (k < -126 ? k + 64 : k);
+  const int k2 = k > 127 ? 1 : (k < -126 ? -64 : 0);
+  float y = (p * pow2(k1)) * pow2(k2);
+  y = x > 89.0f ? __builtin_inff() : y;
+  y = x < -104.0f ? 0.0f : y;
+  return x != x ? x : y;
+}
+
+__device__ __forceinline__ float swiglu(int32_t cg, int32_t cu, float wg, float wu, float ts) {
+  float g = static_cast<float>(cg) * wg;
+  g = g * ts;
+  float u = static_cast<float>(cu) * wu;
+  u = u * ts;
+  const float e = exp_cw(-g);
+  const float d = e + 1.0f;
+  const float y = g / d;
+  return y * u;
+}
+
+// kW waves per row (a workgroup holds kEpiRows / kW rows); wave part p of a
+// row owns the chunks lane + 64 (i kW + p), i < kIt, so each load
+// instruction of a wave covers 64 consecutive chunks (1 KB of int32).  With
+// kW > 1 the parts combine their largest magnitudes through LDS.
+template <int kIt, int kW>
+__global__ __launch_bounds__(kEpiThreads) void deq_swiglu_quant_kernel(EpilogueArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = uniform(static_cast<int>(threadIdx.x / kWave));
+  const int part = wave % kW;
+  const int64_t m = static_cast<int64_t>(blockIdx.x) * (kEpiRows / kW) + wave / kW;
+  // No early return before the barrier below: a wave past the last row
+  // works on the last row and stores nothing.
+  const bool active = m < a.rows;
+  const int64_t mr = active ? m : a.rows - 1;
+  const int chunks = a.n >> 2;
+  // Global-address-space pointers: plain global loads, waited for by vmcnt alone.
+  const MOE_GLOBAL int32_t* row = (const MOE_GLOBAL int32_t*)(a.acc) + mr * 2 * a.n;
+  const MOE_GLOBAL float* ws = (const MOE_GLOBAL float*)(a.weight_scale);
+  const float ts = *(const MOE_GLOBAL float*)((const MOE_GLOBAL uint8_t*)(a.token_scale) + mr * a.ts_stride);
+
+  // Loads of every chunk first (clamped index past the row's end: the data
+  // is loaded but not used), then the arithmetic.
+  i32x4 cg[kIt], cu[kIt];
+  f32x4 wg[kIt], wu[kIt];
+#pragma unroll
+  for (int i = 0; i < kIt; ++i) {
+    const int c = min(lane + (i * kW + part) * kWave, chunks - 1);
+    cg[i] = *reinterpret_cast<const MOE_GLOBAL i32x4*>(row + 4 * c);
+    cu[i] = *reinterpret_cast<const MOE_GLOBAL i32x4*>(row + a.n + 4 * c);
+    wg[i] = *reinterpret_cast<const MOE_GLOBAL f32x4*>(ws + 4 * c);
+    wu[i] = *reinterpret_cast<const MOE_GLOBAL f32x4*>(ws + a.n + 4 * c);
+  }
+  float act[kIt][4];
+  uint32_t mag = 0;
+#pragma unroll
+  for (int i = 0; i < kIt; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) act[i][q] = swiglu(cg[i][q], cu[i][q], wg[i][q], wu[i][q], ts);
+    if (lane + (i * kW + part) * kWave < chunks) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t b = __float_as_uint(act[i][q]) & 0x7fffffffu;  // |a| orders as an integer
+        mag = mag > b ? mag : b;
+      }
+    }
+  }
+  mag = wave_max_u32(mag);
+  if constexpr (kW > 1) {
+    __shared__ uint32_t part_max[kEpiRows];
+    if (lane == 0) part_max[wave] = mag;
+    __syncthreads();
+    const int first = (wave / kW) * kW;
+#pragma unroll
+    for (int q = 0; q < kW; ++q) mag = mag > part_max[first + q] ? mag : part_max[first + q];
+  }
+  if (!active) return;
+  const float amax = __uint_as_float(mag);
+  const float s = 127.0f / (amax + 1e-12f);
+  const float inv = 1.0f / s;
+  uint8_t* out = a.out + m * a.out_row_bytes;
+#pragma unroll
+  for (int i = 0; i < kIt; ++i) {
+    const int c = lane + (i * kW + part) * kWave;
+    if (c < chunks) {
+      const uint32_t b0 = code_bits(act[i][0], s) & 0xffu;
+      const uint32_t b1 = code_bits(act[i][1], s) & 0xffu;
+      const uint32_t b2 = code_bits(act[i][2], s) & 0xffu;
+      const uint32_t b3 = code_bits(act[i][3], s);
+      reinterpret_cast<uint32_t*>(out)[c] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    }
+  }
+  if (part == 0 && lane == 0) *reinterpret_cast<float*>(out + a.scale_off) = inv;
+}
+
+template <int kIt, int kW>
+hipError_t launch_shape(const EpilogueArgs& a, hipStream_t stream) {
+  constexpr int rows_per_group = kEpiRows / kW;
+  const dim3 grid(static_cast<unsigned>((a.rows + rows_per_group - 1) / rows_per_group));
+  hipLaunchKernelGGL((deq_swiglu_quant_kernel<kIt, kW>), grid, dim3(kEpiThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Up to 1024 columns one wave per row with 1, 2 or 4 chunks per lane; up to
+// 2048 two waves and up to 4096 four waves per row, 4 chunks per lane.
+hipError_t launch_deq_swiglu_quant(const EpilogueArgs& a, hipStream_t stream) {
+  if (a.rows == 0) return hipSuccess;
+  const int chunks = a.n / 4;
+  if (chunks <= 64) return launch_shape<1, 1>(a, stream);
+  if (chunks <= 128) return launch_shape<2, 1>(a, stream);
+  if (chunks <= 256) return launch_shape<4, 1>(a, stream);
+  if (chunks <= 512) return launch_shape<4, 2>(a, stream);
+  if (chunks <= 1024) return launch_shape<4, 4>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -104,6 +104,21 @@ struct FusedArgs {
   int32_t scale_off;
 };
 
+// ---- expert-side epilogue: dequantise, SwiGLU, requantise ------------------------
+struct EpilogueArgs {
+  const int32_t* acc;          // [rows][2n]: gate columns 0..n-1, up columns n..2n-1
+  const float* weight_scale;   // [2n]
+  const void* token_scale;     // float of row m at byte m * ts_stride
+  int64_t rows, ts_stride;
+  int32_t n;
+  uint8_t* out;                // int8 rows: codes [0, n), inverse scale at scale_off
+  int64_t out_row_bytes;
+  int32_t scale_off;
+};
+constexpr int kEpilogueMaxN = MOE_EPILOGUE_MAX_N;
+
+hipError_t launch_deq_swiglu_quant(const EpilogueArgs& a, hipStream_t stream);
+
 size_t fused_lds_bytes(int32_t num_experts, int32_t tokens_per_group, int32_t topk, int32_t copies);
 hipError_t launch_fused(const FusedArgs& a, Half x_type, bool quant, int groups, hipStream_t stream);
 

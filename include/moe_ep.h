@@ -73,6 +73,7 @@ enum {
 #define MOE_MAX_TOPK 32        /* k */
 #define MOE_MAX_SOURCES 384    /* source ranks sharing one receive buffer (the
                                   page's CAM_MAX_RANK_SIZE) */
+#define MOE_EPILOGUE_MAX_N 4096 /* n, the epilogue's output columns (2n inputs) */
 
 /* Bytes of one receive-buffer row for hidden size `hidden` and receive type
  * `recv` (page 2.5 and 2.2.1):
@@ -242,6 +243,41 @@ int moe_layout_notify_dispatch(const void* x, moe_dtype xType, int32_t bs, int32
                                void* workspace, size_t workspaceBytes, void* stream);
 
 /* Text for a status code (static storage). */
+/* Expert-side epilogue between dispatch and combine: dequantise the int32
+ * output of the first expert GEMM, SwiGLU, and requantise to int8 -- page
+ * section 4.3 (Fused Deep MoE, stage 2 "DeqSwigluQuant") and section 4.8.1
+ * (the GMM1 epilogue PerTokenDequantSwiGLU).
+ *
+ * acc        [rows][2n] int32, device, 16-byte aligned: row m is the GEMM
+ *            output of receive row m, gate columns 0 .. n-1 then up columns
+ *            n .. 2n-1.
+ * weightScale [2n] float, device, 16-byte aligned: per-column dequant scale.
+ * tokenScale  device bytes, 4-byte aligned: the float scale of row m is at
+ *            byte offset m * tokenScaleStride (a multiple of 4, >= 4).  A dense
+ *            float array has stride 4; the int8 receive buffer's inverse
+ *            scales are used in place with tokenScale = recvX + align32(h)
+ *            and tokenScaleStride = moe_recv_row_bytes(h, MOE_INT8_ROWSCALE).
+ * out        device, 16-byte aligned, outBytes >= rows * moe_recv_row_bytes(n,
+ *            MOE_INT8_ROWSCALE): int8 rows in the receive-buffer format.
+ *
+ * For every row m and column i, each operation rounded to binary32:
+ *   g = (float(acc[m][i]) * weightScale[i]) * ts_m            (int32 -> float
+ *   u = (float(acc[m][n+i]) * weightScale[n+i]) * ts_m         rounds half-even)
+ *   a_i = (g / (1 + e^-g)) * u                                 (Swish(g) * u)
+ * then the row a is quantised like a dispatched row: s = 127 / (max|a| +
+ * 1e-12f), codes rint(a_i * s) (half-even) at bytes [0, n), inv = 1/s as a
+ * float at byte align32(n).  e^x is binary32 Cody-Waite reduction with
+ * ln 2 = 355/512 + (ln 2 - 355/512) and the degree-7 Taylor polynomial,
+ * +inf above 89, +0 below -104.  Activations must be finite (scales and
+ * accumulators that overflow binary32 are outside the contract).
+ *
+ * Requires rows >= 0 and n >= 1 (else MOE_ERR_BAD_SHAPE), n % 4 == 0 and
+ * n <= MOE_EPILOGUE_MAX_N (else MOE_ERR_UNSUPPORTED).  rows == 0 enqueues
+ * nothing. */
+int moe_deq_swiglu_quant(const int32_t* acc, int32_t rows, int32_t n, const float* weightScale,
+                         const void* tokenScale, int64_t tokenScaleStride, void* out, size_t outBytes,
+                         void* stream);
+
 const char* moe_status_str(int status);
 
 /* The hipError_t value of the last MOE_ERR_HIP returned on this thread

@@ -35,7 +35,8 @@ def test_header_symbols_exported(M):
 
 def test_header_constants_match_binding(M):
     text = open(HEADER).read()
-    for name in ("MOE_MAX_EXPERTS", "MOE_MAX_HIDDEN", "MOE_MAX_TOPK", "MOE_MAX_SOURCES"):
+    for name in ("MOE_MAX_EXPERTS", "MOE_MAX_HIDDEN", "MOE_MAX_TOPK", "MOE_MAX_SOURCES",
+                 "MOE_EPILOGUE_MAX_N"):
         val = int(re.search(rf"#define {name} (\d+)", text).group(1))
         assert getattr(M, name) == val
 
@@ -248,3 +249,23 @@ def test_rank_division_by_multiply_high_is_exact():
     for d in range(1, 2049):
         m = np.uint64(((1 << 32) + d - 1) // d)
         assert np.array_equal((e * m) >> np.uint64(32), e // np.uint64(d)), d
+
+
+def test_epilogue_rejects_on_host(M):
+    L = M._lib
+    rb = 2048 + 32  # moe_recv_row_bytes(2048, int8)
+    ok = dict(rows=16, n=2048, stride=4, out_bytes=16 * rb)
+
+    def call(acc=P, rows=ok["rows"], n=ok["n"], ws=P, ts=P, stride=ok["stride"], out=P,
+             out_bytes=ok["out_bytes"]):
+        return L.moe_deq_swiglu_quant(acc, rows, n, ws, ts, stride, out, out_bytes, None)
+
+    assert call(rows=-1) == 2
+    assert call(n=0) == 2
+    assert call(stride=2) == 2 and call(stride=6) == 2 and call(stride=0) == 2
+    assert call(n=6) == 7                       # n % 4
+    assert call(n=4100) == 7                    # above MOE_EPILOGUE_MAX_N
+    assert call(rows=0, acc=None, ws=None, ts=None, out=None) == 0  # nothing to do
+    assert call(acc=None) == 1 and call(ws=None) == 1 and call(ts=None) == 1 and call(out=None) == 1
+    assert call(acc=P + 4) == 3 and call(ws=P + 8) == 3 and call(out=P + 4) == 3 and call(ts=P + 2) == 3
+    assert call(out_bytes=16 * rb - 1) == 6
