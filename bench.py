@@ -17,6 +17,11 @@ of layout+notify+dispatch+combine over the K steps and ``value`` is bs divided
 by it (tokens/s, whole pipeline).  The un-flushed back-to-back rate, a plain
 device copy and the CPU oracle are reported beside it, labelled.
 
+``--stage epilogue`` times the expert-side epilogue kernel (dequantise the
+first expert GEMM's int32 output, SwiGLU, requantise to int8 rows) alone, on
+every receive row of the large shape with an FFN width of 2048, and prints
+its own JSON line (rows/s).
+
 Output: one JSON line on stdout.  ``--gpus N`` with N > 1 exits: this build
 measures one GPU.
 """
@@ -43,7 +48,9 @@ KERNEL_SOURCES = {
     "dispatch": os.path.join(ROOT, "combine_moe_layout_03_amd", "csrc", "dispatch.hip"),
     "combine": os.path.join(ROOT, "combine_moe_layout_03_amd", "csrc", "combine.hip"),
     "fused": os.path.join(ROOT, "combine_moe_layout_03_amd", "csrc", "fused.hip"),
+    "epilogue": os.path.join(ROOT, "combine_moe_layout_03_amd", "csrc", "epilogue.hip"),
 }
+EPILOGUE_METRIC = "expert epilogue (dequant + SwiGLU + int8 requant) rows/s and HBM GB/s (% of peak)"
 
 
 def log(msg: str) -> None:
@@ -107,6 +114,13 @@ def algorithmic_bytes(bs: int, h: int, k: int, quant: bool, out_bytes: int = 2):
     combine = bs * k * row + bs * k * 12 + bs * h * out_bytes
     layout = bs * k * 8
     return dispatch, combine, layout
+
+
+def epilogue_bytes(rows: int, n: int) -> int:
+    """Bytes the epilogue must move: each row reads 2n int32 accumulators and
+    its float token scale and writes n int8 codes and a float inverse scale;
+    the 2n float weight scales are read once per launch."""
+    return rows * (8 * n + 4 + n + 4) + 8 * n
 
 
 def source_hash(path: str) -> str:
@@ -174,6 +188,9 @@ def main(argv=None) -> int:
     ap.add_argument("--sources", type=int, default=1,
                     help="split the workload's tokens into this many source ranks sharing one receive "
                          "buffer (multi-source notify, per-source dispatch and combine)")
+    ap.add_argument("--stage", default="pipeline", choices=["pipeline", "epilogue"],
+                    help="pipeline: layout + notify + dispatch + combine (the headline); epilogue: the "
+                         "expert-side dequant + SwiGLU + int8 requant kernel on its own")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, then WRITE_SIZE) of a bench "
                          "run into profiles/traffic_*.json and exit")
@@ -197,6 +214,8 @@ def main(argv=None) -> int:
         return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.stage == "epilogue":
+        return bench_epilogue(args, M, torch, W, dev)
     quant = args.mode == "int8"
 
     log(f"generating workload {args.workload}")
@@ -370,6 +389,101 @@ def main(argv=None) -> int:
     return 0
 
 
+def bench_epilogue(args, M, torch, W, dev) -> int:
+    """The expert-side epilogue kernel alone on every receive row of the large
+    shape (4096 tokens x top-8 = 32768 rows) with an FFN width of n = 2048:
+    int32 [rows, 2n] in, int8 rows out.  The caches are flushed before each
+    timed launch."""
+    c = W.EPILOGUE_CONFIG
+    log(f"generating epilogue inputs rows={c['rows']} n={c['n']}")
+    case = W.epilogue_case(c["seed"], c["rows"], c["n"])
+    acc = torch.from_numpy(case.acc).to(dev)
+    ws = torch.from_numpy(case.weight_scale).to(dev)
+    ts = torch.from_numpy(case.token_scale).to(dev)
+    rb = M.moe_recv_row_bytes(case.n, M.MOE_INT8_ROWSCALE)
+    out = torch.zeros(case.rows * rb, dtype=torch.uint8, device=dev)
+    flush = torch.ones(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    flush_out = torch.zeros((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    log(f"warm-up x{args.warmup}")
+    for _ in range(args.warmup):
+        torch.sum(flush, dim=0, out=flush_out)
+        M.moe_deq_swiglu_quant(acc, ws, ts, out)
+    torch.cuda.synchronize()
+    log(f"timed x{args.steps}")
+    hev = HipEvents(args.event_flags)
+    ev = [(hev.new(), hev.new()) for _ in range(args.steps)]
+    for e0, e1 in ev:
+        torch.sum(flush, dim=0, out=flush_out)
+        hev.record(e0, stream)
+        M.moe_deq_swiglu_quant(acc, ws, ts, out)
+        hev.record(e1, stream)
+    torch.cuda.synchronize()
+    us = [hev.ms(e0, e1) * 1e3 for e0, e1 in ev]
+    log("copy ceiling")
+    dst = torch.empty_like(flush)
+    for _ in range(2):
+        torch.neg(flush, out=dst)
+    c0, c1 = hev.new(), hev.new()
+    hev.record(c0, stream)
+    for _ in range(10):
+        torch.neg(flush, out=dst)
+    hev.record(c1, stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * flush.numel() * 4 * 10 / (hev.ms(c0, c1) * 1e-3) / 1e9
+    del dst
+    hev.close()
+    mean_us = statistics.mean(us)
+    alg = epilogue_bytes(case.rows, case.n)
+    achieved = alg / (mean_us * 1e-6) / 1e9
+    cpu = None
+    if args.cpu_budget > 0:
+        import oracle
+
+        log(f"cpu baseline (oracle, ~{args.cpu_budget:.0f} s)")
+        oracle.default()
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            oracle.swiglu_quant(case.acc, case.weight_scale, case.token_scale)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_budget or passes >= 50:
+                break
+        cpu = dict(value=case.rows * passes / el, unit="rows/s", cores=1, kind="oracle",
+                   sample=f"all {case.rows} rows x n={case.n}, {passes} pass(es) in {el:.1f} s on one host thread",
+                   host_cpu=platform.processor() or platform.machine(), host_nproc=os.cpu_count())
+    line = {
+        "metric": EPILOGUE_METRIC,
+        "value": case.rows / (mean_us * 1e-6),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": mean_us * 1e-3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "payload": "int32 GEMM accumulators in, int8 codes + fp32 inverse scale per row out",
+        "data": "synthetic",
+        "config": {"workload": "epilogue", "rows": case.rows, "n": case.n,
+                   "rows_from": "4096 tokens x top-8 receive rows of the large shape",
+                   "parallelism": "1 GPU"},
+        "step": "one moe_deq_swiglu_quant launch, caches flushed before it",
+        "timer": f"HIP events on the kernel's stream ({args.event_flags})",
+        "stages_us": {"epilogue": {"mean": mean_us, "p10": pct(us, 0.1), "p50": pct(us, 0.5),
+                                   "p90": pct(us, 0.9)}},
+        "algorithmic_bytes": {"epilogue": alg},
+        "roofline": {"bound": "hbm", "kernel": "deq_swiglu_quant", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": load_traffic("epilogue", "epilogue", f"n{case.n}")},
+        "copy_ceiling_gbps": copy_gbps,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def bench_sources(args, M, torch, w, x, idx, wts, quant: bool, do_flush, stream) -> int:
     """The workload's tokens split evenly into ``--sources`` source ranks
     sharing one receive buffer: a step is every source's layout, one notify
@@ -517,16 +631,24 @@ def ingest_pmc(args, fetch_csv: str, write_csv: str) -> int:
     w = None
     import workloads as W
 
-    c = W.CONFIGS[args.workload]
-    b_dis, b_com, b_lay = algorithmic_bytes(c["bs"], c["hidden"], c["topk"], quant)
-    for kernel, alg in (("dispatch", b_dis), ("combine", b_com), ("fused", b_dis + b_lay)):
-        kname, f = pick(fetch, f"{kernel}_kernel", required=False)
-        _, wr = pick(write, f"{kernel}_kernel", required=False)
+    if args.stage == "epilogue":
+        ce = W.EPILOGUE_CONFIG
+        workload, mode = "epilogue", f"n{ce['n']}"
+        kernels = (("epilogue", "deq_swiglu_quant_kernel", epilogue_bytes(ce["rows"], ce["n"])),)
+    else:
+        c = W.CONFIGS[args.workload]
+        workload, mode = args.workload, args.mode
+        b_dis, b_com, b_lay = algorithmic_bytes(c["bs"], c["hidden"], c["topk"], quant)
+        kernels = (("dispatch", "dispatch_kernel", b_dis), ("combine", "combine_kernel", b_com),
+                   ("fused", "fused_kernel", b_dis + b_lay))
+    for kernel, symbol, alg in kernels:
+        kname, f = pick(fetch, symbol, required=False)
+        _, wr = pick(write, symbol, required=False)
         if f is None or wr is None:
             continue  # not launched in this run
         traffic = f * 1024.0 * f_scale + wr * 1024.0 * w_scale
         rec = {
-            "kernel": kname, "workload": args.workload, "mode": args.mode,
+            "kernel": kname, "workload": workload, "mode": mode,
             "fetch_kib_per_dispatch": f, "write_kib_per_dispatch": wr,
             "copy_calibration": {"bytes_each_way": copy_bytes, "fetch_kib": f_copy, "write_kib": w_copy,
                                  "fetch_scale": f_scale, "write_scale": w_scale},
@@ -535,7 +657,7 @@ def ingest_pmc(args, fetch_csv: str, write_csv: str) -> int:
             "source_sha256_16": source_hash(KERNEL_SOURCES[kernel]),
             "counters_from": [os.path.basename(fetch_csv), os.path.basename(write_csv)],
         }
-        path = os.path.join(PROFILES, f"traffic_{kernel}_{args.workload}_{args.mode}.json")
+        path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}_{mode}.json")
         with open(path, "w") as fh:
             json.dump(rec, fh, indent=1)
         print(path, json.dumps(rec))

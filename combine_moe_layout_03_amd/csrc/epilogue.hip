@@ -19,9 +19,7 @@
 // e^x: Cody and Waite's reduction (Software Manual for the Elementary
 // Functions, 1980) with ln 2 = C1 + C2, C1 = 355/512, then the degree-7
 // Taylor polynomial of e^r in Horner form, then the scale by 2^k, all in
-// binary32.  The scale 2^k is applied as (p * 2^k1) * 2^k2 with the first
-// product exact, so the one rounding (into the subnormal range, or the
-// overflow to infinity) happens in the last multiply whatever k is.
+// binary32.
 #include "device_util.h"
 #include "launch.h"
 #include "quant.h"
@@ -38,14 +36,17 @@ constexpr int kEpiRows = kEpiThreads / kWave;  // rows per workgroup
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float pow2(int k) {  // 2^k, -126 <= k <= 127
-  return __uint_as_float(static_cast<uint32_t>(k + 127) << 23);
-}
-
+// Arguments are clamped to [-104, 89] first; the method itself then gives
+// +inf at 89 (k = 128 and p > 1) and +0 at -104 (p 2^-150 is below half the
+// smallest subnormal), which are the results for every argument beyond.
+// p * 2^k is one v_ldexp_f32: exact for a normal result, rounded once for a
+// subnormal one or overflowing to +inf, as the two-multiply form
+// (p * 2^(k+64)) * 2^-64 or (p * 2^127) * 2 would be.  (A subnormal e^-g never
+// changes the activation anyway: 1 + e^-g rounds to 1 for e^-g < 2^-24.)
+// Arguments must not be NaN (finite scales and accumulators give none).
 __device__ __forceinline__ float exp_cw(float x) {
-  const float xc = fminf(fmaxf(x, -104.0f), 89.0f);
+  const float xc = __builtin_amdgcn_fmed3f(x, -104.0f, 89.0f);
   const float kf = __builtin_rintf(xc * 1.44269502162933349609375f);  // x log2(e)
-  const int k = static_cast<int>(kf);
   float r = xc - kf * 0.693359375f;     // C1 = 355/512: k * C1 is exact
   r = r - kf * -2.12194440e-4f;         // C2 = ln 2 - C1
   float p = 1.0f / 5040.0f;
@@ -56,12 +57,7 @@ __device__ __forceinline__ float exp_cw(float x) {
   p = p * r + 0.5f;
   p = p * r + 1.0f;
   p = p * r + 1.0f;
-  const int k1 = k > 127 ? 127 : (k < -126 ? k + 64 : k);
-  const int k2 = k > 127 ? 1 : (k < -126 ? -64 : 0);
-  float y = (p * pow2(k1)) * pow2(k2);
-  y = x > 89.0f ? __builtin_inff() : y;
-  y = x < -104.0f ? 0.0f : y;
-  return x != x ? x : y;
+  return __builtin_amdgcn_ldexpf(p, static_cast<int>(kf));
 }
 
 __device__ __forceinline__ float swiglu(int32_t cg, int32_t cu, float wg, float wu, float ts) {
