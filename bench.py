@@ -14,8 +14,9 @@ expert GEMMs).  HIP events recorded on the stream the kernels run on (created wi
 system-scope fence, which only serves host visibility) time each stage;
 flushes are outside the timed intervals.  ``ms_per_step`` is the mean
 of layout+notify+dispatch+combine over the K steps and ``value`` is bs divided
-by it (tokens/s, whole pipeline).  The un-flushed back-to-back rate, a plain
-device copy and the CPU oracle are reported beside it, labelled.
+by it (tokens/s, whole pipeline).  The un-flushed back-to-back rate (eager,
+and replayed from one captured HIP graph), a plain device copy and the CPU
+oracle are reported beside it, labelled.
 
 ``--stage epilogue`` times the expert-side epilogue kernel (dequantise the
 first expert GEMM's int32 output, SwiGLU, requantise to int8 rows) alone, on
@@ -42,6 +43,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
+GRAPH_STEPS = 10  # steps captured into one HIP graph for the graph-replay figure
 METRIC = "dispatch+combine tokens/s and HBM GB/s (% of peak) at bs=4096 h=7168 top-8"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
@@ -302,6 +304,33 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     unflushed_ms = hev.ms(e0, e1) / args.steps
 
+    # the same back-to-back steps replayed from one captured HIP graph of
+    # GRAPH_STEPS steps (the library only enqueues kernels, so steps
+    # capture); this removes the host launch overhead that dominates the
+    # small workloads (one graph launch itself costs tens of microseconds
+    # here, hence several steps per graph)
+    log("graph replay, un-flushed back-to-back")
+    graph_ms = None
+    try:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(GRAPH_STEPS):
+                buf.run(x, idx, wts, fused=fused)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // GRAPH_STEPS)
+        g0, g1 = hev.new(), hev.new()
+        hev.record(g0, stream)
+        for _ in range(reps):
+            graph.replay()
+        hev.record(g1, stream)
+        torch.cuda.synchronize()
+        graph_ms = hev.ms(g0, g1) / (reps * GRAPH_STEPS)
+        del graph
+    except RuntimeError as exc:  # an auxiliary figure: report it as missing, say why
+        log(f"graph capture failed, graph_unflushed_ms_per_step is null: {exc}")
+
     # plain device copy of 1 GiB (read + write) as the practical ceiling
     log("copy ceiling")
     src = flush
@@ -381,6 +410,7 @@ def main(argv=None) -> int:
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
         "unflushed_ms_per_step": unflushed_ms,
         "unflushed_tokens_per_s": w.bs / (unflushed_ms * 1e-3),
+        "graph_unflushed_ms_per_step": graph_ms,
         "copy_ceiling_gbps": copy_gbps,
         "wall_ms_per_step_incl_flush": wall / args.steps * 1e3,
         "cpu_baseline": cpu,
