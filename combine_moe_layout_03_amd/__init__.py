@@ -412,8 +412,10 @@ class EpMultiBuffers:
         self.token_per_rank = torch.zeros((self.num_src, rank_size), **i32)
         self.send_token_idx = [torch.zeros((b, topk), **i32) for b in sizes]
         self.bad_id_count = torch.zeros(self.num_src, **i32)
-        ws = max(moe_layout_workspace_bytes(b, topk, e) for b in sizes)
-        self.workspace = torch.zeros(max(ws, 4) // 4, **i32)
+        # one layout workspace per source, so the sources' layouts may run
+        # concurrently on different streams
+        self.workspace = [torch.zeros(max(moe_layout_workspace_bytes(b, topk, e), 4) // 4, **i32)
+                          for b in sizes]
         self.put_offset = torch.zeros((e, self.num_src), **i32)
         self.recv_count = torch.zeros(rank_size, **i32)
         self.recv_base = torch.zeros(rank_size, **i32)
@@ -424,7 +426,7 @@ class EpMultiBuffers:
 
     def layout(self, src: int, topk_idx, stream=None):
         moe_layout(topk_idx, self.epr, self.ranks, self.token_per_expert[src], self.token_per_rank[src],
-                   self.send_token_idx[src], self.bad_id_count[src:src + 1], self.workspace, stream)
+                   self.send_token_idx[src], self.bad_id_count[src:src + 1], self.workspace[src], stream)
 
     def notify(self, stream=None):
         moe_notify_multi(self.token_per_expert, self.epr, self.ranks, self.put_offset, self.recv_count,

@@ -36,10 +36,19 @@ def _run_gpu(cases, h, k, e, r, kind, quant, streams=None):
     if streams is None:
         buf.run(xs, idxs, ws)
     else:
-        # layouts and notify on the current stream; each source's dispatch and
-        # combine on its own stream (sources write disjoint rows)
+        # each source's layout, dispatch and combine on its own stream (each
+        # source has its own layout workspace and outputs, and sources write
+        # disjoint receive rows); the notify over all sources' counts on the
+        # current stream after the layouts have joined
+        ev0 = torch.cuda.Event()
+        ev0.record()
         for s in range(len(cases)):
-            buf.layout(s, idxs[s])
+            st = streams[s % len(streams)]
+            st.wait_event(ev0)
+            with torch.cuda.stream(st):
+                buf.layout(s, idxs[s])
+        for st in streams:
+            torch.cuda.current_stream().wait_stream(st)
         buf.notify()
         ev = torch.cuda.Event()
         ev.record()
@@ -120,8 +129,8 @@ def test_multi_source_large_shape_split_over_16_sources():
 
 def test_multi_source_on_separate_streams():
     cases = _sources(530, (200, 150, 90, 40), 512, 8, 64, 8, "dup", 0.01, "bf16")
-    log("multi-source, dispatch and combine on two streams")
-    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    log("multi-source, layout, dispatch and combine on three streams")
+    streams = [torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()]
     buf = _run_gpu(cases, 512, 8, 64, 8, "bf16", True, streams=streams)
     _compare(buf, cases, 512, 64, 8, "bf16", True)
 
