@@ -15,8 +15,10 @@ system-scope fence, which only serves host visibility) time each stage;
 flushes are outside the timed intervals.  ``ms_per_step`` is the mean
 of layout+notify+dispatch+combine over the K steps and ``value`` is bs divided
 by it (tokens/s, whole pipeline).  The un-flushed back-to-back rate (eager,
-and replayed from one captured HIP graph), a plain device copy and the CPU
-oracle are reported beside it, labelled.
+and replayed from one captured HIP graph), the dispatch and combine kernels
+timed on their own (``dispatch_combine_kernels_alone``: dispatch + combine
+without the layout work the fused launch carries), a plain device copy and
+the CPU oracle are reported beside it, labelled.
 
 ``--stage epilogue`` times the expert-side epilogue kernel (dequantise the
 first expert GEMM's int32 output, SwiGLU, requantise to int8 rows) alone, on
@@ -190,6 +192,8 @@ def main(argv=None) -> int:
     ap.add_argument("--sources", type=int, default=1,
                     help="split the workload's tokens into this many source ranks sharing one receive "
                          "buffer (multi-source notify, per-source dispatch and combine)")
+    ap.add_argument("--skip-kernels-only", action="store_true",
+                    help="with the fused path, do not also time the dispatch and combine kernels alone")
     ap.add_argument("--stage", default="pipeline", choices=["pipeline", "epilogue"],
                     help="pipeline: layout + notify + dispatch + combine (the headline); epilogue: the "
                          "expert-side dequant + SwiGLU + int8 requant kernel on its own")
@@ -331,6 +335,36 @@ def main(argv=None) -> int:
     except RuntimeError as exc:  # an auxiliary figure: report it as missing, say why
         log(f"graph capture failed, graph_unflushed_ms_per_step is null: {exc}")
 
+    # with the fused path, the dispatch and combine kernels on their own as
+    # well (the layout and notify outputs are in place from the steps
+    # above), each after a flush: dispatch + combine without the layout work
+    # that the fused launch carries
+    kernels_only = None
+    if fused and not args.skip_kernels_only:
+        log(f"dispatch and combine kernels alone x{args.steps}")
+        for _ in range(max(1, args.warmup)):  # the first launch of a kernel also loads it
+            do_flush()
+            buf.dispatch(x, idx)
+            buf.combine(idx, wts)
+        torch.cuda.synchronize()
+        kev = [[hev.new() for _ in range(4)] for _ in range(args.steps)]
+        for e in kev:
+            do_flush()
+            hev.record(e[0], stream)
+            buf.dispatch(x, idx)
+            hev.record(e[1], stream)
+            do_flush()
+            hev.record(e[2], stream)
+            buf.combine(idx, wts)
+            hev.record(e[3], stream)
+        torch.cuda.synchronize()
+        kd = statistics.mean(hev.ms(e[0], e[1]) for e in kev) * 1e3
+        kc = statistics.mean(hev.ms(e[2], e[3]) for e in kev) * 1e3
+        bd, bc, _ = algorithmic_bytes(w.bs, w.hidden, w.topk, quant)
+        gbps = (bd + bc) / ((kd + kc) * 1e-6) / 1e9
+        kernels_only = {"dispatch_us": kd, "combine_us": kc, "tokens_per_s": w.bs / ((kd + kc) * 1e-6),
+                        "hbm_gbps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS}
+
     # plain device copy of 1 GiB (read + write) as the practical ceiling
     log("copy ceiling")
     src = flush
@@ -411,6 +445,7 @@ def main(argv=None) -> int:
         "unflushed_ms_per_step": unflushed_ms,
         "unflushed_tokens_per_s": w.bs / (unflushed_ms * 1e-3),
         "graph_unflushed_ms_per_step": graph_ms,
+        "dispatch_combine_kernels_alone": kernels_only,
         "copy_ceiling_gbps": copy_gbps,
         "wall_ms_per_step_incl_flush": wall / args.steps * 1e3,
         "cpu_baseline": cpu,
