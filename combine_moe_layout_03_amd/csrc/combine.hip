@@ -1,19 +1,27 @@
 // Stage 4, combine ("UMDK/CAM communication acceleration library deep
 // analysis v2", section 2.6, moe_combine_normal_zb::ReadBufferAndWeightedSum).
 //
-// kWpt waves per token, each owning every kWpt-th group of 64 chunks of the
-// row.  Each wave first resolves the receive row, weight and (int8) inverse
-// scale of each of the token's k entries into scalar registers.  Then each
-// lane walks chunks of kElems elements, software-pipelined: the k row loads
-// of the next chunk are issued before the current chunk is summed, so loads
-// and arithmetic overlap inside every wave.  The loaded values are folded into binary32
-// accumulators in entry order j = 0..k-1, exactly as the page does:
+// Every output element is the page's sum in entry order j = 0..k-1:
 //   acc = +0; acc = acc + v_j * w_j  (v_j = float(row) or float(q) * inv)
 // with every multiply and add rounded separately (this file is compiled with
 // floating-point contraction off), so the result is bit-identical to the
 // sequential binary32 definition.  The sum is rounded half-even to the
 // output type (bf16: the hardware v_cvt_pk_bf16_f32 pair conversion) and
-// stored with 16-byte stores.
+// stored with 16-byte stores.  Two kernels, four waves per token in both:
+//
+// combine_rows_kernel (int8 rows, k <= 8): wave p owns, in every row, the
+// chunks (8 codes each) lane + 64 (p kC + i), i < kC, and reads the token's
+// rows one after another in entry order -- the order it adds in -- with the
+// loads of row j + 2 in flight while row j is added into accumulators held
+// in registers.  Each wave's share of a row is kC contiguous 512-byte
+// pieces.  At h = 7168, k = 8 this measured 2-4 us faster than reading a
+// slice of all k rows at once.
+//
+// combine_kernel (16-bit rows, and int8 rows with k > 8): each wave owns
+// every fourth group of 64 chunks and walks its chunks, software-pipelined:
+// the k row loads of the next chunk are issued before the current chunk is
+// summed.  For 16-bit rows this was the faster of the two (95 against
+// 107 us for bf16 rows at h = 7168, k = 8).
 #include "device_util.h"
 #include "launch.h"
 
@@ -235,12 +243,121 @@ hipError_t launch_shape(const RouteArgs& a, const uint8_t* recv, const float* w,
   return hipGetLastError();
 }
 
+// int8 rows, k <= kMaxK: the token's rows one at a time (see the file
+// header).  Lane j resolves entry j; lanes j >= k take entry k - 1's row (so
+// the loads of rows past k re-read a row this wave has just read, from L2)
+// but are never added.  Rows are read with no branches around the loads:
+// skipping the rows past k with a branch measured 1.4 us slower.
+template <Out kOut, int kC, int kMaxK>
+__global__ __launch_bounds__(kCombineThreads) void combine_rows_kernel(RouteArgs a,
+                                                                       const uint8_t* __restrict__ recv,
+                                                                       const float* __restrict__ topk_w,
+                                                                       void* __restrict__ out) {
+  constexpr Recv kRecv = Recv::kInt8;
+  constexpr int kElems = 8;
+  constexpr int kD = 2;  // rows in flight ahead of the one being added
+  using C = Chunk<kRecv, kElems>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int part = uniform(static_cast<int>(threadIdx.x / kWave));
+  const int t = blockIdx.x;
+  if (t >= a.bs) return;
+  const gbytes base = (gbytes)(recv);
+
+  const int k = a.k;
+  const int i_e = t * k + min(lane, k - 1);
+  const int e = a.topk_idx[i_e];
+  const int slot = a.send_token_idx[i_e];
+  const float my_w = topk_w[i_e];
+  const int ec = min(max(e, 0), a.num_experts - 1);
+  const int rank = static_cast<int>((static_cast<uint64_t>(ec) * a.epr_magic) >> 32);
+  const int64_t row = static_cast<int64_t>(a.recv_base[rank]) + a.put_offset[ec * a.put_stride] + slot;
+  const bool ok = static_cast<unsigned>(e) < static_cast<unsigned>(a.num_experts) && slot >= 0 && row >= 0 &&
+                  row < a.cap_rows;
+  const int64_t my_off = ok ? row * a.row_bytes : 0;  // not dispatched: row 0, read but not added
+  const float my_inv = *reinterpret_cast<const MOE_GLOBAL float*>(base + my_off + a.scale_off);
+  const int off_lo = static_cast<int>(static_cast<uint64_t>(my_off) & 0xffffffffu);
+  const int off_hi = static_cast<int>(static_cast<uint64_t>(my_off) >> 32);
+  const int addv = (ok && lane < k) ? 1 : 0;
+  int64_t row_off[kMaxK];
+  bool add[kMaxK];
+#pragma unroll
+  for (int q = 0; q < kMaxK; ++q) {
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(off_lo, q));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(off_hi, q));
+    row_off[q] = static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+    add[q] = __builtin_amdgcn_readlane(addv, q) != 0;
+  }
+
+  const int chunks = a.hidden / kElems;
+  int cidx[kC];
+#pragma unroll
+  for (int i = 0; i < kC; ++i) cidx[i] = lane + (part * kC + i) * kWave;
+  auto load_row = [&](C (&r)[kC], int j) {
+#pragma unroll
+    for (int i = 0; i < kC; ++i)
+      load_chunk<kRecv, kElems, false>(r[i], base + row_off[j] + static_cast<int64_t>(min(cidx[i], chunks - 1)) * kElems);
+  };
+  float acc[kC][kElems];
+#pragma unroll
+  for (int i = 0; i < kC; ++i)
+#pragma unroll
+    for (int q = 0; q < kElems; ++q) acc[i][q] = 0.0f;
+  C buf[kD + 1][kC];
+#pragma unroll
+  for (int j = 0; j < kD && j < kMaxK; ++j) load_row(buf[j], j);
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j + kD < kMaxK) load_row(buf[(j + kD) % (kD + 1)], j + kD);
+    if (add[j]) {
+      const float w = lane_float(my_w, j);
+      const float inv = lane_float(my_inv, j);
+#pragma unroll
+      for (int i = 0; i < kC; ++i)
+#pragma unroll
+        for (int q = 0; q < kElems; ++q) {
+          const float v = element<kRecv, kElems>(buf[j % (kD + 1)][i], q, inv);
+          const float p = v * w;
+          acc[i][q] = acc[i][q] + p;
+        }
+    }
+  }
+  const size_t out_base = static_cast<size_t>(t) * a.hidden;
+#pragma unroll
+  for (int i = 0; i < kC; ++i)
+    if (cidx[i] < chunks) store_out<kOut, kElems, false>(out, out_base + static_cast<size_t>(cidx[i]) * kElems, acc[i]);
+}
+
+template <Out kOut, int kMaxK>
+hipError_t launch_rows_c(const RouteArgs& a, const uint8_t* recv, const float* w, void* out,
+                         hipStream_t stream) {
+  // kC chunks per lane, four waves: 256 kC chunks of 8 codes per token
+  const int chunks = a.hidden / 8;
+#define MOE_ROWS_CASE(C)                                                                                   \
+  if (chunks <= 256 * (C)) {                                                                               \
+    hipLaunchKernelGGL((combine_rows_kernel<kOut, C, kMaxK>), dim3(a.bs), dim3(kCombineThreads), 0, stream, \
+                       a, recv, w, out);                                                                   \
+    return hipGetLastError();                                                                              \
+  }
+  MOE_ROWS_CASE(1)
+  MOE_ROWS_CASE(2)
+  MOE_ROWS_CASE(4)
+  MOE_ROWS_CASE(8)
+#undef MOE_ROWS_CASE
+  return hipErrorInvalidValue;
+}
+
 template <Recv kRecv, Out kOut>
 hipError_t launch_k(const RouteArgs& a, const uint8_t* recv, const float* w, void* out,
                     hipStream_t stream) {
-  if (a.k <= 4) return launch_shape<kRecv, kOut, 4>(a, recv, w, out, stream);
-  if (a.k <= 8) return launch_shape<kRecv, kOut, 8>(a, recv, w, out, stream);
-  return launch_shape<kRecv, kOut, 32>(a, recv, w, out, stream);
+  if constexpr (kRecv == Recv::kInt8) {
+    if (a.k <= 4) return launch_rows_c<kOut, 4>(a, recv, w, out, stream);
+    if (a.k <= 8) return launch_rows_c<kOut, 8>(a, recv, w, out, stream);
+    return launch_shape<kRecv, kOut, 32>(a, recv, w, out, stream);
+  } else {
+    if (a.k <= 4) return launch_shape<kRecv, kOut, 4>(a, recv, w, out, stream);
+    if (a.k <= 8) return launch_shape<kRecv, kOut, 8>(a, recv, w, out, stream);
+    return launch_shape<kRecv, kOut, 32>(a, recv, w, out, stream);
+  }
 }
 
 template <Recv kRecv>
