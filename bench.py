@@ -699,16 +699,23 @@ def ingest_pmc(args, fetch_csv: str, write_csv: str) -> int:
     if args.stage == "epilogue":
         ce = W.EPILOGUE_CONFIG
         workload, mode = "epilogue", f"n{ce['n']}"
-        kernels = (("epilogue", "deq_swiglu_quant_kernel", epilogue_bytes(ce["rows"], ce["n"])),)
+        kernels = (("epilogue", ("deq_swiglu_quant_kernel",), epilogue_bytes(ce["rows"], ce["n"])),)
     else:
         c = W.CONFIGS[args.workload]
         workload, mode = args.workload, args.mode
         b_dis, b_com, b_lay = algorithmic_bytes(c["bs"], c["hidden"], c["topk"], quant)
-        kernels = (("dispatch", "dispatch_kernel", b_dis), ("combine", "combine_kernel", b_com),
-                   ("fused", "fused_kernel", b_dis + b_lay))
-    for kernel, symbol, alg in kernels:
-        kname, f = pick(fetch, symbol, required=False)
-        _, wr = pick(write, symbol, required=False)
+        kernels = (("dispatch", ("dispatch_kernel",), b_dis),
+                   ("combine", ("combine_rows_kernel", "combine_kernel"), b_com),
+                   ("fused", ("fused_kernel",), b_dis + b_lay))
+    for kernel, symbols, alg in kernels:
+        if isinstance(symbols, str):
+            symbols = (symbols,)
+        kname = f = wr = None
+        for symbol in symbols:  # the first symbol the run launched
+            kname, f = pick(fetch, symbol, required=False)
+            _, wr = pick(write, symbol, required=False)
+            if f is not None and wr is not None:
+                break
         if f is None or wr is None:
             continue  # not launched in this run
         traffic = f * 1024.0 * f_scale + wr * 1024.0 * w_scale
