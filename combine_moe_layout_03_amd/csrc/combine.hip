@@ -9,19 +9,17 @@
 // output type (bf16: the hardware v_cvt_pk_bf16_f32 pair conversion) and
 // stored with 16-byte stores.  Two kernels, four waves per token in both:
 //
-// combine_rows_kernel (int8 rows, k <= 8): wave p owns, in every row, the
-// chunks (8 codes each) lane + 64 (p kC + i), i < kC, and reads the token's
-// rows one after another in entry order -- the order it adds in -- with the
-// loads of row j + 2 in flight while row j is added into accumulators held
-// in registers.  Each wave's share of a row is kC contiguous 512-byte
-// pieces.  At h = 7168, k = 8 this measured 2-4 us faster than reading a
-// slice of all k rows at once.
+// combine_rows_kernel (k <= 8): wave p owns, in every row, the chunks (8
+// elements each) lane + 64 (p kC + i), i < kC, and reads the token's rows
+// one after another in entry order -- the order it adds in -- with the loads
+// of row j + 2 in flight while row j is added into accumulators held in
+// registers.  Each wave's share of a row is kC contiguous 512-byte (int8)
+// or 1024-byte (16-bit) pieces.  At h = 7168, k = 8 this measured 2-4 us
+// faster than reading a slice of all k rows at once, for int8 and bf16 rows.
 //
-// combine_kernel (16-bit rows, and int8 rows with k > 8): each wave owns
-// every fourth group of 64 chunks and walks its chunks, software-pipelined:
-// the k row loads of the next chunk are issued before the current chunk is
-// summed.  For 16-bit rows this was the faster of the two (95 against
-// 107 us for bf16 rows at h = 7168, k = 8).
+// combine_kernel (k > 8): each wave owns every fourth group of 64 chunks and
+// walks its chunks, software-pipelined: the k row loads of the next chunk
+// are issued before the current chunk is summed.
 #include "device_util.h"
 #include "launch.h"
 
@@ -243,18 +241,19 @@ hipError_t launch_shape(const RouteArgs& a, const uint8_t* recv, const float* w,
   return hipGetLastError();
 }
 
-// int8 rows, k <= kMaxK: the token's rows one at a time (see the file
+// k <= kMaxK: the token's rows one at a time (see the file
 // header).  Lane j resolves entry j; lanes j >= k take entry k - 1's row (so
 // the loads of rows past k re-read a row this wave has just read, from L2)
 // but are never added.  Rows are read with no branches around the loads:
 // skipping the rows past k with a branch measured 1.4 us slower.
-template <Out kOut, int kC, int kMaxK>
+template <Recv kRecv, Out kOut, int kC, int kMaxK>
 __global__ __launch_bounds__(kCombineThreads) void combine_rows_kernel(RouteArgs a,
                                                                        const uint8_t* __restrict__ recv,
                                                                        const float* __restrict__ topk_w,
                                                                        void* __restrict__ out) {
-  constexpr Recv kRecv = Recv::kInt8;
   constexpr int kElems = 8;
+  constexpr int kChunkBytes = kElems * elem_bytes<kRecv>();
+  constexpr bool kNt = kRecv != Recv::kInt8;  // 16-bit rows: non-temporal loads
   constexpr int kD = 2;  // rows in flight ahead of the one being added
   using C = Chunk<kRecv, kElems>;
   const int lane = threadIdx.x & (kWave - 1);
@@ -274,7 +273,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_rows_kernel(RouteArgs
   const bool ok = static_cast<unsigned>(e) < static_cast<unsigned>(a.num_experts) && slot >= 0 && row >= 0 &&
                   row < a.cap_rows;
   const int64_t my_off = ok ? row * a.row_bytes : 0;  // not dispatched: row 0, read but not added
-  const float my_inv = *reinterpret_cast<const MOE_GLOBAL float*>(base + my_off + a.scale_off);
+  float my_inv = 1.0f;
+  if constexpr (kRecv == Recv::kInt8)
+    my_inv = *reinterpret_cast<const MOE_GLOBAL float*>(base + my_off + a.scale_off);
   const int off_lo = static_cast<int>(static_cast<uint64_t>(my_off) & 0xffffffffu);
   const int off_hi = static_cast<int>(static_cast<uint64_t>(my_off) >> 32);
   const int addv = (ok && lane < k) ? 1 : 0;
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_rows_kernel(RouteArgs
   auto load_row = [&](C (&r)[kC], int j) {
 #pragma unroll
     for (int i = 0; i < kC; ++i)
-      load_chunk<kRecv, kElems, false>(r[i], base + row_off[j] + static_cast<int64_t>(min(cidx[i], chunks - 1)) * kElems);
+      load_chunk<kRecv, kElems, kNt>(r[i], base + row_off[j] + static_cast<int64_t>(min(cidx[i], chunks - 1)) * kChunkBytes);
   };
   float acc[kC][kElems];
 #pragma unroll
@@ -327,14 +328,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_rows_kernel(RouteArgs
     if (cidx[i] < chunks) store_out<kOut, kElems, false>(out, out_base + static_cast<size_t>(cidx[i]) * kElems, acc[i]);
 }
 
-template <Out kOut, int kMaxK>
+template <Recv kRecv, Out kOut, int kMaxK>
 hipError_t launch_rows_c(const RouteArgs& a, const uint8_t* recv, const float* w, void* out,
                          hipStream_t stream) {
-  // kC chunks per lane, four waves: 256 kC chunks of 8 codes per token
+  // kC chunks per lane, four waves: 256 kC chunks of 8 elements per token
   const int chunks = a.hidden / 8;
 #define MOE_ROWS_CASE(C)                                                                                   \
   if (chunks <= 256 * (C)) {                                                                               \
-    hipLaunchKernelGGL((combine_rows_kernel<kOut, C, kMaxK>), dim3(a.bs), dim3(kCombineThreads), 0, stream, \
+    hipLaunchKernelGGL((combine_rows_kernel<kRecv, kOut, C, kMaxK>), dim3(a.bs), dim3(kCombineThreads), 0, stream, \
                        a, recv, w, out);                                                                   \
     return hipGetLastError();                                                                              \
   }
@@ -349,15 +350,9 @@ hipError_t launch_rows_c(const RouteArgs& a, const uint8_t* recv, const float* w
 template <Recv kRecv, Out kOut>
 hipError_t launch_k(const RouteArgs& a, const uint8_t* recv, const float* w, void* out,
                     hipStream_t stream) {
-  if constexpr (kRecv == Recv::kInt8) {
-    if (a.k <= 4) return launch_rows_c<kOut, 4>(a, recv, w, out, stream);
-    if (a.k <= 8) return launch_rows_c<kOut, 8>(a, recv, w, out, stream);
-    return launch_shape<kRecv, kOut, 32>(a, recv, w, out, stream);
-  } else {
-    if (a.k <= 4) return launch_shape<kRecv, kOut, 4>(a, recv, w, out, stream);
-    if (a.k <= 8) return launch_shape<kRecv, kOut, 8>(a, recv, w, out, stream);
-    return launch_shape<kRecv, kOut, 32>(a, recv, w, out, stream);
-  }
+  if (a.k <= 4) return launch_rows_c<kRecv, kOut, 4>(a, recv, w, out, stream);
+  if (a.k <= 8) return launch_rows_c<kRecv, kOut, 8>(a, recv, w, out, stream);
+  return launch_shape<kRecv, kOut, 32>(a, recv, w, out, stream);
 }
 
 template <Recv kRecv>
