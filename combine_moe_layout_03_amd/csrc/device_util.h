@@ -46,22 +46,39 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int d = kWave / 2; d >= 1; d >>= 1) {
-    const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), d, kWave));
-    v = v > o ? v : o;
-  }
+// Cross-lane steps through DPP (the data-parallel-primitives operand form of
+// VALU instructions), not through the LDS crossbar: a shift of 1, 2, 4 and
+// 8 lanes within each row of 16 lanes (a lane shifted in from outside its
+// row reads 0), then row_bcast:15 (the last lane of a row, to every lane of
+// the next row; applied to rows 1 and 3) and row_bcast:31 (lane 31 to rows 2
+// and 3).  Run as a Hillis-Steele scan these give every lane the combination
+// of all lanes up to and including itself.  The whole wave must be active.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <typename Op>
+__device__ __forceinline__ int wave_scan_dpp(int v, Op op) {
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, kDppRowShr1, 0xf, 0xf, false));
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, kDppRowShr2, 0xf, 0xf, false));
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, kDppRowShr4, 0xf, 0xf, false));
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, kDppRowShr8, 0xf, 0xf, false));
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xa, 0xf, false));
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xc, 0xf, false));
   return v;
 }
 
-__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
-  return v;
+// Largest value over the wave, in every lane (a wave-uniform result).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  const int m = wave_scan_dpp(static_cast<int>(v), [](int a, int b) {
+    return static_cast<int>(static_cast<uint32_t>(a) > static_cast<uint32_t>(b) ? static_cast<uint32_t>(a)
+                                                                                 : static_cast<uint32_t>(b));
+  });
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(m, kWave - 1));
+}
+
+// Inclusive prefix sum over the lanes of the wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  return wave_scan_dpp(v, [](int a, int b) { return a + b; });
 }
 
 // A value known to be the same in every lane, moved to a scalar register.

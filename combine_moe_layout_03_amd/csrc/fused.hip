@@ -11,18 +11,23 @@
 // workgroup's arrival is a device-scope atomic on one address, and 256-512 of
 // them serialise at the memory side, tens of microseconds.  Counting the ids
 // is cheap next to the rows, so here every workgroup counts all of them
-// itself and no workgroup waits on another:
-//   1. Each thread issues the loads of its first 32 ids, then each wave the
-//      loads of its first token's row; the row arrives while the rest runs.
-//   2. All bs*k ids are counted into two LDS histograms: the entries before
-//      this workgroup's first entry, and the rest.  Their sum is the layout
-//      stage's per-expert totals (with invalid ids in the last bin).  Each
-//      histogram has C interleaved copies (lane l adds to copy l % C, the
-//      copies of one bin in adjacent banks): lanes of one atomic that hit
-//      the same expert hit at most 64 / C to one word: with one copy, a
-//      batch that sends every entry to one expert makes each atomic 64-way
-//      serial (about 18 us more at bs 4096); with 8 copies it costs what a
-//      uniform batch does.  The copies are summed afterwards.
+// itself and no workgroup waits on another.  A workgroup's 16 waves split
+// into 8 counting waves and 8 row waves:
+//   1. The counting waves issue the loads of all their ids; after the one
+//      workgroup barrier, each row wave issues the loads of its first
+//      token's row (when it fits in registers), which arrive while steps 2-4
+//      run.  Issuing a row's 14 loads stalls a wave for as long as the
+//      memory system takes to accept them (up to about 10 us at bs 4096,
+//      h 7168), so the row waves do nothing else until step 5.
+//   2. The counting waves count all bs*k ids into two LDS histograms: the
+//      entries before this workgroup's first entry, and the rest.  Their sum
+//      is the layout stage's per-expert totals (with invalid ids in the last
+//      bin).  Each histogram has C copies (lane l adds to copy l % C): lanes
+//      of one atomic that hit the same expert hit at most 64 / C to one
+//      word: with one copy, a batch that sends every entry to one expert
+//      makes each atomic 64-way serial (about 18 us more at bs 4096); with
+//      8 copies it costs what a uniform batch does.  The copies are summed
+//      afterwards.
 //   3. An exclusive scan of the totals in LDS is the notify stage: the
 //      receive row of (expert e, slot s) is scan[e] + s.  Workgroup 0 writes
 //      the layout and notify outputs.
@@ -31,8 +36,11 @@
 //      to the expert's running count (seeded with the counts before the
 //      workgroup), so each entry's slot is its stable rank within its
 //      expert.  The slots go to LDS and to sendTokenIdx.
+//   The counting waves synchronise steps 2-4 among themselves through LDS
+//   counters; the row waves wait for the last of them.
 //   5. Each wave quantises (or passes through) its tokens and writes every
-//      copy, as the dispatch kernel does.
+//      copy, as the dispatch kernel does; the counting waves load their rows
+//      here.
 // The ids are read once per workgroup from L2 (bs*k*4 bytes each); with one
 // workgroup per CU that is the only redundant work.
 #include <hip/hip_runtime.h>
@@ -50,9 +58,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = kFusedWaves;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kQuads = 8;       // 16-byte id loads per thread in a whole batch
-constexpr int kBatch = kThreads * kQuads * 4;  // ids per whole batch
-constexpr int kTailLoads = 8;  // 4-byte id loads per thread in the rest
+constexpr int kCountWaves = kWaves / 2;  // waves that count the ids
+constexpr int kCountThreads = kCountWaves * kWave;
+constexpr int kQuads = 16;  // groups of four ids per counting thread and round
+constexpr int kSyncs = 3;   // sync points of the counting waves
+constexpr int kMaxPer = (MOE_MAX_EXPERTS + kCountThreads - 1) / kCountThreads;  // experts per counting thread
+// s_waitcnt vmcnt(0) with expcnt and lgkmcnt at their maxima.  The compiler
+// places its waits for loads per register, merging the two paths below as
+// if either could have run: the ids' registers look in flight on the row
+// path, and the row's on the id path, so code after the paths join would
+// wait there for part of the row.  An explicit wait on each path, where
+// nothing is in flight in fact, clears that state.
+constexpr int kWaitVm0 = 0x0f70;
 
 // Row t into registers, 16 bytes (8 elements) per chunk, chunk lane + 64 i
 // in v[i].  Chunks past the row's end load its last chunk again (a duplicate
@@ -73,14 +90,18 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   extern __shared__ int32_t lds[];
   const int E = a.num_experts;
   const int C = 1 << a.copies_log2;       // histogram copies: lane l counts into copy l % C
-  int32_t* hpre = lds;                    // [(E + 1) * C] copies of the counts before this group
-  int32_t* htot = hpre + (E + 1) * C;     // [(E + 1) * C] copies of the counts from this group on
+  // Copy c of bin e at [c * (E + 1) + e]: summing the copies of a bin, the
+  // lanes of a wave read consecutive words (a bin-major layout made that
+  // read 8-way bank-conflicted, 1.2 us at 8 copies).
+  int32_t* hpre = lds;                    // [C][E + 1] copies of the counts before this group
+  int32_t* htot = hpre + (E + 1) * C;     // [C][E + 1] copies of the counts from this group on
   int32_t* pre = htot + (E + 1) * C;      // [E + 1] counts before this group; then running counts
   int32_t* tot = pre + (E + 1);           // [E + 1] counts from this group on; then totals
   int32_t* gsc = tot + (E + 1);           // [E + 1] exclusive scan of the totals (gsc[E]: all valid)
   int32_t* ids_l = gsc + (E + 1);         // [T * k] own entries' ids
   int32_t* slot_l = ids_l + a.tokens_per_group * a.k;  // [T * k] own entries' slots (-1: dropped)
-  __shared__ int32_t wave_sum[kWaves];
+  __shared__ int32_t wave_sum[kCountWaves];
+  __shared__ int32_t sync_ctr[kSyncs];  // counting-wave arrivals per sync point
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -92,167 +113,202 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   const int e_begin = t_begin * a.k;
   const int own = (t_end - t_begin) * a.k;
 
-  // 1-2. Histograms of all ids: before this group's first entry, and the
-  //      rest; the group's own ids are also kept in LDS.  Whole batches of
-  //      kQuads * 4 ids per thread are read with unguarded 16-byte loads off
-  //      one base (when the ids are 16-byte aligned), so they issue back to
-  //      back and need one address register; the first batch is issued
-  //      before the row loads, and since loads complete in order, counting
-  //      it waits for the ids only.  The rest of the ids (and all of them
-  //      when unaligned) are read kTailLoads per thread with clamped indices.
-  for (int e = tid; e < 2 * (E + 1) * C; e += kThreads) hpre[e] = 0;  // hpre and htot
-  __syncthreads();
+  // 1-2. Histograms of all ids, by the counting waves 0 .. kCountWaves - 1:
+  //      before this group's first entry, and the rest; the group's own ids
+  //      are also kept in LDS.  A counting thread reads kQuads groups of four
+  //      ids per round (16-byte loads when the ids are 16-byte aligned),
+  //      indices clamped to the last whole group and the loads issued back to
+  //      back; the last n % 4 ids are counted one by one.
+  //      The other waves (the row waves) load their rows meanwhile when a
+  //      row fits in registers (up to 14 chunks per lane, h <= 7168), asked
+  //      for after the counting waves' first ids, which then arrive first.
+  //      A wave stalls while its row's loads wait to issue, which lasts until
+  //      most rows are in (about 10 us at bs 4096, h 7168); so the row waves
+  //      take no part in the count, the scan or the ranking, and those
+  //      phases synchronise only the counting waves, through LDS counters,
+  //      not the workgroup barrier.  The row waves wait for one flag, set
+  //      once the slots are ranked.  Longer rows are loaded by every wave
+  //      after that flag.
   const int e_end = e_begin + own;
   const int copy = lane & (C - 1);
+  const bool counter = wave < kCountWaves;
+  const int nq = n >> 2;  // whole groups of four ids
   auto count_one = [&](int i, int e) {
     const int bin = static_cast<unsigned>(e) < static_cast<unsigned>(E) ? e : E;
-    atomicAdd((i < e_begin ? hpre : htot) + bin * C + copy, 1);
+    atomicAdd((i < e_begin ? hpre : htot) + copy * (E + 1) + bin, 1);
     if (i >= e_begin && i < e_end) ids_l[i - e_begin] = e;
   };
   int4 quads[kQuads];
-  auto load_batch = [&](int b) {
-    const int4* src = reinterpret_cast<const int4*>(a.topk_idx + b);
+  auto load_round = [&](int q0) {
+    if (a.ids_aligned16) {
+      const int4* src = reinterpret_cast<const int4*>(a.topk_idx);
 #pragma unroll
-    for (int u = 0; u < kQuads; ++u) quads[u] = src[u * kThreads + tid];
-  };
-  auto count_batch = [&](int b) {
+      for (int u = 0; u < kQuads; ++u) quads[u] = src[min(q0 + u * kCountThreads + tid, nq - 1)];
+    } else {
 #pragma unroll
-    for (int u = 0; u < kQuads; ++u) {
-      const int i = b + 4 * (u * kThreads + tid);
-      count_one(i, quads[u].x);
-      count_one(i + 1, quads[u].y);
-      count_one(i + 2, quads[u].z);
-      count_one(i + 3, quads[u].w);
+      for (int u = 0; u < kQuads; ++u) {
+        const int32_t* src = a.topk_idx + 4 * min(q0 + u * kCountThreads + tid, nq - 1);
+        quads[u] = make_int4(src[0], src[1], src[2], src[3]);
+      }
     }
   };
+  auto count_round = [&](int q0) {
+#pragma unroll
+    for (int u = 0; u < kQuads; ++u) {
+      const int q = q0 + u * kCountThreads + tid;
+      if (q < nq) {
+        count_one(4 * q, quads[u].x);
+        count_one(4 * q + 1, quads[u].y);
+        count_one(4 * q + 2, quads[u].z);
+        count_one(4 * q + 3, quads[u].w);
+      }
+    }
+  };
+  // Arrival of every counting wave at sync point p: LDS writes before it
+  // are seen by every counting wave after it.
+  auto counters_sync = [&](int p) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    if (lane == 0) __hip_atomic_fetch_add(&sync_ctr[p], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    while (__hip_atomic_load(&sync_ctr[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < kCountWaves) {
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+  constexpr int kRound = kCountThreads * kQuads;  // groups of four per round
+  if (counter && nq > 0) load_round(0);
+  for (int e = tid; e < 2 * (E + 1) * C; e += kThreads) hpre[e] = 0;  // hpre and htot
+  if (tid < kSyncs) sync_ctr[tid] = 0;
+  __syncthreads();
   // The first token of this wave (waves past the group's last token load
-  // that token's row again and never use it): loaded early, used at the end.
+  // that token's row again and never use it).
   uint4 v[kVpl];
   const int t_first = t_begin + wave;
   const int t_pre = t_first < t_end ? t_first : t_end - 1;
-  int b = 0;
-  // The row is loaded during the count when it fits in registers beside a
-  // whole batch of ids (up to 14 chunks per lane, h <= 7168); a longer row
-  // would spill, so it is loaded after the count.
   constexpr bool kRowDuringCount = kVpl <= 14;
-  const bool whole = a.ids_aligned16 && n >= kBatch;
-  const bool row_early = whole && kRowDuringCount;
-  if (whole) {
-    load_batch(0);
-    if (row_early) load_row<kVpl>(v, a.x, t_pre, a.hidden, lane);
-    count_batch(0);
-    for (b = kBatch; b + kBatch <= n; b += kBatch) {
-      load_batch(b);
-      count_batch(b);
+  const bool have_row = kRowDuringCount && !counter;
+  if (counter) {
+    if (nq > 0) count_round(0);
+    for (int q0 = kRound; q0 < nq; q0 += kRound) {
+      load_round(q0);
+      count_round(q0);
     }
-  }
-  for (; b < n; b += kThreads * kTailLoads) {
-    int ids[kTailLoads];
-#pragma unroll
-    for (int u = 0; u < kTailLoads; ++u) {
-      const int i = b + u * kThreads + tid;
-      ids[u] = a.topk_idx[i < n ? i : n - 1];
-    }
-#pragma unroll
-    for (int u = 0; u < kTailLoads; ++u) {
-      const int i = b + u * kThreads + tid;
-      if (i < n) count_one(i, ids[u]);
-    }
-  }
-  if (!row_early) load_row<kVpl>(v, a.x, t_pre, a.hidden, lane);  // few ids, or a long row: counted first
-  __syncthreads();
-  for (int e = tid; e <= E; e += kThreads) {
-    int sp = 0, st = 0;
-    for (int c = 0; c < C; ++c) {
-      sp += hpre[e * C + c];
-      st += htot[e * C + c];
-    }
-    pre[e] = sp;
-    tot[e] = st;
-  }
-  __syncthreads();
+    const int i = 4 * nq + tid;
+    if (i < n) count_one(i, a.topk_idx[i]);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // ids that no lane used
+    counters_sync(0);
 
-  // 3. Totals and their exclusive scan (notify).  Thread t owns the
-  //    contiguous experts [t * per, (t + 1) * per).
-  {
-    const int per = (E + kThreads - 1) / kThreads;  // 1 or 2 (E <= 2048)
+    // 3. Totals and their exclusive scan (notify).  Counting thread c owns
+    //    the contiguous experts [c * per, (c + 1) * per), per <= kMaxPer,
+    //    sums their histogram copies and scans; the last thread also sums
+    //    the invalid-id bin E.
+    const int per = (E + kCountThreads - 1) / kCountThreads;
     const int e0 = tid * per;
-    int c0 = 0, c1 = 0;
-    if (e0 < E) c0 = tot[e0] + pre[e0];
-    if (per > 1 && e0 + 1 < E) c1 = tot[e0 + 1] + pre[e0 + 1];
-    const int sum = c0 + c1;
-    const int incl = wave_inclusive_scan(sum, lane);
+    int cnt[kMaxPer];
+    int sum = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxPer; ++q) {
+      cnt[q] = 0;
+      const int e = e0 + q;
+      if (q < per && e < E) {
+        int sp = 0, st = 0;
+        for (int c = 0; c < C; ++c) {
+          sp += hpre[c * (E + 1) + e];
+          st += htot[c * (E + 1) + e];
+        }
+        pre[e] = sp;
+        cnt[q] = sp + st;
+        sum += cnt[q];
+      }
+    }
+    if (tid == kCountThreads - 1) {
+      int sp = 0, st = 0;
+      for (int c = 0; c < C; ++c) {
+        sp += hpre[c * (E + 1) + E];
+        st += htot[c * (E + 1) + E];
+      }
+      tot[E] = sp + st;
+    }
+    const int incl = wave_inclusive_scan(sum);
     if (lane == kWave - 1) wave_sum[wave] = incl;
-    __syncthreads();
+    counters_sync(1);
     int off = 0;
     for (int w = 0; w < wave; ++w) off += wave_sum[w];
-    const int excl = off + incl - sum;
-    if (e0 < E) {
-      tot[e0] = c0;
-      gsc[e0] = excl;
+    int excl = off + incl - sum;
+#pragma unroll
+    for (int q = 0; q < kMaxPer; ++q) {
+      const int e = e0 + q;
+      if (q < per && e < E) {
+        tot[e] = cnt[q];
+        gsc[e] = excl;
+        excl += cnt[q];
+      }
     }
-    if (per > 1 && e0 + 1 < E) {
-      tot[e0 + 1] = c1;
-      gsc[e0 + 1] = excl + c0;
-    }
-    if (tid == 0) {
+    if (tid == kCountThreads - 1) {
       int total = 0;
-      for (int w = 0; w < kWaves; ++w) total += wave_sum[w];
+      for (int w = 0; w < kCountWaves; ++w) total += wave_sum[w];
       gsc[E] = total;
-      tot[E] += pre[E];
     }
-  }
-  __syncthreads();
-  if (group == 0) {
-    for (int e = tid; e < E; e += kThreads) {
-      const int first = (e / a.epr) * a.epr;
-      a.token_per_expert[e] = tot[e];
-      a.recv_token_per_expert[e] = tot[e];
-      a.put_offset[e] = gsc[e] - gsc[first];
-    }
-    for (int r = tid; r < a.ranks; r += kThreads) {
-      const int cnt = gsc[(r + 1) * a.epr] - gsc[r * a.epr];
-      a.recv_base[r] = gsc[r * a.epr];
-      a.recv_count[r] = cnt;
-      a.token_per_rank[r] = cnt;
-    }
-    if (tid == 0 && a.bad_count != nullptr) *a.bad_count = tot[E];
-  }
 
-  // 4. Slots of this group's own entries, in entry order, by wave 0 alone
-  //    (LDS atomics of one wave complete in issue order, which keeps the
-  //    ranks stable across rounds).
-  if (wave == 0) {
-    for (int r0 = 0; r0 < own; r0 += kWave) {
-      const int li = r0 + lane;
-      const bool in_range = li < own;
-      const int e = in_range ? ids_l[li] : -1;
-      const bool valid = in_range && static_cast<unsigned>(e) < static_cast<unsigned>(E);
-      uint64_t peers = __ballot(valid);
-      for (int bit = 0; bit < a.id_bits; ++bit) {
-        const bool on = (e >> bit) & 1;
-        const uint64_t set = __ballot(on);
-        peers &= on ? set : ~set;
-      }
-      const int below = valid ? lanes_below(peers) : 0;
-      const int leader = valid ? 63 - __builtin_clzll(peers) : lane;
-      int ret = 0;
-      if (valid && leader == lane) ret = atomicAdd(&pre[e], __popcll(peers));
-      const int start = __shfl(ret, leader, kWave);
-      if (in_range) {
-        const int slot = valid ? start + below : -1;
-        ids_l[li] = valid ? e : 0;
-        slot_l[li] = slot;
-        a.send_token_idx[e_begin + li] = slot;
+    // 4. Slots of this group's own entries, in entry order, by wave 0 alone
+    //    (LDS atomics of one wave complete in issue order, which keeps the
+    //    ranks stable across rounds).
+    if (wave == 0) {
+      for (int r0 = 0; r0 < own; r0 += kWave) {
+        const int li = r0 + lane;
+        const bool in_range = li < own;
+        const int e = in_range ? ids_l[li] : -1;
+        const bool valid = in_range && static_cast<unsigned>(e) < static_cast<unsigned>(E);
+        uint64_t peers = __ballot(valid);
+        for (int bit = 0; bit < a.id_bits; ++bit) {
+          const bool on = (e >> bit) & 1;
+          const uint64_t set = __ballot(on);
+          peers &= on ? set : ~set;
+        }
+        const int below = valid ? lanes_below(peers) : 0;
+        const int leader = valid ? 63 - __builtin_clzll(peers) : lane;
+        int ret = 0;
+        if (valid && leader == lane) ret = atomicAdd(&pre[e], __popcll(peers));
+        const int start = __shfl(ret, leader, kWave);
+        if (in_range) {
+          const int slot = valid ? start + below : -1;
+          ids_l[li] = valid ? e : 0;
+          slot_l[li] = slot;
+          a.send_token_idx[e_begin + li] = slot;
+        }
       }
     }
+    counters_sync(2);  // slots ready
+    if (group == 0) {
+      for (int e = tid; e < E; e += kCountThreads) {
+        const int first = (e / a.epr) * a.epr;
+        a.token_per_expert[e] = tot[e];
+        a.recv_token_per_expert[e] = tot[e];
+        a.put_offset[e] = gsc[e] - gsc[first];
+      }
+      for (int r = tid; r < a.ranks; r += kCountThreads) {
+        const int c = gsc[(r + 1) * a.epr] - gsc[r * a.epr];
+        a.recv_base[r] = gsc[r * a.epr];
+        a.recv_count[r] = c;
+        a.token_per_rank[r] = c;
+      }
+      if (tid == 0 && a.bad_count != nullptr) *a.bad_count = tot[E];
+    }
+  } else if (kRowDuringCount) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // nothing in flight here: free
+    load_row<kVpl>(v, a.x, t_pre, a.hidden, lane);
   }
-  __syncthreads();
+  // The row waves wait for every counting wave to pass the last sync point.
+  if (!counter) {
+    while (__hip_atomic_load(&sync_ctr[kSyncs - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < kCountWaves) {
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  }
 
   // 5. Dispatch of this group's tokens: wave w takes tokens w, w + 16, ...
   const int chunks = a.hidden >> 3;
   for (int t = t_first; t < t_end; t += kWaves) {
-    if (t != t_first) load_row<kVpl>(v, a.x, t, a.hidden, lane);
+    if (t != t_first || !have_row) load_row<kVpl>(v, a.x, t, a.hidden, lane);
     const int li0 = (t - t_begin) * a.k;
     if constexpr (!kQuant) {
       for (int j = 0; j < a.k; ++j) {

@@ -82,7 +82,6 @@ constexpr int kFusedMaxHidden = 16 * 64 * 8;    // row held in registers: 16 chu
 constexpr int64_t kFusedMaxEntries = 1 << 16;   // bs * k: every workgroup counts all ids
 constexpr size_t kFusedMaxLds = 64 * 1024;
 constexpr int kFusedMaxCopiesLog2 = 3;          // up to 8 copies of each LDS histogram
-static_assert(MOE_MAX_EXPERTS <= 2 * kFusedWaves * 64, "the fused scan gives each thread two experts");
 
 struct FusedArgs {
   const uint16_t* x;

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kNotifyThreads) void notify_kernel(
     cnt[j] = (j < per && e < num_experts) ? token_per_expert[e] : 0;
     sum += cnt[j];
   }
-  const int incl = wave_inclusive_scan(sum, lane);
+  const int incl = wave_inclusive_scan(sum);
   if (lane == kWave - 1) wave_sum[wave] = incl;
   __syncthreads();
   int run = incl - sum;
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kMultiThreads) void notify_multi_kernel(
       if (++src == num_src) { src = 0; ++e; }
     }
   }
-  const int incl = wave_inclusive_scan(sum, lane);
+  const int incl = wave_inclusive_scan(sum);
   if (lane == kWave - 1) wave_sum[wave] = incl;
   __syncthreads();
   int run = incl - sum;
