@@ -13,10 +13,12 @@
 // is cheap next to the rows, so here every workgroup counts all of them
 // itself and no workgroup waits on another.  A workgroup's 16 waves split
 // into 8 counting waves and 8 row waves:
-//   1. The counting waves issue the loads of all their ids; after the one
+//   1. The counting waves issue the loads of all their ids; after a
 //      workgroup barrier, each row wave issues the loads of its first
-//      token's row (when it fits in registers), which arrive while steps 2-4
-//      run.  Issuing a row's 14 loads stalls a wave for as long as the
+//      token's row (up to 14 chunks per lane, h <= 7168; a longer row
+//      follows step 4), which arrive while steps 2-4 run.  Tokens go to the
+//      row waves first, so a group of up to 8 tokens has all its rows
+//      early.  Issuing a row's 14 loads stalls a wave for as long as the
 //      memory system takes to accept them (up to about 10 us at bs 4096,
 //      h 7168), so the row waves do nothing else until step 5.
 //   2. The counting waves count all bs*k ids into two LDS histograms: the
@@ -37,7 +39,7 @@
 //      workgroup), so each entry's slot is its stable rank within its
 //      expert.  The slots go to LDS and to sendTokenIdx.
 //   The counting waves synchronise steps 2-4 among themselves through LDS
-//   counters; the row waves wait for the last of them.
+//   counters; the one workgroup barrier after step 4 lets the row waves on.
 //   5. Each wave quantises (or passes through) its tokens and writes every
 //      copy, as the dispatch kernel does; the counting waves load their rows
 //      here.
@@ -61,7 +63,10 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kCountWaves = kWaves / 2;  // waves that count the ids
 constexpr int kCountThreads = kCountWaves * kWave;
 constexpr int kQuads = 16;  // groups of four ids per counting thread and round
-constexpr int kSyncs = 3;   // sync points of the counting waves
+constexpr int kSyncs = 2;   // sync points of the counting waves
+constexpr int kMaxCopies = 1 << kFusedMaxCopiesLog2;
+constexpr int kMaxIdBits = 11;  // bits of an expert id (E <= 2048)
+static_assert(MOE_MAX_EXPERTS <= (1 << kMaxIdBits), "expert ids fit in kMaxIdBits bits");
 constexpr int kMaxPer = (MOE_MAX_EXPERTS + kCountThreads - 1) / kCountThreads;  // experts per counting thread
 // s_waitcnt vmcnt(0) with expcnt and lgkmcnt at their maxima.  The compiler
 // places its waits for loads per register, merging the two paths below as
@@ -119,24 +124,22 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   //      ids per round (16-byte loads when the ids are 16-byte aligned),
   //      indices clamped to the last whole group and the loads issued back to
   //      back; the last n % 4 ids are counted one by one.
-  //      The other waves (the row waves) load their rows meanwhile when a
-  //      row fits in registers (up to 14 chunks per lane, h <= 7168), asked
-  //      for after the counting waves' first ids, which then arrive first.
-  //      A wave stalls while its row's loads wait to issue, which lasts until
-  //      most rows are in (about 10 us at bs 4096, h 7168); so the row waves
-  //      take no part in the count, the scan or the ranking, and those
-  //      phases synchronise only the counting waves, through LDS counters,
-  //      not the workgroup barrier.  The row waves wait for one flag, set
-  //      once the slots are ranked.  Longer rows are loaded by every wave
-  //      after that flag.
-  const int e_end = e_begin + own;
+  //      The other waves (the row waves) load their first tokens' rows
+  //      meanwhile, asked for after the counting waves' ids, which then
+  //      arrive first.  A wave stalls while its row's loads wait to issue,
+  //      which lasts until most rows are in (about 10 us at bs 4096,
+  //      h 7168); so the row waves take no part in the count, the scan or
+  //      the ranking, and those phases synchronise only the counting waves,
+  //      through LDS counters.  The row waves go on at the workgroup barrier
+  //      after the ranking.
   const int copy = lane & (C - 1);
   const bool counter = wave < kCountWaves;
   const int nq = n >> 2;  // whole groups of four ids
+  const int hist_pre = copy * (E + 1);          // this lane's copy in hpre
+  const int hist_tot = hist_pre + (E + 1) * C;  // and in htot, which follows hpre
   auto count_one = [&](int i, int e) {
-    const int bin = static_cast<unsigned>(e) < static_cast<unsigned>(E) ? e : E;
-    atomicAdd((i < e_begin ? hpre : htot) + copy * (E + 1) + bin, 1);
-    if (i >= e_begin && i < e_end) ids_l[i - e_begin] = e;
+    const int bin = static_cast<int>(min(static_cast<unsigned>(e), static_cast<unsigned>(E)));  // invalid: E
+    atomicAdd(hpre + (i < e_begin ? hist_pre : hist_tot) + bin, 1);
   };
   int4 quads[kQuads];
   auto load_round = [&](int q0) {
@@ -175,15 +178,23 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
   constexpr int kRound = kCountThreads * kQuads;  // groups of four per round
+  // The group's own ids (for the ranking) are read beside the first round.
+  const bool own_first = counter && tid < own;
+  const int own_id = own_first ? a.topk_idx[e_begin + tid] : 0;
   if (counter && nq > 0) load_round(0);
   for (int e = tid; e < 2 * (E + 1) * C; e += kThreads) hpre[e] = 0;  // hpre and htot
   if (tid < kSyncs) sync_ctr[tid] = 0;
   __syncthreads();
-  // The first token of this wave (waves past the group's last token load
-  // that token's row again and never use it).
+  // The first token of this wave.
   uint4 v[kVpl];
-  const int t_first = t_begin + wave;
-  const int t_pre = t_first < t_end ? t_first : t_end - 1;
+  // Tokens go to the row waves first: wave w takes the group's tokens
+  // (w - kCountWaves) mod kWaves, then every kWaves-th after it, so a group
+  // of at most kWaves - kCountWaves tokens has all its rows loaded early.
+  const int t_first = t_begin + (wave + kWaves - kCountWaves) % kWaves;
+  // A row of up to 14 chunks per lane (h <= 7168) is loaded early; a
+  // longer one would not fit in registers beside a counting wave's ids (the
+  // kernel's register budget covers both kinds of wave) and is loaded after
+  // the barrier.
   constexpr bool kRowDuringCount = kVpl <= 14;
   const bool have_row = kRowDuringCount && !counter;
   if (counter) {
@@ -194,6 +205,8 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
     }
     const int i = 4 * nq + tid;
     if (i < n) count_one(i, a.topk_idx[i]);
+    if (own_first) ids_l[tid] = own_id;
+    for (int li = tid + kCountThreads; li < own; li += kCountThreads) ids_l[li] = a.topk_idx[e_begin + li];
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // ids that no lane used
     counters_sync(0);
 
@@ -211,9 +224,12 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
       const int e = e0 + q;
       if (q < per && e < E) {
         int sp = 0, st = 0;
-        for (int c = 0; c < C; ++c) {
-          sp += hpre[c * (E + 1) + e];
-          st += htot[c * (E + 1) + e];
+#pragma unroll
+        for (int c = 0; c < kMaxCopies; ++c) {
+          if (c < C) {
+            sp += hpre[c * (E + 1) + e];
+            st += htot[c * (E + 1) + e];
+          }
         }
         pre[e] = sp;
         cnt[q] = sp + st;
@@ -222,9 +238,12 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
     }
     if (tid == kCountThreads - 1) {
       int sp = 0, st = 0;
-      for (int c = 0; c < C; ++c) {
-        sp += hpre[c * (E + 1) + E];
-        st += htot[c * (E + 1) + E];
+#pragma unroll
+      for (int c = 0; c < kMaxCopies; ++c) {
+        if (c < C) {
+          sp += hpre[c * (E + 1) + E];
+          st += htot[c * (E + 1) + E];
+        }
       }
       tot[E] = sp + st;
     }
@@ -259,10 +278,13 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
         const int e = in_range ? ids_l[li] : -1;
         const bool valid = in_range && static_cast<unsigned>(e) < static_cast<unsigned>(E);
         uint64_t peers = __ballot(valid);
-        for (int bit = 0; bit < a.id_bits; ++bit) {
-          const bool on = (e >> bit) & 1;
-          const uint64_t set = __ballot(on);
-          peers &= on ? set : ~set;
+#pragma unroll
+        for (int bit = 0; bit < kMaxIdBits; ++bit) {
+          if (bit < a.id_bits) {
+            const bool on = (e >> bit) & 1;
+            const uint64_t set = __ballot(on);
+            peers &= on ? set : ~set;
+          }
         }
         const int below = valid ? lanes_below(peers) : 0;
         const int leader = valid ? 63 - __builtin_clzll(peers) : lane;
@@ -277,32 +299,27 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
         }
       }
     }
-    counters_sync(2);  // slots ready
-    if (group == 0) {
-      for (int e = tid; e < E; e += kCountThreads) {
-        const int first = (e / a.epr) * a.epr;
-        a.token_per_expert[e] = tot[e];
-        a.recv_token_per_expert[e] = tot[e];
-        a.put_offset[e] = gsc[e] - gsc[first];
-      }
-      for (int r = tid; r < a.ranks; r += kCountThreads) {
-        const int c = gsc[(r + 1) * a.epr] - gsc[r * a.epr];
-        a.recv_base[r] = gsc[r * a.epr];
-        a.recv_count[r] = c;
-        a.token_per_rank[r] = c;
-      }
-      if (tid == 0 && a.bad_count != nullptr) *a.bad_count = tot[E];
-    }
-  } else if (kRowDuringCount) {
+  } else if (kRowDuringCount && t_first < t_end) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // nothing in flight here: free
-    load_row<kVpl>(v, a.x, t_pre, a.hidden, lane);
+    load_row<kVpl>(v, a.x, t_first, a.hidden, lane);
   }
-  // The row waves wait for every counting wave to pass the last sync point.
-  if (!counter) {
-    while (__hip_atomic_load(&sync_ctr[kSyncs - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < kCountWaves) {
-      __builtin_amdgcn_s_sleep(1);
+  // The row waves are here at the latest when their rows' loads have
+  // issued; the counting waves once the slots are ranked.
+  __syncthreads();
+  if (group == 0 && counter) {
+    for (int e = tid; e < E; e += kCountThreads) {
+      const int first = (e / a.epr) * a.epr;
+      a.token_per_expert[e] = tot[e];
+      a.recv_token_per_expert[e] = tot[e];
+      a.put_offset[e] = gsc[e] - gsc[first];
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    for (int r = tid; r < a.ranks; r += kCountThreads) {
+      const int c = gsc[(r + 1) * a.epr] - gsc[r * a.epr];
+      a.recv_base[r] = gsc[r * a.epr];
+      a.recv_count[r] = c;
+      a.token_per_rank[r] = c;
+    }
+    if (tid == 0 && a.bad_count != nullptr) *a.bad_count = tot[E];
   }
 
   // 5. Dispatch of this group's tokens: wave w takes tokens w, w + 16, ...
