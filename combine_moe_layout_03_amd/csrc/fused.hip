@@ -142,7 +142,10 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
     atomicAdd(hpre + (i < e_begin ? hist_pre : hist_tot) + bin, 1);
   };
   int4 quads[kQuads];
+  // A wave whose first group of the round is past the last loads nothing
+  // (its later groups are further on).
   auto load_round = [&](int q0) {
+    if (q0 + wave * kWave >= nq) return;
     if (a.ids_aligned16) {
       const int4* src = reinterpret_cast<const int4*>(a.topk_idx);
 #pragma unroll
@@ -156,6 +159,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
     }
   };
   auto count_round = [&](int q0) {
+    if (q0 + wave * kWave >= nq) return;
 #pragma unroll
     for (int u = 0; u < kQuads; ++u) {
       const int q = q0 + u * kCountThreads + tid;
