@@ -31,17 +31,19 @@
 //      8 copies it costs what a uniform batch does.  The copies are summed
 //      afterwards.
 //   3. An exclusive scan of the totals in LDS is the notify stage: the
-//      receive row of (expert e, slot s) is scan[e] + s.  Workgroup 0 writes
-//      the layout and notify outputs.
+//      receive row of (expert e, slot s) is scan[e] + s.  The first
+//      ceil(E / 64) counting waves (one expert per lane; up to 4 when
+//      E > 512) scan; the other counting waves load their rows instead, as
+//      the row waves did.  Workgroup 0 writes the layout and notify outputs.
 //   4. Wave 0 ranks the workgroup's own entries in entry order: match-any
 //      ballots group equal ids, and the group leader adds the group's size
 //      to the expert's running count (seeded with the counts before the
 //      workgroup), so each entry's slot is its stable rank within its
 //      expert.  The slots go to LDS and to sendTokenIdx.
-//   The counting waves synchronise steps 2-4 among themselves through LDS
-//   counters; the one workgroup barrier after step 4 lets the row waves on.
+//   The counting waves synchronise steps 2-3 among themselves through LDS
+//   counters; a workgroup barrier after step 4 lets every wave on.
 //   5. Each wave quantises (or passes through) its tokens and writes every
-//      copy, as the dispatch kernel does; the counting waves load their rows
+//      copy, as the dispatch kernel does; the scanning waves load their rows
 //      here.
 // The ids are read once per workgroup from L2 (bs*k*4 bytes each); with one
 // workgroup per CU that is the only redundant work.
@@ -63,11 +65,13 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kCountWaves = kWaves / 2;  // waves that count the ids
 constexpr int kCountThreads = kCountWaves * kWave;
 constexpr int kQuads = 16;  // groups of four ids per counting thread and round
-constexpr int kSyncs = 2;   // sync points of the counting waves
+constexpr int kSyncs = 2;   // sync points of the counting waves: ids counted, scan sums
 constexpr int kMaxCopies = 1 << kFusedMaxCopiesLog2;
 constexpr int kMaxIdBits = 11;  // bits of an expert id (E <= 2048)
 static_assert(MOE_MAX_EXPERTS <= (1 << kMaxIdBits), "expert ids fit in kMaxIdBits bits");
-constexpr int kMaxPer = (MOE_MAX_EXPERTS + kCountThreads - 1) / kCountThreads;  // experts per counting thread
+constexpr int kMaxPer = 4;  // experts per scanning lane (at E = 2048)
+constexpr int kScanExpertsPerWave = kMaxPer * kWave;
+static_assert(MOE_MAX_EXPERTS <= kScanExpertsPerWave * kCountWaves, "the counting waves can scan every expert");
 // s_waitcnt vmcnt(0) with expcnt and lgkmcnt at their maxima.  The compiler
 // places its waits for loads per register, merging the two paths below as
 // if either could have run: the ids' registers look in flight on the row
@@ -171,12 +175,15 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
       }
     }
   };
-  // Arrival of every counting wave at sync point p: LDS writes before it
-  // are seen by every counting wave after it.
-  auto counters_sync = [&](int p) {
+  // Sync point p among some of the counting waves: each arrives once (its
+  // LDS writes before the arrival are seen after the wait), and a waiting
+  // wave goes on once `count` waves have arrived.
+  auto counters_arrive = [&](int p) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     if (lane == 0) __hip_atomic_fetch_add(&sync_ctr[p], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    while (__hip_atomic_load(&sync_ctr[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < kCountWaves) {
+  };
+  auto counters_wait = [&](int p, int count) {
+    while (__hip_atomic_load(&sync_ctr[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < count) {
       __builtin_amdgcn_s_sleep(1);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -200,7 +207,11 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   // kernel's register budget covers both kinds of wave) and is loaded after
   // the barrier.
   constexpr bool kRowDuringCount = kVpl <= 14;
-  const bool have_row = kRowDuringCount && !counter;
+  // Waves 0 .. scan_waves - 1 scan (one expert per lane, at most 4 when
+  // E > 512) and wave 0 ranks; every other wave loads its row early.
+  const int scan_waves = min(kCountWaves, (E + kWave - 1) / kWave);
+  const bool scanner = wave < scan_waves;
+  const bool have_row = kRowDuringCount && !scanner;
   if (counter) {
     if (nq > 0) count_round(0);
     for (int q0 = kRound; q0 < nq; q0 += kRound) {
@@ -212,13 +223,17 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
     if (own_first) ids_l[tid] = own_id;
     for (int li = tid + kCountThreads; li < own; li += kCountThreads) ids_l[li] = a.topk_idx[e_begin + li];
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // ids that no lane used
-    counters_sync(0);
+    counters_arrive(0);
+  }
+  if (scanner) {
+    counters_wait(0, kCountWaves);
 
-    // 3. Totals and their exclusive scan (notify).  Counting thread c owns
+    // 3. Totals and their exclusive scan (notify).  Scanning thread c owns
     //    the contiguous experts [c * per, (c + 1) * per), per <= kMaxPer,
-    //    sums their histogram copies and scans; the last thread also sums
-    //    the invalid-id bin E.
-    const int per = (E + kCountThreads - 1) / kCountThreads;
+    //    sums their histogram copies and scans; the last scanning thread
+    //    also sums the invalid-id bin E.
+    const int scan_threads = scan_waves * kWave;
+    const int per = (E + scan_threads - 1) / scan_threads;  // <= kMaxPer
     const int e0 = tid * per;
     int cnt[kMaxPer];
     int sum = 0;
@@ -240,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
         sum += cnt[q];
       }
     }
-    if (tid == kCountThreads - 1) {
+    if (tid == scan_threads - 1) {
       int sp = 0, st = 0;
 #pragma unroll
       for (int c = 0; c < kMaxCopies; ++c) {
@@ -252,10 +267,20 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
       tot[E] = sp + st;
     }
     const int incl = wave_inclusive_scan(sum);
-    if (lane == kWave - 1) wave_sum[wave] = incl;
-    counters_sync(1);
     int off = 0;
-    for (int w = 0; w < wave; ++w) off += wave_sum[w];
+    int total = incl;  // one scanning wave: its last lane's sum
+    if (scan_waves > 1) {
+      if (lane == kWave - 1) wave_sum[wave] = incl;
+      counters_arrive(1);
+      counters_wait(1, scan_waves);
+      total = 0;
+      for (int w = 0; w < scan_waves; ++w) {
+        if (w < wave) off += wave_sum[w];
+        total += wave_sum[w];
+      }
+    } else {
+      total = __builtin_amdgcn_readlane(incl, kWave - 1);
+    }
     int excl = off + incl - sum;
 #pragma unroll
     for (int q = 0; q < kMaxPer; ++q) {
@@ -266,11 +291,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
         excl += cnt[q];
       }
     }
-    if (tid == kCountThreads - 1) {
-      int total = 0;
-      for (int w = 0; w < kCountWaves; ++w) total += wave_sum[w];
-      gsc[E] = total;
-    }
+    if (tid == scan_threads - 1) gsc[E] = total;
 
     // 4. Slots of this group's own entries, in entry order, by wave 0 alone
     //    (LDS atomics of one wave complete in issue order, which keeps the
@@ -307,8 +328,11 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // nothing in flight here: free
     load_row<kVpl>(v, a.x, t_first, a.hidden, lane);
   }
-  // The row waves are here at the latest when their rows' loads have
-  // issued; the counting waves once the slots are ranked.
+  // The waves that load their rows early are here at the latest when those
+  // loads have issued; the scanning waves once the slots are ranked.  (Held
+  // at this barrier, no wave starts its stores before every early row's
+  // loads have issued: with an LDS flag instead, stores that began once the
+  // slots were ready kept some rows' loads from issuing for up to 20 us.)
   __syncthreads();
   if (group == 0 && counter) {
     for (int e = tid; e < E; e += kCountThreads) {
