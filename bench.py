@@ -48,11 +48,14 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
 GRAPH_STEPS = 10  # steps captured into one HIP graph for the graph-replay figure
 METRIC = "dispatch+combine tokens/s and HBM GB/s (% of peak) at bs=4096 h=7168 top-8"
 PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "combine_moe_layout_03_amd", "csrc")
+# A kernel's source: its own file and the headers every kernel file includes.
+KERNEL_HEADERS = [os.path.join(CSRC, f) for f in ("device_util.h", "launch.h", "quant.h")]
 KERNEL_SOURCES = {
-    "dispatch": os.path.join(ROOT, "combine_moe_layout_03_amd", "csrc", "dispatch.hip"),
-    "combine": os.path.join(ROOT, "combine_moe_layout_03_amd", "csrc", "combine.hip"),
-    "fused": os.path.join(ROOT, "combine_moe_layout_03_amd", "csrc", "fused.hip"),
-    "epilogue": os.path.join(ROOT, "combine_moe_layout_03_amd", "csrc", "epilogue.hip"),
+    "dispatch": [os.path.join(CSRC, "dispatch.hip")] + KERNEL_HEADERS,
+    "combine": [os.path.join(CSRC, "combine.hip")] + KERNEL_HEADERS,
+    "fused": [os.path.join(CSRC, "fused.hip")] + KERNEL_HEADERS,
+    "epilogue": [os.path.join(CSRC, "epilogue.hip")] + KERNEL_HEADERS,
 }
 EPILOGUE_METRIC = "expert epilogue (dequant + SwiGLU + int8 requant) rows/s and HBM GB/s (% of peak)"
 
@@ -127,9 +130,12 @@ def epilogue_bytes(rows: int, n: int) -> int:
     return rows * (8 * n + 4 + n + 4) + 8 * n
 
 
-def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def pct(values, q):
