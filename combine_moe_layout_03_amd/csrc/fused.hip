@@ -35,11 +35,12 @@
 //      ceil(E / 64) counting waves (one expert per lane; up to 4 when
 //      E > 512) scan; the other counting waves load their rows instead, as
 //      the row waves did.  Workgroup 0 writes the layout and notify outputs.
-//   4. Wave 0 ranks the workgroup's own entries in entry order: match-any
-//      ballots group equal ids, and the group leader adds the group's size
-//      to the expert's running count (seeded with the counts before the
-//      workgroup), so each entry's slot is its stable rank within its
-//      expert.  The slots go to LDS and to sendTokenIdx.
+//   4. The scanning waves rank the workgroup's own entries, rounds of 64
+//      entries in turn: an entry's slot is its expert's count before the
+//      workgroup plus the same-expert entries before it in the workgroup,
+//      counted with match-any ballots over its own round and each earlier
+//      one, so the rounds are independent (its stable rank within its
+//      expert).  The slots go to LDS and to sendTokenIdx.
 //   The counting waves synchronise steps 2-3 among themselves through LDS
 //   counters; a workgroup barrier after step 4 lets every wave on.
 //   5. Each wave quantises (or passes through) its tokens and writes every
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   // read 8-way bank-conflicted, 1.2 us at 8 copies).
   int32_t* hpre = lds;                    // [C][E + 1] copies of the counts before this group
   int32_t* htot = hpre + (E + 1) * C;     // [C][E + 1] copies of the counts from this group on
-  int32_t* pre = htot + (E + 1) * C;      // [E + 1] counts before this group; then running counts
+  int32_t* pre = htot + (E + 1) * C;      // [E + 1] counts before this group
   int32_t* tot = pre + (E + 1);           // [E + 1] counts from this group on; then totals
   int32_t* gsc = tot + (E + 1);           // [E + 1] exclusive scan of the totals (gsc[E]: all valid)
   int32_t* ids_l = gsc + (E + 1);         // [T * k] own entries' ids
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   // the barrier.
   constexpr bool kRowDuringCount = kVpl <= 14;
   // Waves 0 .. scan_waves - 1 scan (one expert per lane, at most 4 when
-  // E > 512) and wave 0 ranks; every other wave loads its row early.
+  // E > 512) and rank; every other wave loads its row early.
   const int scan_waves = min(kCountWaves, (E + kWave - 1) / kWave);
   const bool scanner = wave < scan_waves;
   const bool have_row = kRowDuringCount && !scanner;
@@ -293,35 +294,40 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
     }
     if (tid == scan_threads - 1) gsc[E] = total;
 
-    // 4. Slots of this group's own entries, in entry order, by wave 0 alone
-    //    (LDS atomics of one wave complete in issue order, which keeps the
-    //    ranks stable across rounds).
-    if (wave == 0) {
-      for (int r0 = 0; r0 < own; r0 += kWave) {
-        const int li = r0 + lane;
-        const bool in_range = li < own;
-        const int e = in_range ? ids_l[li] : -1;
-        const bool valid = in_range && static_cast<unsigned>(e) < static_cast<unsigned>(E);
-        uint64_t peers = __ballot(valid);
+    // 4. Slots of this group's own entries: entry li's slot is its expert's
+    //    count before the group (pre) plus the entries of the same expert
+    //    before it in the group.  Rounds of 64 entries go to the scanning
+    //    waves in turn (wave w: rounds w, w + scan_waves, ...), each round
+    //    on its own: match-any ballots over the round give the same-expert
+    //    lanes below, and over each earlier round the same-expert entries
+    //    there, so no round waits for another.
+    for (int r = wave; r * kWave < own; r += scan_waves) {
+      const int li = r * kWave + lane;
+      const bool in_range = li < own;
+      const int e = in_range ? ids_l[li] : -1;
+      const bool valid = in_range && static_cast<unsigned>(e) < static_cast<unsigned>(E);
+      // lanes whose entry (of round r2's ids `e2`) has this lane's expert
+      auto same_expert = [&](int e2, bool valid2) {
+        uint64_t m = __ballot(valid2);
 #pragma unroll
         for (int bit = 0; bit < kMaxIdBits; ++bit) {
           if (bit < a.id_bits) {
-            const bool on = (e >> bit) & 1;
-            const uint64_t set = __ballot(on);
-            peers &= on ? set : ~set;
+            const uint64_t set = __ballot((e2 >> bit) & 1);
+            m &= ((e >> bit) & 1) ? set : ~set;
           }
         }
-        const int below = valid ? lanes_below(peers) : 0;
-        const int leader = valid ? 63 - __builtin_clzll(peers) : lane;
-        int ret = 0;
-        if (valid && leader == lane) ret = atomicAdd(&pre[e], __popcll(peers));
-        const int start = __shfl(ret, leader, kWave);
-        if (in_range) {
-          const int slot = valid ? start + below : -1;
-          ids_l[li] = valid ? e : 0;
-          slot_l[li] = slot;
-          a.send_token_idx[e_begin + li] = slot;
-        }
+        return m;
+      };
+      int before = valid ? lanes_below(same_expert(e, valid)) : 0;
+      for (int r2 = 0; r2 < r; ++r2) {
+        const int e2 = ids_l[r2 * kWave + lane];  // an earlier round is whole
+        const uint64_t m = same_expert(e2, static_cast<unsigned>(e2) < static_cast<unsigned>(E));
+        before += valid ? __popcll(m) : 0;
+      }
+      if (in_range) {
+        const int slot = valid ? pre[e] + before : -1;
+        slot_l[li] = slot;
+        a.send_token_idx[e_begin + li] = slot;
       }
     }
   } else if (kRowDuringCount && t_first < t_end) {

@@ -48,6 +48,11 @@ FUSED_RANDOM = [
     (315, 4096, 512, 8, 256, 16, "hot", 0.0, "bf16", True),
     (316, 8192, 64, 8, 256, 16, "hot", 0.01, "bf16", True),
     (317, 2000, 24, 8, 2048, 64, "hot", 0.0, "fp16", True),
+    # three scanning waves (E = 130), and eight with two experts per lane (E = 576)
+    (318, 700, 96, 6, 130, 10, "uniform", 0.02, "bf16", True),
+    (319, 1500, 40, 4, 576, 12, "zipf1.2", 0.0, "bf16", True),
+    # 8 tokens per workgroup at h = 7168: every row loaded during the count
+    (320, 2048, 7168, 8, 256, 16, "dup", 0.0, "bf16", True),
 ]
 
 
