@@ -7,7 +7,7 @@
 // token's k receive rows.  Quantisation:
 //   amax = max |x_i|            -- taken on the 16-bit patterns with the sign
 //                                  bit cleared (magnitude order = integer
-//                                  order), reduced across the wave by shuffles
+//                                  order), reduced across the wave (DPP)
 //   s    = 127.0f / (amax + 1e-12f),  inv = 1.0f / s
 //                               -- correctly rounded binary32 divisions
 //   q_i  = rint(x_i * s)        -- one binary32 multiply, then round half to

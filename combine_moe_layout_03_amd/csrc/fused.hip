@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   int32_t* hpre = lds;                    // [C][E + 1] copies of the counts before this group
   int32_t* htot = hpre + (E + 1) * C;     // [C][E + 1] copies of the counts from this group on
   int32_t* pre = htot + (E + 1) * C;      // [E + 1] counts before this group
-  int32_t* tot = pre + (E + 1);           // [E + 1] counts from this group on; then totals
+  int32_t* tot = pre + (E + 1);           // [E + 1] totals (tot[E]: invalid ids)
   int32_t* gsc = tot + (E + 1);           // [E + 1] exclusive scan of the totals (gsc[E]: all valid)
   int32_t* ids_l = gsc + (E + 1);         // [T * k] own entries' ids
   int32_t* slot_l = ids_l + a.tokens_per_group * a.k;  // [T * k] own entries' slots (-1: dropped)
