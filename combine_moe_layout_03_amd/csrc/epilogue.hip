@@ -92,14 +92,17 @@ __global__ __launch_bounds__(kEpiThreads) void deq_swiglu_quant_kernel(EpilogueA
   const float ts = *(const MOE_GLOBAL float*)((const MOE_GLOBAL uint8_t*)(a.token_scale) + mr * a.ts_stride);
 
   // Loads of every chunk first (clamped index past the row's end: the data
-  // is loaded but not used), then the arithmetic.
+  // is loaded but not used), then the arithmetic.  The accumulators are
+  // loaded and the codes stored non-temporally (each is touched once): at
+  // 32768 rows x n 2048 that measured 102.3 us against 105.6 us with
+  // ordinary loads and stores, and 109.5 us with non-temporal loads alone.
   i32x4 cg[kIt], cu[kIt];
   f32x4 wg[kIt], wu[kIt];
 #pragma unroll
   for (int i = 0; i < kIt; ++i) {
     const int c = min(lane + (i * kW + part) * kWave, chunks - 1);
-    cg[i] = *reinterpret_cast<const MOE_GLOBAL i32x4*>(row + 4 * c);
-    cu[i] = *reinterpret_cast<const MOE_GLOBAL i32x4*>(row + a.n + 4 * c);
+    cg[i] = __builtin_nontemporal_load(reinterpret_cast<const MOE_GLOBAL i32x4*>(row + 4 * c));
+    cu[i] = __builtin_nontemporal_load(reinterpret_cast<const MOE_GLOBAL i32x4*>(row + a.n + 4 * c));
     wg[i] = *reinterpret_cast<const MOE_GLOBAL f32x4*>(ws + 4 * c);
     wu[i] = *reinterpret_cast<const MOE_GLOBAL f32x4*>(ws + a.n + 4 * c);
   }
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(kEpiThreads) void deq_swiglu_quant_kernel(EpilogueA
       const uint32_t b1 = code_bits(act[i][1], s) & 0xffu;
       const uint32_t b2 = code_bits(act[i][2], s) & 0xffu;
       const uint32_t b3 = code_bits(act[i][3], s);
-      reinterpret_cast<uint32_t*>(out)[c] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+      __builtin_nontemporal_store(b0 | (b1 << 8) | (b2 << 16) | (b3 << 24), reinterpret_cast<uint32_t*>(out) + c);
     }
   }
   if (part == 0 && lane == 0) *reinterpret_cast<float*>(out + a.scale_off) = inv;
