@@ -84,6 +84,10 @@ constexpr int kWaitVm0 = 0x0f70;
 // Row t into registers, 16 bytes (8 elements) per chunk, chunk lane + 64 i
 // in v[i].  Chunks past the row's end load its last chunk again (a duplicate
 // changes no maximum and is never stored), so every load is unconditional.
+// The loads are non-temporal (a row is read once): about 0.5-1 us faster at
+// bs 4096, h 7168 than ordinary loads.  (Non-temporal stores of the receive
+// rows were 27 us slower: the rows are scattered, and ordinary stores let
+// the Infinity Cache gather them.)
 template <int kVpl>
 __device__ __forceinline__ void load_row(uint4 (&v)[kVpl], const uint16_t* x, int t, int hidden, int lane) {
   const uint32_t last = static_cast<uint32_t>(hidden >> 3) - 1u;
@@ -91,7 +95,8 @@ __device__ __forceinline__ void load_row(uint4 (&v)[kVpl], const uint16_t* x, in
 #pragma unroll
   for (int i = 0; i < kVpl; ++i) {
     const uint32_t c = static_cast<uint32_t>(lane + i * kWave);
-    v[i] = src[c < last ? c : last];
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (c < last ? c : last)));
+    v[i] = make_uint4(w.x, w.y, w.z, w.w);
   }
 }
 
