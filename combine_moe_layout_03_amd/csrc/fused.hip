@@ -183,7 +183,9 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   };
   // Sync point p among some of the counting waves: each arrives once (its
   // LDS writes before the arrival are seen after the wait), and a waiting
-  // wave goes on once `count` waves have arrived.
+  // wave goes on once `count` waves have arrived.  Every wave a wait counts
+  // on arrives unconditionally (the kernel has no early exit, and a
+  // workgroup's waves are resident together), so each wait ends.
   auto counters_arrive = [&](int p) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     if (lane == 0) __hip_atomic_fetch_add(&sync_ctr[p], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
