@@ -100,3 +100,20 @@ def test_fused_fallback_shape_matches(seed, bs, h, k, e, r):
     log(f"fused entry point, fallback shape {bs}x{h} k={k} E={e}")
     g = GpuRun(w, True).run_all(fused=True).host()
     compare(w, True, "bf16", g, oracle_run(w, True, "bf16"))
+
+
+@pytest.mark.parametrize("seed,bs,h,k,e,r", [(340, 4096, 256, 8, 256, 16), (341, 37, 64, 3, 12, 3),
+                                             (342, 1000, 128, 6, 64, 8)],
+                         ids=["one_whole_round", "few_ids", "partial_round"])
+def test_fused_ids_not_16_byte_aligned(seed, bs, h, k, e, r):
+    """topk_idx at an address that is 4- but not 16-byte aligned: the
+    counting waves read the ids four at a time with 4-byte loads."""
+    w = W.random_case(seed, bs, h, k, e, r, routing="dup", bad_frac=0.01)
+    run = GpuRun(w, True)
+    store = torch.empty(bs * k + 1, dtype=torch.int32, device="cuda")
+    store[1:] = run.idx.reshape(-1)
+    run.idx = store[1:].view(bs, k)
+    assert run.idx.data_ptr() % 16 != 0
+    log(f"fused with unaligned ids {bs}x{h} k={k} E={e}")
+    g = run.run_all(fused=True).host()
+    compare(w, True, "bf16", g, oracle_run(w, True, "bf16"))
