@@ -25,7 +25,7 @@ first expert GEMM's int32 output, SwiGLU, requantise to int8 rows) alone, on
 every receive row of the large shape with an FFN width of 2048, and prints
 its own JSON line (rows/s).
 
-Output: one JSON line on stdout.  ``--gpus N`` with N > 1 exits: this build
+Output: one JSON line on stdout.  ``--gpus N`` with N > 1 exits: the bench
 measures one GPU.
 """
 
@@ -214,7 +214,7 @@ def main(argv=None) -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the expert-parallel ranks are logical partitions of one "
-              "device's receive buffer; multi-GPU runs are not part of this build.", file=sys.stderr)
+              "device's receive buffer; this bench does not launch multi-GPU runs.", file=sys.stderr)
         return 2
 
     import torch

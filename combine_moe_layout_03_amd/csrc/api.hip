@@ -390,7 +390,7 @@ const char* moe_status_str(int status) {
     case MOE_ERR_BAD_DTYPE: return "unsupported element type for this argument";
     case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than moe_layout_workspace_bytes()";
     case MOE_ERR_BUFFER_TOO_SMALL: return "receive buffer smaller than bs * topk rows";
-    case MOE_ERR_UNSUPPORTED: return "size not supported by this build (see MOE_MAX_* and hidden % 8)";
+    case MOE_ERR_UNSUPPORTED: return "size not supported by the library (see MOE_MAX_* and hidden % 8)";
     case MOE_ERR_HIP: return "HIP launch failed (see moe_last_hip_error)";
     default: return "unknown status";
   }

@@ -67,7 +67,7 @@ enum {
   MOE_ERR_HIP = 8
 };
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define MOE_MAX_EXPERTS 2048   /* E = R * EPR */
 #define MOE_MAX_HIDDEN 16384   /* h */
 #define MOE_MAX_TOPK 32        /* k */
