@@ -240,6 +240,23 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
     //    the contiguous experts [c * per, (c + 1) * per), per <= kMaxPer,
     //    sums their histogram copies and scans; the last scanning thread
     //    also sums the invalid-id bin E.
+    // The C copies of bin e summed: all kMaxCopies reads are issued at once
+    // (copy indices clamped to C - 1, the extra reads not added); reads
+    // guarded one by one waited for each other, about 1 us per scan.
+    auto sum_copies = [&](int e, int& sp, int& st) {
+      int vp[kMaxCopies], vt[kMaxCopies];
+#pragma unroll
+      for (int c = 0; c < kMaxCopies; ++c) {
+        const int cc = min(c, C - 1);
+        vp[c] = hpre[cc * (E + 1) + e];
+        vt[c] = htot[cc * (E + 1) + e];
+      }
+#pragma unroll
+      for (int c = 0; c < kMaxCopies; ++c) {
+        sp += c < C ? vp[c] : 0;
+        st += c < C ? vt[c] : 0;
+      }
+    };
     const int scan_threads = scan_waves * kWave;
     const int per = (E + scan_threads - 1) / scan_threads;  // <= kMaxPer
     const int e0 = tid * per;
@@ -251,13 +268,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
       const int e = e0 + q;
       if (q < per && e < E) {
         int sp = 0, st = 0;
-#pragma unroll
-        for (int c = 0; c < kMaxCopies; ++c) {
-          if (c < C) {
-            sp += hpre[c * (E + 1) + e];
-            st += htot[c * (E + 1) + e];
-          }
-        }
+        sum_copies(e, sp, st);
         pre[e] = sp;
         cnt[q] = sp + st;
         sum += cnt[q];
@@ -265,13 +276,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
     }
     if (tid == scan_threads - 1) {
       int sp = 0, st = 0;
-#pragma unroll
-      for (int c = 0; c < kMaxCopies; ++c) {
-        if (c < C) {
-          sp += hpre[c * (E + 1) + E];
-          st += htot[c * (E + 1) + E];
-        }
-      }
+      sum_copies(E, sp, st);
       tot[E] = sp + st;
     }
     const int incl = wave_inclusive_scan(sum);
@@ -282,9 +287,13 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
       counters_arrive(1);
       counters_wait(1, scan_waves);
       total = 0;
-      for (int w = 0; w < scan_waves; ++w) {
-        if (w < wave) off += wave_sum[w];
-        total += wave_sum[w];
+      int ws[kCountWaves];  // all reads at once, as in sum_copies
+#pragma unroll
+      for (int w = 0; w < kCountWaves; ++w) ws[w] = wave_sum[min(w, scan_waves - 1)];
+#pragma unroll
+      for (int w = 0; w < kCountWaves; ++w) {
+        off += w < wave ? ws[w] : 0;
+        total += w < scan_waves ? ws[w] : 0;
       }
     } else {
       total = __builtin_amdgcn_readlane(incl, kWave - 1);
