@@ -183,7 +183,7 @@ def cpu_baseline(w, quant: bool, budget_s: float):
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large", choices=["tiny", "small", "mid", "large", "stress"])
     ap.add_argument("--mode", default="int8", choices=["int8", "pass"])
