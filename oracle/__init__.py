@@ -4,8 +4,8 @@ TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
 benchmark's CPU-baseline leg, never by the product library.  Every function
 forwards host arrays to the single-threaded C oracle, which computes the
 method's plain definition (the header of moe_oracle.c names the passages of
-"UMDK/CAM communication acceleration library deep analysis v2", section 2, it
-follows and the readings it takes).
+"UMDK/CAM communication acceleration library deep analysis v2", sections 2 and
+4, it follows and the readings it takes).
 
 Receive buffers are returned in canonical form: passthrough rows as uint16
 patterns ``[rows, h]``; quantised rows as int8 codes ``[rows, h]`` plus the
@@ -50,6 +50,7 @@ _SIGS = {
     "oracle_exp_f32": [_P, _P, _I64],
     "oracle_swiglu_quant_row": [_P, _I64, _P, ctypes.c_float, _P, _P, _P],
     "oracle_swiglu_quant": [_P, _I64, _I64, _P, _P, _I64, _P, _P],
+    "oracle_grouped_gemm_i8": [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _P],
 }
 
 
@@ -211,6 +212,30 @@ class Oracle:
         _check(self.L.oracle_swiglu_quant(_ptr(a), rows, n, _ptr(ws), _ptr(ts), 1, _ptr(codes),
                                           _ptr(inv)), "swiglu_quant")
         return dict(codes=codes, inv=inv)
+
+    def grouped_gemm_i8(self, a: np.ndarray, k: int, group_count: np.ndarray, w: np.ndarray,
+                        rows: Optional[np.ndarray] = None):
+        """First expert matmul: a int8 [R, stride] receive rows (codes in the
+        first k bytes of each row), group_count int32 [G], w int8 [G, n, k].
+        Returns (out int32 [len(rows), n], row_group int32 [len(rows)]) for
+        the listed rows (all R rows when ``rows`` is None); a row that no
+        expert owns gets group -1 and an all-zero out row."""
+        a8 = np.ascontiguousarray(a).view(np.int8)
+        if a8.ndim != 2 or a8.shape[1] < k:
+            raise ValueError("a: [rows, stride >= k]")
+        gc = np.ascontiguousarray(group_count, dtype=np.int32).reshape(-1)
+        w8 = np.ascontiguousarray(w).view(np.int8)
+        if w8.ndim != 3 or w8.shape[0] != gc.size or w8.shape[2] != k:
+            raise ValueError("w: [groups, n, k]")
+        n = w8.shape[1]
+        lst = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+        nl = a8.shape[0] if lst is None else lst.size
+        out = np.zeros((nl, n), np.int32)
+        grp = np.zeros(nl, np.int32)
+        _check(self.L.oracle_grouped_gemm_i8(_ptr(a8), a8.shape[1], a8.shape[0], k, _ptr(gc), gc.size,
+                                             _ptr(w8), n, _ptr(lst), nl, _ptr(out), _ptr(grp)),
+               "grouped_gemm_i8")
+        return out, grp
 
     def dispatch(self, x_bits: np.ndarray, x_kind: str, topk_idx: np.ndarray,
                  send_token_idx: np.ndarray, put_offset: np.ndarray, recv_base: np.ndarray,
@@ -393,3 +418,7 @@ def swiglu_quant_row(*a, **kw):
 
 def swiglu_quant(*a, **kw):
     return default().swiglu_quant(*a, **kw)
+
+
+def grouped_gemm_i8(*a, **kw):
+    return default().grouped_gemm_i8(*a, **kw)

@@ -18,9 +18,10 @@
  *   2.5  moe_dispatch_normal_zb / QuantProcess (row scatter, dynamic int8),
  *   2.6  moe_combine_normal_zb / ReadBufferAndWeightedSum (weighted gather),
  *   2.8  the per-rank zero-buffer layout (token region read by combine).
- * and, for the expert-side epilogue between dispatch and combine, section 4
- * "Fused Deep MoE": 4.3 (stage 2, DeqSwigluQuant) and 4.8.1 (the GMM1
- * epilogue PerTokenDequantSwiGLU).
+ * and, for the expert side between dispatch and combine, section 4
+ * "Fused Deep MoE": 4.3 (stage 2: GMM1, int8 x int8 -> int32, then
+ * DeqSwigluQuant), 4.6 (the per-expert cumulative token counts, gmGroupList)
+ * and 4.8.1 (the GMM1 epilogue PerTokenDequantSwiGLU).
  *
  * Everything here is the plain definition, in the order the page gives,
  * single-threaded, in IEEE binary32 where the page fixes float (the quantiser
@@ -46,7 +47,11 @@
  *    half of the accumulator row (the page shows x*sigmoid(x) on the left
  *    half and the right half passed through, but not the product), and its
  *    output row is quantised like a dispatched row; e^x is computed by a
- *    named published method, written out (exp_cw).
+ *    named published method, written out (exp_cw);
+ *  - the first expert matmul (GMM1) gives expert g the rows [S_g, S_g + c_g)
+ *    of the receive buffer, S_g the sum of the counts before g (a negative
+ *    count counts as 0), takes its weights as [groups][n][k] (one k-vector
+ *    per output column) and sums the int8 products exactly into int32.
  *
  * Parity pins live in tests/ (brute force, stable-sort and prefix-sum
  * equivalence, hand-worked quantiser rows, order-sensitive combine rows,
@@ -538,6 +543,55 @@ int oracle_swiglu_quant(const int32_t *acc, int64_t rows, int64_t n, const float
     int rc = oracle_swiglu_quant_row(acc + m * 2 * n, n, weight_scale, token_scale[m * ts_stride],
                                      codes + m * n, &inv[m], NULL);
     if (rc) return rc;
+  }
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* First expert matmul (GMM1): section 4.3, stage 2 -- the dispatched int8    */
+/* rows times each expert's int8 weights, accumulated in int32 -- with the    */
+/* experts' row ranges given by per-expert token counts (section 4.6,         */
+/* gmGroupList holds their running sums).                                     */
+/* ------------------------------------------------------------------------ */
+
+/* Row m of the receive buffer is a[m * a_stride .. + k) (int8 codes); the
+ * weights of expert g are w[(g * n + j) * k + i] for output column j.
+ * Expert g owns rows [S_g, S_g + c_g), c_g = max(group_count[g], 0) and S_g
+ * the sum of c over the experts before g.  For the rows listed in row_list
+ * (all rows 0 .. rows-1 in order when row_list is NULL; then nlist = rows):
+ *   out[q][j] = sum over i of a[m][i] * w[g][j][i]   (exact, in int64)
+ * and row_group[q] = g; a row that no expert owns gets row_group -1 and its
+ * out row is left as it is.  A sum outside int32 is an error (it cannot
+ * happen for k <= 2^17). */
+int oracle_grouped_gemm_i8(const int8_t *a, int64_t a_stride, int64_t rows, int64_t k,
+                           const int32_t *group_count, int64_t groups, const int8_t *w,
+                           int64_t n, const int64_t *row_list, int64_t nlist, int32_t *out,
+                           int32_t *row_group) {
+  if (rows < 0 || k < 1 || n < 1 || groups < 1 || a_stride < k || nlist < 0) return ORACLE_BAD_ARG;
+  if (!row_list && nlist != rows) return ORACLE_BAD_ARG;
+  if (nlist == 0) return ORACLE_OK;
+  if (!a || !group_count || !w || !out || !row_group) return ORACLE_BAD_ARG;
+  for (int64_t q = 0; q < nlist; ++q) {
+    int64_t m = row_list ? row_list[q] : q;
+    if (m < 0 || m >= rows) return ORACLE_BAD_ARG;
+    int64_t owner = -1, start = 0;
+    for (int64_t g = 0; g < groups; ++g) {
+      int64_t c = group_count[g] > 0 ? group_count[g] : 0;
+      if (m >= start && m < start + c) {
+        owner = g;
+        break;
+      }
+      start += c;
+    }
+    row_group[q] = (int32_t)owner;
+    if (owner < 0) continue;
+    for (int64_t j = 0; j < n; ++j) {
+      int64_t acc = 0;
+      for (int64_t i = 0; i < k; ++i)
+        acc += (int64_t)a[m * a_stride + i] * (int64_t)w[(owner * n + j) * k + i];
+      if (acc > INT32_MAX || acc < INT32_MIN) return ORACLE_INTERNAL;
+      out[q * n + j] = (int32_t)acc;
+    }
   }
   return ORACLE_OK;
 }

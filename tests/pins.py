@@ -11,7 +11,9 @@ builds and expect a failure.  The pins are:
 * the hand-worked rows in tests/golden/ (quantiser ties, scale values,
   order-sensitive combine sums, output rounding);
 * exact rational arithmetic for the quantiser's scale, inverse and codes, and
-  float64 error bounds for the combine sums.
+  float64 error bounds for the combine sums;
+* for the first expert matmul, numpy's int64 matrix product per expert,
+  closed forms of constant and extreme operands, and column-picking weights.
 """
 
 from __future__ import annotations
@@ -23,6 +25,8 @@ from fractions import Fraction
 from typing import Dict, Tuple
 
 import numpy as np
+
+import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -578,7 +582,6 @@ def check_combine_random_rows(orc, seed: int = 5) -> None:
     """Combine over receive rows that differ per (token, k) entry, so a
     permuted weight, a dropped or repeated term, or a wrong row address
     moves the result far outside the float64 bound."""
-    import workloads as W
 
     for kind in ("bf16", "int8"):
         w = W.random_case(seed, 37, 24, 6, 12, 3, routing="dup", bad_frac=0.05)
@@ -721,3 +724,84 @@ def check_swiglu_dequant_exact(orc, seed: int = 9, n: int = 64) -> None:
             assert f32_bits(act[i]) == f32_bits(np.float32(float(a))), (trial, i)
         exp_codes, exp_inv = quant_f32_expected(act)
         assert np.array_equal(codes, exp_codes) and f32_bits(inv) == f32_bits(exp_inv), trial
+
+
+# --------------------------------------------------------------------------
+# first expert matmul (GMM1: int8 x int8 -> int32 over per-expert row ranges)
+# --------------------------------------------------------------------------
+
+def gemm_owners(counts, rows: int) -> np.ndarray:
+    """Owner of each row: expert g holds the next max(c_g, 0) rows, in
+    expert order; rows past the experts' total belong to nobody (-1)."""
+    owner = np.full(rows, -1, np.int64)
+    start = 0
+    for g, c in enumerate(np.asarray(counts, dtype=np.int64)):
+        c = max(int(c), 0)
+        owner[start:min(start + c, rows)] = g
+        start += c
+    return owner
+
+
+def check_gemm_per_expert_matmul(orc, seed: int = 3) -> None:
+    """Each expert's rows equal numpy's int64 product of those rows with the
+    transposed weights of that expert; rows of no expert are left alone.
+    Rows are read at a stride larger than k (padding bytes are random)."""
+    c = W.gemm_case(seed, rows=45, k=80, n=24, groups=5, stride=112,
+                    counts=[7, 0, 13, 1, 16])
+    out, grp = orc.grouped_gemm_i8(c.a, c.k, c.group_count, c.w)
+    owner = gemm_owners(c.group_count, c.rows)
+    assert np.array_equal(grp, owner)
+    start = 0
+    for g, cnt in enumerate(c.group_count):
+        ref = c.a[start:start + cnt, :c.k].astype(np.int64) @ c.w[g].astype(np.int64).T
+        assert np.array_equal(out[start:start + cnt].astype(np.int64), ref), g
+        start += int(cnt)
+    assert not out[start:].any()
+
+
+def check_gemm_closed_forms(orc) -> None:
+    """Constant operands: all-ones rows against weights g+1 give k*(g+1);
+    the int8 extremes at k = 8192 give 8192 * (-128)^2 = 2^27 and
+    8192 * 127 * (-128) = -133169152, both exact."""
+    k, n = 40, 16
+    a = np.ones((9, k), np.int8)
+    w = np.stack([np.full((n, k), g + 1, np.int8) for g in range(3)])
+    out, grp = orc.grouped_gemm_i8(a, k, np.array([2, 3, 4], np.int32), w)
+    assert np.array_equal(out, (k * (grp[:, None] + 1)) * np.ones((1, n), np.int64))
+    k = 8192
+    a = np.full((2, k), -128, np.int8)
+    a[1] = 127
+    w = np.full((1, 16, k), -128, np.int8)
+    out, _ = orc.grouped_gemm_i8(a, k, np.array([2], np.int32), w)
+    assert (out[0] == 2 ** 27).all() and (out[1] == -133169152).all()
+
+
+def check_gemm_permutation(orc, seed: int = 4) -> None:
+    """Weights that pick one input column per output column: w[g][j][i] = 1
+    exactly when i = p_g(j), so out[m][j] = a[m][p_g(j)].  With k != n and
+    permutations that are not their own inverses, a transposed weight read
+    or a swapped operand gives other columns."""
+    k, n, rows = 48, 32, 12
+    a = W.gemm_case(seed, rows=rows, k=k, n=1, groups=1).a
+    perms = [(np.arange(n) * 5 + g * 7 + 3) % k for g in range(3)]
+    w = np.zeros((3, n, k), np.int8)
+    for g, p in enumerate(perms):
+        w[g, np.arange(n), p] = 1
+    counts = np.array([5, 4, 3], np.int32)
+    out, grp = orc.grouped_gemm_i8(a, k, counts, w)
+    for m in range(rows):
+        assert np.array_equal(out[m], a[m, perms[grp[m]]].astype(np.int32)), m
+
+
+def check_gemm_ownership(orc, seed: int = 5) -> None:
+    """Negative counts own no rows, empty experts are skipped, rows past the
+    total belong to nobody, and a row list returns the same rows as the full
+    call."""
+    c = W.gemm_case(seed, rows=20, k=16, n=16, groups=4, counts=[-3, 6, 0, 9])
+    out, grp = orc.grouped_gemm_i8(c.a, c.k, c.group_count, c.w)
+    assert np.array_equal(grp, [1] * 6 + [3] * 9 + [-1] * 5)
+    ref3 = c.a[6:15].astype(np.int64) @ c.w[3].astype(np.int64).T
+    assert np.array_equal(out[6:15], ref3)
+    sel = np.array([19, 0, 7, 14, 5])
+    out_s, grp_s = orc.grouped_gemm_i8(c.a, c.k, c.group_count, c.w, rows=sel)
+    assert np.array_equal(grp_s, grp[sel]) and np.array_equal(out_s, out[sel])

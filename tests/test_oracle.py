@@ -223,3 +223,19 @@ def test_swiglu_rows_equal_row_by_row(orc):
         assert pins.f32_bits(got["inv"][m]) == pins.f32_bits(inv)
     empty = orc.swiglu_quant(np.zeros((0, 2 * n), np.int32), ws, np.zeros(0, np.float32))
     assert empty["codes"].shape == (0, n)
+
+
+def test_gemm_per_expert_matmul(orc):
+    pins.check_gemm_per_expert_matmul(orc)
+
+
+def test_gemm_closed_forms(orc):
+    pins.check_gemm_closed_forms(orc)
+
+
+def test_gemm_column_picking_weights(orc):
+    pins.check_gemm_permutation(orc)
+
+
+def test_gemm_row_ownership(orc):
+    pins.check_gemm_ownership(orc)

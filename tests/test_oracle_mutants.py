@@ -97,6 +97,20 @@ MUTANTS = {
                              "swiglu_dequant"),
     # epilogue: the scale stored instead of its inverse
     "swiglu_store_scale": ("inv[0] = 1.0f / s;", "inv[0] = s;", "swiglu"),
+    # first expert matmul: weights read as [groups][k][n]
+    "gemm_weights_transposed": ("(int64_t)w[(owner * n + j) * k + i]",
+                                "(int64_t)w[(owner * k + i) * n + j]", "gemm"),
+    # first expert matmul: a row past an expert's end still counted as its
+    "gemm_group_end_inclusive": ("if (m >= start && m < start + c) {",
+                                 "if (m >= start && m <= start + c) {", "gemm"),
+    # first expert matmul: negative counts not clamped
+    "gemm_negative_count": ("int64_t c = group_count[g] > 0 ? group_count[g] : 0;",
+                            "int64_t c = group_count[g];", "gemm"),
+    # first expert matmul: the last product dropped
+    "gemm_drop_last_k": ("for (int64_t i = 0; i < k; ++i)\n        acc += (int64_t)a",
+                         "for (int64_t i = 0; i + 1 < k; ++i)\n        acc += (int64_t)a", "gemm"),
+    # first expert matmul: rows read densely instead of at the row stride
+    "gemm_dense_rows": ("(int64_t)a[m * a_stride + i]", "(int64_t)a[m * k + i]", "gemm"),
     # exp: Taylor series cut at degree 6
     "exp_degree6": ("float p = 1.0f / 5040.0f;\n  p = p * r + 1.0f / 720.0f;",
                     "float p = 1.0f / 720.0f;", "exp"),
@@ -197,6 +211,11 @@ def _run_pin(orc, which):
         pins.check_swiglu_dequant_exact(orc)
     elif which == "exp":
         pins.check_exp(orc)
+    elif which == "gemm":
+        pins.check_gemm_per_expert_matmul(orc)
+        pins.check_gemm_closed_forms(orc)
+        pins.check_gemm_permutation(orc)
+        pins.check_gemm_ownership(orc)
     elif which == "conversions":
         pins.check_conversions(orc)
     else:
