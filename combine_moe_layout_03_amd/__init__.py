@@ -28,12 +28,14 @@ __all__ = [
     "moe_dispatch", "moe_combine", "moe_status_str", "moe_last_hip_error", "EpBuffers",
     "dtype_code", "moe_fused_supported", "moe_layout_notify_dispatch", "moe_notify_multi",
     "moe_dispatch_src", "moe_combine_src", "EpMultiBuffers", "MOE_MAX_SOURCES",
-    "moe_deq_swiglu_quant", "token_scales_of", "MOE_EPILOGUE_MAX_N",
+    "moe_deq_swiglu_quant", "token_scales_of", "MOE_EPILOGUE_MAX_N", "moe_grouped_gemm_i8",
+    "MOE_GEMM_MAX_K", "MOE_GEMM_MAX_N", "MOE_GEMM_MAX_GROUPS",
 ]
 
 MOE_BF16, MOE_FP16, MOE_FP32, MOE_INT8_ROWSCALE = 0, 1, 2, 3
 MOE_MAX_EXPERTS, MOE_MAX_HIDDEN, MOE_MAX_TOPK, MOE_MAX_SOURCES = 2048, 16384, 32, 384
 MOE_EPILOGUE_MAX_N = 4096
+MOE_GEMM_MAX_K = MOE_GEMM_MAX_N = MOE_GEMM_MAX_GROUPS = 65536
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_ep.so")
 
@@ -61,6 +63,7 @@ _SIGS = {
     "moe_layout_notify_dispatch": ([_P, _INT, _I32, _I32, _I32, _P, _I32, _I32, _INT, _P, _P, _P, _P, _P, _P,
                                     _P, _P, _P, _SZ, _P, _SZ, _P], _INT),
     "moe_deq_swiglu_quant": ([_P, _I32, _I32, _P, _P, ctypes.c_int64, _P, _SZ, _P], _INT),
+    "moe_grouped_gemm_i8": ([_P, ctypes.c_int64, _I32, _I32, _P, _I32, _P, _I32, _P, _SZ, _P], _INT),
     "moe_status_str": ([_INT], ctypes.c_char_p),
     "moe_last_hip_error": ([], _INT),
 }
@@ -310,6 +313,30 @@ def moe_deq_swiglu_quant(acc: torch.Tensor, weight_scale: torch.Tensor, token_sc
     _check("moe_deq_swiglu_quant", _lib.moe_deq_swiglu_quant(
         _dev(acc, "acc", torch.int32), n_rows, n, _dev(weight_scale, "weight_scale", torch.float32),
         token_scale.data_ptr(), token_scale_stride, _dev(out, "out"), out.numel() * out.element_size(),
+        _stream(stream)))
+
+
+def moe_grouped_gemm_i8(a: torch.Tensor, a_row_bytes: int, rows: int, k: int,
+                        group_count: torch.Tensor, w: torch.Tensor, out: torch.Tensor,
+                        stream=None) -> None:
+    """First expert matmul: ``a`` is a device byte buffer (uint8 or int8,
+    e.g. the int8 receive buffer) whose row m starts at byte m * a_row_bytes
+    and holds k int8 codes; group_count int32 [groups] (device) gives each
+    expert's rows in order; w int8 [groups, n, k]; out int32 [rows, n] gets
+    out[m][j] = sum_i a[m][i] * w[g][j][i] for the rows of expert g (rows of
+    no expert are not written)."""
+    if w.dim() != 3 or w.shape[2] != k or w.dtype not in (torch.int8, torch.uint8):
+        raise ValueError("w must be int8 [groups, n, k]")
+    groups, n = w.shape[0], w.shape[1]
+    if group_count.numel() != groups:
+        raise ValueError("group_count must hold one count per group")
+    if a.dtype not in (torch.int8, torch.uint8):
+        raise ValueError("a must be a byte buffer")
+    if rows > 0 and a.numel() < (rows - 1) * a_row_bytes + k:
+        raise ValueError("a is smaller than (rows - 1) * a_row_bytes + k bytes")
+    _check("moe_grouped_gemm_i8", _lib.moe_grouped_gemm_i8(
+        _dev(a, "a"), a_row_bytes, rows, k, _dev(group_count, "group_count", torch.int32), groups,
+        _dev(w, "w"), n, _dev(out, "out", torch.int32), out.numel() * out.element_size(),
         _stream(stream)))
 
 

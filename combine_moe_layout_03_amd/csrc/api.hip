@@ -381,6 +381,32 @@ int moe_deq_swiglu_quant(const int32_t* acc, int32_t rows, int32_t n, const floa
   return hip_status(moe::launch_deq_swiglu_quant(a, static_cast<hipStream_t>(stream)));
 }
 
+int moe_grouped_gemm_i8(const void* a, int64_t a_row_bytes, int32_t rows, int32_t k,
+                        const int32_t* group_count, int32_t groups, const void* w, int32_t n,
+                        int32_t* out, size_t out_bytes, void* stream) {
+  if (rows < 0 || k < 1 || n < 1 || groups < 1 || a_row_bytes < k) return MOE_ERR_BAD_SHAPE;
+  if (k % 16 != 0 || k > MOE_GEMM_MAX_K || n > MOE_GEMM_MAX_N || groups > MOE_GEMM_MAX_GROUPS)
+    return MOE_ERR_UNSUPPORTED;
+  if (a_row_bytes % 16 != 0) return MOE_ERR_BAD_ALIGN;
+  if (rows == 0) return MOE_OK;
+  if (!a || !group_count || !w || !out) return MOE_ERR_NULL_PTR;
+  if (!aligned(a, 16) || !aligned(w, 16) || !aligned(group_count, 4) || !aligned(out, 4))
+    return MOE_ERR_BAD_ALIGN;
+  if (out_bytes / 4u / static_cast<size_t>(n) < static_cast<size_t>(rows)) return MOE_ERR_BUFFER_TOO_SMALL;
+  if (moe::grouped_gemm_blocks(rows, groups, n) > moe::kGemmMaxBlocks) return MOE_ERR_UNSUPPORTED;
+  moe::GemmArgs g{};
+  g.a = static_cast<const int8_t*>(a);
+  g.a_stride = a_row_bytes;
+  g.rows = rows;
+  g.k = k;
+  g.group_count = group_count;
+  g.groups = groups;
+  g.w = static_cast<const int8_t*>(w);
+  g.n = n;
+  g.out = out;
+  return hip_status(moe::launch_grouped_gemm_i8(g, static_cast<hipStream_t>(stream)));
+}
+
 const char* moe_status_str(int status) {
   switch (status) {
     case MOE_OK: return "ok";

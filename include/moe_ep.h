@@ -74,6 +74,9 @@ enum {
 #define MOE_MAX_SOURCES 384    /* source ranks sharing one receive buffer (the
                                   page's CAM_MAX_RANK_SIZE) */
 #define MOE_EPILOGUE_MAX_N 4096 /* n, the epilogue's output columns (2n inputs) */
+#define MOE_GEMM_MAX_K 65536    /* k of the first expert matmul: sums stay below 2^31 */
+#define MOE_GEMM_MAX_N 65536    /* n of the first expert matmul */
+#define MOE_GEMM_MAX_GROUPS 65536 /* experts of one first-expert-matmul call */
 
 /* Bytes of one receive-buffer row for hidden size `hidden` and receive type
  * `recv` (page 2.5 and 2.2.1):
@@ -242,7 +245,6 @@ int moe_layout_notify_dispatch(const void* x, moe_dtype xType, int32_t bs, int32
                                int32_t* recvTokenPerExpert, void* recvX, size_t recvXBytes,
                                void* workspace, size_t workspaceBytes, void* stream);
 
-/* Text for a status code (static storage). */
 /* Expert-side epilogue between dispatch and combine: dequantise the int32
  * output of the first expert GEMM, SwiGLU, and requantise to int8 -- page
  * section 4.3 (Fused Deep MoE, stage 2 "DeqSwigluQuant") and section 4.8.1
@@ -278,6 +280,38 @@ int moe_deq_swiglu_quant(const int32_t* acc, int32_t rows, int32_t n, const floa
                          const void* tokenScale, int64_t tokenScaleStride, void* out, size_t outBytes,
                          void* stream);
 
+/* First expert matmul (GMM1) of the expert side: the dispatched int8 rows
+ * times each expert's int8 weights, summed exactly in int32 -- page section
+ * 4.3 (Fused Deep MoE, stage 2: "GMM1 (INT8 x INT8 -> INT32)") with the
+ * experts' row ranges given by per-expert token counts (section 4.6, the
+ * cumulative counts gmGroupList).  Its output is moe_deq_swiglu_quant's acc.
+ *
+ * a          device, 16-byte aligned: row m at a + m * aRowBytes holds k int8
+ *            codes in its first k bytes (the rest of the row is not read).
+ *            The int8 receive buffer is used in place with aRowBytes =
+ *            moe_recv_row_bytes(k, MOE_INT8_ROWSCALE).  It must hold
+ *            (rows - 1) * aRowBytes + k bytes.
+ * groupCount [groups] int32, device, 4-byte aligned: expert g owns rows
+ *            [S_g, S_g + c_g) with c_g = max(groupCount[g], 0) and S_g the
+ *            sum of c over the experts before g; rows at or past `rows` are
+ *            owned by nobody.  moe_notify's recvTokenPerExpert (one source)
+ *            or a rank's slice of it are such counts.  Not read by the host.
+ * w          [groups][n][k] int8, device, 16-byte aligned: the weights of
+ *            expert g for output column j are the k bytes at (g * n + j) * k.
+ * out        [rows][n] int32, device, 4-byte aligned, outBytes >= rows * n * 4:
+ *            out[m][j] = sum over i < k of a[m][i] * w[g][j][i] for each row m
+ *            owned by expert g (exact: every partial sum is below 2^31 in
+ *            magnitude).  Rows that no expert owns are not written.
+ *
+ * Requires rows >= 0, k >= 1, n >= 1, groups >= 1, aRowBytes >= k (else
+ * MOE_ERR_BAD_SHAPE); k % 16 == 0, k <= MOE_GEMM_MAX_K, n <= MOE_GEMM_MAX_N,
+ * groups <= MOE_GEMM_MAX_GROUPS (else MOE_ERR_UNSUPPORTED); aRowBytes a
+ * multiple of 16 (else MOE_ERR_BAD_ALIGN).  rows == 0 enqueues nothing. */
+int moe_grouped_gemm_i8(const void* a, int64_t aRowBytes, int32_t rows, int32_t k,
+                        const int32_t* groupCount, int32_t groups, const void* w, int32_t n,
+                        int32_t* out, size_t outBytes, void* stream);
+
+/* Text for a status code (static storage). */
 const char* moe_status_str(int status);
 
 /* The hipError_t value of the last MOE_ERR_HIP returned on this thread

@@ -36,7 +36,7 @@ def test_header_symbols_exported(M):
 def test_header_constants_match_binding(M):
     text = open(HEADER).read()
     for name in ("MOE_MAX_EXPERTS", "MOE_MAX_HIDDEN", "MOE_MAX_TOPK", "MOE_MAX_SOURCES",
-                 "MOE_EPILOGUE_MAX_N"):
+                 "MOE_EPILOGUE_MAX_N", "MOE_GEMM_MAX_K", "MOE_GEMM_MAX_N", "MOE_GEMM_MAX_GROUPS"):
         val = int(re.search(rf"#define {name} (\d+)", text).group(1))
         assert getattr(M, name) == val
 
@@ -269,3 +269,25 @@ def test_epilogue_rejects_on_host(M):
     assert call(acc=None) == 1 and call(ws=None) == 1 and call(ts=None) == 1 and call(out=None) == 1
     assert call(acc=P + 4) == 3 and call(ws=P + 8) == 3 and call(out=P + 4) == 3 and call(ts=P + 2) == 3
     assert call(out_bytes=16 * rb - 1) == 6
+
+
+def test_grouped_gemm_rejects_on_host(M):
+    L = M._lib
+    ok = dict(a_row_bytes=7200, rows=64, k=7168, groups=16, n=4096, out_bytes=64 * 4096 * 4)
+
+    def call(a=P, a_row_bytes=ok["a_row_bytes"], rows=ok["rows"], k=ok["k"], gc=P,
+             groups=ok["groups"], w=P, n=ok["n"], out=P, out_bytes=ok["out_bytes"]):
+        return L.moe_grouped_gemm_i8(a, a_row_bytes, rows, k, gc, groups, w, n, out, out_bytes, None)
+
+    assert call(rows=-1) == 2 and call(k=0) == 2 and call(n=0) == 2 and call(groups=0) == 2
+    assert call(a_row_bytes=7152) == 2          # shorter than k
+    assert call(k=7160, a_row_bytes=7168) == 7  # k % 16
+    assert call(k=65552, a_row_bytes=65552) == 7 and call(n=65537) == 7 and call(groups=65537) == 7
+    assert call(a_row_bytes=7208) == 3          # row stride not a multiple of 16
+    assert call(rows=0, a=None, gc=None, w=None, out=None) == 0  # nothing to do
+    assert call(a=None) == 1 and call(gc=None) == 1 and call(w=None) == 1 and call(out=None) == 1
+    assert call(a=P + 8) == 3 and call(w=P + 4) == 3 and call(gc=P + 2) == 3 and call(out=P + 2) == 3
+    assert call(out_bytes=64 * 4096 * 4 - 1) == 6
+    # more workgroups than one launch takes: rows / 256 + groups row slots x n / 128 column tiles
+    assert call(rows=2 ** 31 - 1, a_row_bytes=16, k=16, n=65536,
+                out_bytes=(2 ** 31 - 1) * 65536 * 4) == 7
