@@ -23,7 +23,11 @@ the CPU oracle are reported beside it, labelled.
 ``--stage epilogue`` times the expert-side epilogue kernel (dequantise the
 first expert GEMM's int32 output, SwiGLU, requantise to int8 rows) alone, on
 every receive row of the large shape with an FFN width of 2048, and prints
-its own JSON line (rows/s).
+its own JSON line (rows/s).  ``--stage gemm`` times the first expert matmul
+(int8 receive rows x int8 expert weights -> int32, grouped by expert) on one
+GPU's share of the large shape on a 16-rank expert-parallel group (32768
+rows, 16 experts, k = 7168, 2 x 2048 output columns) and prints its own line
+(rows/s, with int8 TOP/s against the MFMA peak).
 
 Output: one JSON line on stdout.  ``--gpus N`` with N > 1 exits: the bench
 measures one GPU.
@@ -56,8 +60,11 @@ KERNEL_SOURCES = {
     "combine": [os.path.join(CSRC, "combine.hip")] + KERNEL_HEADERS,
     "fused": [os.path.join(CSRC, "fused.hip")] + KERNEL_HEADERS,
     "epilogue": [os.path.join(CSRC, "epilogue.hip")] + KERNEL_HEADERS,
+    "gemm": [os.path.join(CSRC, "gemm.hip")] + KERNEL_HEADERS,
 }
 EPILOGUE_METRIC = "expert epilogue (dequant + SwiGLU + int8 requant) rows/s and HBM GB/s (% of peak)"
+GEMM_METRIC = "first expert matmul (int8 x int8 -> int32, grouped by expert) rows/s and TOP/s (% of peak)"
+MFMA_I8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, 5.0 POP/s
 
 
 def log(msg: str) -> None:
@@ -159,6 +166,17 @@ def load_traffic(kernel: str, workload: str, mode: str):
     return t.get("traffic_bytes_per_launch")
 
 
+def gemm_ops(rows: int, n: int, k: int) -> int:
+    """Multiplies and adds of the first expert matmul over `rows` owned rows."""
+    return 2 * rows * n * k
+
+
+def gemm_bytes(rows: int, n: int, k: int, groups: int) -> int:
+    """Bytes the first expert matmul must move at least once: the k codes of
+    every row, every expert's weights, the int32 output and the counts."""
+    return rows * k + groups * n * k + rows * n * 4 + groups * 4
+
+
 def cpu_baseline(w, quant: bool, budget_s: float):
     """The oracle as it stands, single-threaded on a host core, over the full
     workload, repeated until about ``budget_s`` seconds have passed."""
@@ -200,9 +218,10 @@ def main(argv=None) -> int:
                          "buffer (multi-source notify, per-source dispatch and combine)")
     ap.add_argument("--skip-kernels-only", action="store_true",
                     help="with the fused path, do not also time the dispatch and combine kernels alone")
-    ap.add_argument("--stage", default="pipeline", choices=["pipeline", "epilogue"],
+    ap.add_argument("--stage", default="pipeline", choices=["pipeline", "epilogue", "gemm"],
                     help="pipeline: layout + notify + dispatch + combine (the headline); epilogue: the "
-                         "expert-side dequant + SwiGLU + int8 requant kernel on its own")
+                         "expert-side dequant + SwiGLU + int8 requant kernel on its own; gemm: the first "
+                         "expert matmul on its own")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, then WRITE_SIZE) of a bench "
                          "run into profiles/traffic_*.json and exit")
@@ -228,6 +247,8 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     if args.stage == "epilogue":
         return bench_epilogue(args, M, torch, W, dev)
+    if args.stage == "gemm":
+        return bench_gemm(args, M, torch, W, dev)
     quant = args.mode == "int8"
 
     log(f"generating workload {args.workload}")
@@ -555,6 +576,126 @@ def bench_epilogue(args, M, torch, W, dev) -> int:
     return 0
 
 
+def bench_gemm(args, M, torch, W, dev) -> int:
+    """The first expert matmul alone on one GPU's share of the large shape on
+    a 16-rank expert-parallel group: 32768 int8 rows (7200-byte receive rows)
+    spread over 16 experts as uniform routing spreads them, k = 7168, n = 4096
+    (gate and up columns of an FFN of width 2048).  The caches are flushed
+    before each timed launch."""
+    import numpy as np
+
+    c = W.GEMM_CONFIG
+    rows, k, n, groups = c["rows"], c["k"], c["n"], c["groups"]
+    stride = M.moe_recv_row_bytes(k, M.MOE_INT8_ROWSCALE)
+    log(f"generating gemm inputs rows={rows} k={k} n={n} groups={groups}")
+    case = W.gemm_case(c["seed"], rows, k, n, groups, stride=stride)
+    a = torch.from_numpy(case.a.reshape(-1).view("uint8")).to(dev)
+    wt = torch.from_numpy(case.w.view("uint8")).to(dev)
+    gc = torch.from_numpy(case.group_count).to(dev)
+    out = torch.zeros((rows, n), dtype=torch.int32, device=dev)
+    owned = int(min(max(case.group_count.astype("int64").clip(0).sum(), 0), rows))
+    flush = torch.ones(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    flush_out = torch.zeros((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        M.moe_grouped_gemm_i8(a, stride, rows, k, gc, wt, out)
+
+    log(f"warm-up x{args.warmup}")
+    for _ in range(args.warmup):
+        torch.sum(flush, dim=0, out=flush_out)
+        launch()
+    torch.cuda.synchronize()
+    log(f"timed x{args.steps}")
+    hev = HipEvents(args.event_flags)
+    ev = [(hev.new(), hev.new()) for _ in range(args.steps)]
+    for e0, e1 in ev:
+        torch.sum(flush, dim=0, out=flush_out)
+        hev.record(e0, stream)
+        launch()
+        hev.record(e1, stream)
+    torch.cuda.synchronize()
+    us = [hev.ms(e0, e1) * 1e3 for e0, e1 in ev]
+    log("un-flushed back-to-back")
+    u0, u1 = hev.new(), hev.new()
+    hev.record(u0, stream)
+    for _ in range(args.steps):
+        launch()
+    hev.record(u1, stream)
+    torch.cuda.synchronize()
+    unflushed_us = hev.ms(u0, u1) * 1e3 / args.steps
+    log("copy ceiling")
+    dst = torch.empty_like(flush)
+    for _ in range(2):
+        torch.neg(flush, out=dst)
+    c0, c1 = hev.new(), hev.new()
+    hev.record(c0, stream)
+    for _ in range(10):
+        torch.neg(flush, out=dst)
+    hev.record(c1, stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * flush.numel() * 4 * 10 / (hev.ms(c0, c1) * 1e-3) / 1e9
+    del dst
+    hev.close()
+    mean_us = statistics.mean(us)
+    ops = gemm_ops(owned, n, k)
+    tops = ops / (mean_us * 1e-6) / 1e12
+    alg = gemm_bytes(owned, n, k, groups)
+    cpu = None
+    if args.cpu_budget > 0:
+        import oracle
+
+        log(f"cpu baseline (oracle, ~{args.cpu_budget:.0f} s)")
+        oracle.default()
+        done, t0, batch = 0, time.perf_counter(), 8
+        while True:
+            sel = (W.u64(c["seed"], 40 + done // batch, batch) % np.uint64(rows)).astype("int64")
+            oracle.grouped_gemm_i8(case.a, k, case.group_count, case.w, rows=sel)
+            done += batch
+            el = time.perf_counter() - t0
+            if el >= args.cpu_budget or done >= 4096:
+                break
+        cpu = dict(value=done / el, unit="rows/s", cores=1, kind="oracle",
+                   sample=f"{done} random rows of the {rows} (each: {n} x {k} products), {el:.1f} s on one "
+                          "host thread",
+                   host_cpu=platform.processor() or platform.machine(), host_nproc=os.cpu_count())
+    line = {
+        "metric": GEMM_METRIC,
+        "value": owned / (mean_us * 1e-6),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": mean_us * 1e-3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "payload": "int8 receive rows and int8 expert weights in, int32 sums out",
+        "data": "synthetic",
+        "config": {"workload": "gemm", "rows": rows, "owned_rows": owned, "k": k, "n": n, "groups": groups,
+                   "row_bytes": stride,
+                   "rows_from": "one rank's receive rows on a 16-rank expert-parallel group at the large "
+                                "shape (16 experts of 256)",
+                   "parallelism": "1 GPU"},
+        "step": "one moe_grouped_gemm_i8 launch, caches flushed before it",
+        "timer": f"HIP events on the kernel's stream ({args.event_flags})",
+        "stages_us": {"gemm": {"mean": mean_us, "p10": pct(us, 0.1), "p50": pct(us, 0.5),
+                               "p90": pct(us, 0.9)}},
+        "ops_per_launch": ops,
+        "algorithmic_bytes": {"gemm": alg},
+        "hbm_gbps_at_algorithmic_bytes": alg / (mean_us * 1e-6) / 1e9,
+        "roofline": {"bound": "mfma", "kernel": "grouped_gemm_i8", "achieved": tops,
+                     "peak": MFMA_I8_PEAK_TOPS, "unit": "TOP/s", "frac": tops / MFMA_I8_PEAK_TOPS,
+                     "traffic": load_traffic("gemm", "gemm", f"n{n}")},
+        "unflushed_us_per_launch": unflushed_us,
+        "copy_ceiling_gbps": copy_gbps,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def bench_sources(args, M, torch, w, x, idx, wts, quant: bool, do_flush, stream) -> int:
     """The workload's tokens split evenly into ``--sources`` source ranks
     sharing one receive buffer: a step is every source's layout, one notify
@@ -702,7 +843,13 @@ def ingest_pmc(args, fetch_csv: str, write_csv: str) -> int:
     w = None
     import workloads as W
 
-    if args.stage == "epilogue":
+    if args.stage == "gemm":
+        cg = W.GEMM_CONFIG
+        workload, mode = "gemm", f"n{cg['n']}"
+        counts = W.gemm_case(cg["seed"], 1, 16, 1, cg["groups"], owned=cg["rows"]).group_count
+        owned = int(min(counts.astype("int64").sum(), cg["rows"]))
+        kernels = (("gemm", ("grouped_gemm_kernel",), gemm_bytes(owned, cg["n"], cg["k"], cg["groups"])),)
+    elif args.stage == "epilogue":
         ce = W.EPILOGUE_CONFIG
         workload, mode = "epilogue", f"n{ce['n']}"
         kernels = (("epilogue", ("deq_swiglu_quant_kernel",), epilogue_bytes(ce["rows"], ce["n"])),)

@@ -12,14 +12,18 @@
 //
 // Tiling (gfx950, wave64, v_mfma_i32_16x16x64_i8): a workgroup of WM x WN
 // waves computes a TM x TN tile of one expert's output; each wave owns a
-// (TM/WM) x (TN/WN) block of 16 x 16 MFMA tiles.  K is walked in stages of
-// 128 bytes: every thread loads its 16-byte pieces of the next stage's A
-// rows and B rows (weight rows, k contiguous) into registers while the waves
-// run the current stage's MFMAs out of LDS.  LDS rows are 144 bytes apart,
-// so the 16 rows that one fragment read touches start 36 dwords apart and
-// fall in distinct banks.  A lane's fragment of A and of B takes the same 16
-// bytes of k (bytes 16 * (lane / 16) of the 64-byte step), so each product
-// pairs a[m][i] with w[g][j][i].
+// (TM/WM) x (TN/WN) block of 16 x 16 MFMA tiles (the library launches
+// 128 x 128 tiles of 2 x 2 waves, two workgroups per CU).  K is walked in
+// stages of SK = 256 bytes: every thread loads its 16-byte pieces of the
+// next stage's A rows and B rows (weight rows, k contiguous) into registers
+// while the waves run the current stage's MFMAs out of LDS.  In LDS a row's
+// 16-byte pieces are XOR-swizzled by the row index (piece p of row r at
+// position p ^ (r % 16)), so the 16 rows one fragment read touches hit 16
+// different positions: no bank conflicts (the hardware counter reads zero;
+// rows padded to 272 bytes instead conflicted on a third of the LDS cycles).
+// A lane's fragment of A and of B takes the same 16 bytes of k (logical
+// piece kk / 16 + lane / 16 of the stage), so each product pairs a[m][i]
+// with w[g][j][i].
 //
 // The counts live on the device and the host does not read them, so the
 // launch has ceil(rows / TM) + groups row slots (enough for any counts whose
@@ -35,12 +39,6 @@ namespace moe {
 namespace {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kStageK = 128;             // bytes of k per stage
-constexpr int kPieces = kStageK / 16;    // 16-byte pieces of a row per stage
-constexpr int kLdsPitch = kStageK + 16;  // bytes between LDS rows
-constexpr int kXcds = 8;                 // workgroups go round-robin over the XCDs
-constexpr int kBandSlots = 4;            // row slots per band of the tile order
 
 struct TileSlot {
   int32_t group, row0, row_end;
@@ -80,16 +78,17 @@ __device__ void find_slot(const GemmArgs& a, int64_t slot, int lane, TileSlot* o
   }
 }
 
-// Position of workgroup b in the tile order: consecutive workgroups land on
-// different XCDs, so each XCD is given a contiguous range of the order.
-__device__ __forceinline__ int64_t xcd_order(int64_t b, int64_t total) {
-  const int64_t per = total / kXcds, rem = total % kXcds;
-  const int64_t x = b % kXcds, i = b / kXcds;
-  return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
-}
-
-template <int TM, int TN, int WM, int WN>
+template <int TM, int TN, int WM, int WN, int SK, int kDepth>
 __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs a) {
+  static_assert(kDepth == 1 || kDepth == 2, "stages held in registers ahead of the LDS stage");
+  constexpr int kStageK = SK;              // bytes of k per stage
+  constexpr int kPieces = kStageK / 16;    // 16-byte pieces of a row per stage
+  // LDS rows are kStageK bytes apart; the 16-byte piece p of tile row r
+  // sits at position p ^ (r % kPieces) of its row
+  constexpr bool kSwizzle = true;
+  constexpr int kLdsPitch = kStageK + (kSwizzle ? 0 : 16);
+  constexpr int kSwz = kSwizzle ? kPieces - 1 : 0;
+  static_assert(kPieces <= 16, "a fragment's 16 rows cover every swizzle position");
   constexpr int kThreads = kWave * WM * WN;
   constexpr int kWaveM = TM / WM, kWaveN = TN / WN;
   constexpr int kMI = kWaveM / 16, kNI = kWaveN / 16;
@@ -104,16 +103,16 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
 
-  // workgroup -> (row slot, column tile): bands of kBandSlots row slots,
-  // column tiles outer within a band
+  // workgroup -> (row slot, column tile), column tiles innermost.  The
+  // hardware deals consecutive workgroups round-robin to the 8 XCDs, so with
+  // 32 column tiles each XCD holds the same 4 column tiles of every row slot
+  // it runs: their weight rows (4 x 0.9 MB at k = 7168) stay in its L2 while
+  // the whole GPU works through one expert's row slots.  (A contiguous range
+  // of the order per XCD, or bands of several row slots, measured 6-15 %
+  // slower at the benchmark shape.)
   const int64_t n_tiles = (a.n + TN - 1) / TN;
-  const int64_t slots = static_cast<int64_t>(gridDim.x) / n_tiles;
-  const int64_t order = xcd_order(blockIdx.x, gridDim.x);
-  const int64_t band = order / (kBandSlots * n_tiles);
-  const int64_t within = order - band * kBandSlots * n_tiles;
-  const int64_t band_slots = min(static_cast<int64_t>(kBandSlots), slots - band * kBandSlots);
-  const int64_t col_tile = within / band_slots;
-  const int64_t slot = band * kBandSlots + within % band_slots;
+  const int64_t slot = blockIdx.x / n_tiles;
+  const int64_t col_tile = blockIdx.x - slot * n_tiles;
 
   if (wave == 0) {
     if (lane == 0) slot_info.group = -1;
@@ -140,8 +139,9 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
     b_src[p] = a.w + (static_cast<int64_t>(group) * a.n + col) * a.k + piece * 16;
   }
 
-  i32x4 ra[kAPasses], rb[kBPasses];
-  auto load_stage = [&](int k0) {
+  using ARegs = i32x4[kAPasses];
+  using BRegs = i32x4[kBPasses];
+  auto load_stage = [&](int k0, ARegs& ra, BRegs& rb) {
     if (k0 + piece * 16 < a.k) {
 #pragma unroll
       for (int p = 0; p < kAPasses; ++p) ra[p] = *reinterpret_cast<const i32x4*>(a_src[p] + k0);
@@ -154,45 +154,79 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
       for (int p = 0; p < kBPasses; ++p) rb[p] = i32x4{0, 0, 0, 0};
     }
   };
-  auto store_stage = [&]() {
+  auto store_stage = [&](const ARegs& ra, const BRegs& rb) {
 #pragma unroll
-    for (int p = 0; p < kAPasses; ++p)
-      *reinterpret_cast<i32x4*>(lds_a + (r0 + p * kRowsPerPass) * kLdsPitch + piece * 16) = ra[p];
+    for (int p = 0; p < kAPasses; ++p) {
+      const int r = r0 + p * kRowsPerPass;
+      *reinterpret_cast<i32x4*>(lds_a + r * kLdsPitch + ((piece ^ (r & kSwz)) * 16)) = ra[p];
+    }
 #pragma unroll
-    for (int p = 0; p < kBPasses; ++p)
-      *reinterpret_cast<i32x4*>(lds_b + (r0 + p * kRowsPerPass) * kLdsPitch + piece * 16) = rb[p];
+    for (int p = 0; p < kBPasses; ++p) {
+      const int r = r0 + p * kRowsPerPass;
+      *reinterpret_cast<i32x4*>(lds_b + r * kLdsPitch + ((piece ^ (r & kSwz)) * 16)) = rb[p];
+    }
   };
 
   const int wm = wave / WN, wn = wave % WN;
-  const uint8_t* fa = lds_a + (wm * kWaveM + lane % 16) * kLdsPitch + (lane / 16) * 16;
-  const uint8_t* fb = lds_b + (wn * kWaveN + lane % 16) * kLdsPitch + (lane / 16) * 16;
+  // a fragment's rows are 16-aligned, so row % kPieces is lane % kPieces
+  const uint8_t* fa = lds_a + (wm * kWaveM + lane % 16) * kLdsPitch;
+  const uint8_t* fb = lds_b + (wn * kWaveN + lane % 16) * kLdsPitch;
+  const int lane_swz = lane & kSwz;
   i32x4 acc[kMI][kNI];
 #pragma unroll
   for (int i = 0; i < kMI; ++i)
 #pragma unroll
     for (int j = 0; j < kNI; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
-  const int stages = (a.k + kStageK - 1) / kStageK;
-  load_stage(0);
-  for (int s = 0; s < stages; ++s) {
-    if (s) __syncthreads();  // every wave is done reading the previous stage
-    store_stage();
-    __syncthreads();
-    if (s + 1 < stages) load_stage((s + 1) * kStageK);
+  auto compute_stage = [&]() {
 #pragma unroll
     for (int kk = 0; kk < kStageK; kk += 64) {
+      const int pos = ((kk / 16 + lane / 16) ^ lane_swz) * 16;
       i32x4 af[kMI], bf[kNI];
 #pragma unroll
       for (int i = 0; i < kMI; ++i)
-        af[i] = *reinterpret_cast<const i32x4*>(fa + i * 16 * kLdsPitch + kk);
+        af[i] = *reinterpret_cast<const i32x4*>(fa + i * 16 * kLdsPitch + pos);
 #pragma unroll
       for (int j = 0; j < kNI; ++j)
-        bf[j] = *reinterpret_cast<const i32x4*>(fb + j * 16 * kLdsPitch + kk);
+        bf[j] = *reinterpret_cast<const i32x4*>(fb + j * 16 * kLdsPitch + pos);
 #pragma unroll
       for (int i = 0; i < kMI; ++i)
 #pragma unroll
         for (int j = 0; j < kNI; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // One LDS stage; the next kDepth stages are in flight into registers while
+  // it is computed.  The barrier before a store waits for every wave to be
+  // done reading the stage it replaces.
+  const int stages = (a.k + kStageK - 1) / kStageK;
+  ARegs ra0, ra1;
+  BRegs rb0, rb1;
+  load_stage(0, ra0, rb0);
+  if (kDepth == 1) {
+    for (int s = 0; s < stages; ++s) {
+      if (s) __syncthreads();
+      store_stage(ra0, rb0);
+      __syncthreads();
+      if (s + 1 < stages) load_stage((s + 1) * kStageK, ra0, rb0);
+      compute_stage();
+    }
+  } else {
+    if (stages > 1) load_stage(kStageK, ra1, rb1);
+    for (int s = 0; s < stages; s += 2) {
+      if (s) __syncthreads();
+      store_stage(ra0, rb0);
+      __syncthreads();
+      if (s + 2 < stages) load_stage((s + 2) * kStageK, ra0, rb0);
+      compute_stage();
+      if (s + 1 < stages) {
+        __syncthreads();
+        store_stage(ra1, rb1);
+        __syncthreads();
+        if (s + 3 < stages) load_stage((s + 3) * kStageK, ra1, rb1);
+        compute_stage();
+      }
     }
   }
 
@@ -211,13 +245,13 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
   }
 }
 
-template <int TM, int TN, int WM, int WN>
+template <int TM, int TN, int WM, int WN, int SK, int kDepth>
 hipError_t launch_shape(const GemmArgs& a, hipStream_t stream) {
   const int64_t slots = (a.rows + TM - 1) / TM + a.groups;
   const int64_t n_tiles = (a.n + TN - 1) / TN;
   const int64_t blocks = slots * n_tiles;
   if (blocks > kGemmMaxBlocks) return hipErrorInvalidValue;
-  grouped_gemm_kernel<TM, TN, WM, WN>
+  grouped_gemm_kernel<TM, TN, WM, WN, SK, kDepth>
       <<<dim3(static_cast<uint32_t>(blocks)), dim3(kWave * WM * WN), 0, stream>>>(a);
   return hipGetLastError();
 }
@@ -230,7 +264,7 @@ int64_t grouped_gemm_blocks(int64_t rows, int32_t groups, int32_t n) {
 
 hipError_t launch_grouped_gemm_i8(const GemmArgs& a, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;
-  return launch_shape<kGemmTileM, kGemmTileN, 2, 2>(a, stream);
+  return launch_shape<kGemmTileM, kGemmTileN, 2, 2, 256, 1>(a, stream);
 }
 
 }  // namespace moe

@@ -130,7 +130,7 @@ struct GemmArgs {
   int32_t n;
   int32_t* out;                // [rows][n]
 };
-constexpr int kGemmTileM = 256, kGemmTileN = 128;
+constexpr int kGemmTileM = 128, kGemmTileN = 128;
 constexpr int64_t kGemmMaxBlocks = int64_t(1) << 24;
 // Workgroups of one launch (row slots x column tiles).
 int64_t grouped_gemm_blocks(int64_t rows, int32_t groups, int32_t n);
