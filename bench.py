@@ -60,7 +60,7 @@ KERNEL_SOURCES = {
     "combine": [os.path.join(CSRC, "combine.hip")] + KERNEL_HEADERS,
     "fused": [os.path.join(CSRC, "fused.hip")] + KERNEL_HEADERS,
     "epilogue": [os.path.join(CSRC, "epilogue.hip")] + KERNEL_HEADERS,
-    "gemm": [os.path.join(CSRC, "gemm.hip")] + KERNEL_HEADERS,
+    "gemm": [os.path.join(CSRC, "gemm.hip"), os.path.join(CSRC, "gemm.h")] + KERNEL_HEADERS,
 }
 EPILOGUE_METRIC = "expert epilogue (dequant + SwiGLU + int8 requant) rows/s and HBM GB/s (% of peak)"
 GEMM_METRIC = "first expert matmul (int8 x int8 -> int32, grouped by expert) rows/s and TOP/s (% of peak)"

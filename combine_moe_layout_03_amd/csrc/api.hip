@@ -7,6 +7,7 @@
 #include <limits>
 
 #include "launch.h"
+#include "gemm.h"
 #include "moe_ep.h"
 
 namespace {

@@ -34,6 +34,7 @@
 // past n repeat row n - 1 and are never stored.
 #include "device_util.h"
 #include "launch.h"
+#include "gemm.h"
 
 namespace moe {
 namespace {

@@ -118,23 +118,6 @@ constexpr int kEpilogueMaxN = MOE_EPILOGUE_MAX_N;
 
 hipError_t launch_deq_swiglu_quant(const EpilogueArgs& a, hipStream_t stream);
 
-// ---- first expert matmul (int8 x int8 -> int32 over per-expert row ranges) ------
-struct GemmArgs {
-  const int8_t* a;             // receive rows: row m at a + m * a_stride, k int8 codes
-  int64_t a_stride;            // bytes between rows (a multiple of 16)
-  int64_t rows;                // rows of a and of out
-  int32_t k;                   // a multiple of 16
-  const int32_t* group_count;  // [groups]: rows of each expert, in order
-  int32_t groups;
-  const int8_t* w;             // [groups][n][k]
-  int32_t n;
-  int32_t* out;                // [rows][n]
-};
-constexpr int kGemmTileM = 128, kGemmTileN = 128;
-constexpr int64_t kGemmMaxBlocks = int64_t(1) << 24;
-// Workgroups of one launch (row slots x column tiles).
-int64_t grouped_gemm_blocks(int64_t rows, int32_t groups, int32_t n);
-hipError_t launch_grouped_gemm_i8(const GemmArgs& a, hipStream_t stream);
 size_t fused_lds_bytes(int32_t num_experts, int32_t tokens_per_group, int32_t topk, int32_t copies);
 hipError_t launch_fused(const FusedArgs& a, Half x_type, bool quant, int groups, hipStream_t stream);
 
