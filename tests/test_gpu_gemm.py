@@ -3,7 +3,8 @@ the GPU against the CPU oracle, through the C ABI.
 
 Bar: bit-exact int32 outputs (integer sums, exact on both sides), rows owned
 by no expert left as they were, on every row of the small cases and on
-sampled rows of the shape the benchmark times.  The cases cover several row
+sampled rows of the shape the benchmark times and of the layer's second
+matmul.  The cases cover several row
 and column tiles with ragged ends, k that ends inside a 128-byte stage,
 empty and negative counts, counts past the row capacity, more experts than
 one wave scans at once, and the int8 receive buffer used in place.
@@ -93,6 +94,21 @@ def test_gemm_full_size_sampled_rows():
     pick = W.u64(7, 0, 32) % np.uint64(case.rows)
     rows = np.unique(np.concatenate([starts, ends - 1, pick.astype(np.int64)]))
     assert_same(case, got, "full size", rows=rows)
+
+
+def test_gemm_second_matmul_shape_sampled_rows():
+    """The shape of the layer's second expert matmul on the same share: the
+    epilogue's int8 rows (k = 2048 codes in 2080-byte rows) times weights
+    [16][7168][2048]; first and last row of every expert and 32 random rows."""
+    rows, k, n, groups = 32768, 2048, 7168, 16
+    case = W.gemm_case(3002, rows, k, n, groups, stride=align32(k) + 32)
+    log("grouped gemm second-matmul shape")
+    got = run_gpu(case)
+    ends = np.cumsum(case.group_count)
+    starts = ends - case.group_count
+    pick = W.u64(8, 0, 32) % np.uint64(rows)
+    sel = np.unique(np.concatenate([starts, ends - 1, pick.astype(np.int64)]))
+    assert_same(case, got, "second-matmul shape", rows=sel)
 
 
 def test_gemm_on_receive_buffer_then_epilogue():
