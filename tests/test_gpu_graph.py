@@ -71,3 +71,61 @@ def test_graph_replays_match_oracle(name, quant, fused):
     ref_other = oracle.pipeline(other.w.x, other.w.x_dtype, other.w.topk_idx, other.w.topk_w,
                                 other.w.expert_num_per_rank, other.w.rank_size, quant, other.w.x_dtype)
     assert np.array_equal(got_other, ref_other["out"]), "eager run between replays"
+
+
+def test_graph_expert_side_replays_match_oracle():
+    """The first expert matmul and its epilogue captured together and
+    replayed on new rows and new per-expert counts, with eager matmuls
+    between replays; every replay against the oracle."""
+    import combine_moe_layout_03_amd as M
+
+    rows, k, n_out, groups, stride = 300, 96, 64, 4, 128
+    wts = W.gemm_case(920, 1, k, 2 * n_out, groups).w
+    ws = (0.5 + W.uniform01(920, 5, 2 * n_out)).astype(np.float32) * np.float32(2.0 ** -10)
+    ts = (0.005 + 0.015 * W.uniform01(920, 6, rows)).astype(np.float32)
+    a = torch.zeros(rows * stride, dtype=torch.uint8, device="cuda")
+    gc = torch.zeros(groups, dtype=torch.int32, device="cuda")
+    w_d = torch.from_numpy(wts.view(np.uint8)).cuda()
+    ws_d, ts_d = torch.from_numpy(ws).cuda(), torch.from_numpy(ts).cuda()
+    acc = torch.zeros((rows, 2 * n_out), dtype=torch.int32, device="cuda")
+    rb = M.moe_recv_row_bytes(n_out, M.MOE_INT8_ROWSCALE)
+    out = torch.zeros(rows * rb, dtype=torch.uint8, device="cuda")
+
+    def step():
+        M.moe_grouped_gemm_i8(a, stride, rows, k, gc, w_d, acc)
+        M.moe_deq_swiglu_quant(acc, ws_d, ts_d, out)
+
+    log("graph expert side: eager warm-up")
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    log("graph expert side: capture")
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    other = W.gemm_case(930, 200, k, 2 * n_out, groups, stride=stride, counts=[50, 50, 50, 50])
+    other_a = torch.from_numpy(other.a.reshape(-1).view(np.uint8)).cuda()
+    other_out = torch.zeros((200, 2 * n_out), dtype=torch.int32, device="cuda")
+    for r, counts in enumerate(([100, 0, 150, 50], [300, 0, 0, 0], [10, 20, 30, 40])):
+        c = W.gemm_case(940 + r, rows, k, 2 * n_out, groups, stride=stride, counts=counts)
+        a.copy_(torch.from_numpy(c.a.reshape(-1).view(np.uint8)))
+        gc.copy_(torch.from_numpy(c.group_count))
+        acc.fill_(0)
+        torch.cuda.synchronize()
+        log(f"graph expert side: replay {r}")
+        graph.replay()
+        torch.cuda.synchronize()
+        exp_acc, grp = oracle.grouped_gemm_i8(c.a, k, c.group_count, wts)
+        exp_acc[grp < 0] = 0   # rows of no expert keep the zeros set before the replay
+        assert np.array_equal(acc.cpu().numpy(), exp_acc), f"replay {r}: matmul"
+        exp = oracle.swiglu_quant(exp_acc, ws, ts)
+        raw = out.cpu().numpy().reshape(rows, rb)
+        assert np.array_equal(np.ascontiguousarray(raw[:, :n_out]).view(np.int8), exp["codes"]), f"replay {r}"
+        off = (n_out + 31) // 32 * 32
+        inv = np.ascontiguousarray(raw[:, off:off + 4]).view(np.float32).reshape(-1)
+        assert np.array_equal(inv.view(np.uint32), exp["inv"].view(np.uint32)), f"replay {r}: scales"
+        M.moe_grouped_gemm_i8(other_a, stride, 200, k, torch.from_numpy(other.group_count).cuda(), w_d,
+                              other_out)
+        torch.cuda.synchronize()
+    exp_o, _ = oracle.grouped_gemm_i8(other.a, k, other.group_count, wts)
+    assert np.array_equal(other_out.cpu().numpy(), exp_o), "eager matmul between replays"
