@@ -154,6 +154,25 @@ def test_gemm_on_receive_buffer_then_epilogue():
     assert np.array_equal(got_inv.view(np.uint32), exp["inv"].view(np.uint32))
 
 
+def test_gemm_extremes_at_max_k():
+    """k = MOE_GEMM_MAX_K with the int8 extremes: (-128)(-128) summed 65536
+    times is 2^30 and 127(-128) summed is -1065353216, both exact in int32;
+    the same values from the oracle and from the closed form."""
+    mod = M()
+    k, n, rows = mod.MOE_GEMM_MAX_K, 32, 6
+    a = np.full((rows, k), -128, np.int8)
+    a[1::2] = 127
+    wts = np.full((2, n, k), -128, np.int8)
+    wts[1, ::2] = 127
+    counts = np.array([3, 3], np.int32)
+    case = W.GemmCase(rows=rows, k=k, n=n, stride=k, a=a, group_count=counts, w=wts, seed=0)
+    log("grouped gemm extremes at k = 65536")
+    got = run_gpu(case)
+    assert_same(case, got, "extremes")
+    assert got[0, 0] == 2 ** 30 and got[1, 0] == -1065353216
+    assert got[3, 0] == 127 * 127 * k and got[4, 1] == 2 ** 30 and got[4, 0] == -1065353216
+
+
 def test_gemm_zero_rows_and_repeat():
     """rows = 0 enqueues nothing; two calls in a row give the same bits, the
     second on fewer rows with other counts."""
