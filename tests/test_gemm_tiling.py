@@ -1,0 +1,113 @@
+"""CPU check of the grouped GEMM's grid and indexing (no GPU needed).
+
+Replays, on the host, how the launch maps workgroups to (expert, row tile,
+column tile) through the prefix sum over the per-expert counts, and which
+rows, weight rows and output elements each workgroup touches, for the tile
+shape the library launches (read from its headers).  Asserts that every
+load stays inside the buffers the C ABI documents, and that every output
+element of a row some expert owns is written exactly once and no other
+element is written.
+"""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads as W
+
+CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                    "combine_moe_layout_03_amd", "csrc")
+
+
+def _shape():
+    h = open(os.path.join(CSRC, "gemm.h")).read()
+    tm, tn = map(int, re.search(r"kGemmTileM = (\d+), kGemmTileN = (\d+);", h).groups())
+    g = open(os.path.join(CSRC, "gemm.hip")).read()
+    wm, wn, sk = map(int, re.search(r"launch_shape<kGemmTileM, kGemmTileN, (\d+), (\d+), (\d+), \d+>", g).groups())
+    return tm, tn, wm, wn, sk
+
+
+def _slot(counts, rows, slot, tm):
+    """(expert, first row, end row) of a row slot, or None: the kernel's
+    wave-wide prefix sums over chunks of 64 experts."""
+    row_base = tile_base = 0
+    found = None
+    for g0 in range(0, len(counts), 64):
+        c = np.array([max(int(v), 0) for v in counts[g0:g0 + 64]], np.int64)
+        incl = np.cumsum(c)
+        s = np.minimum(row_base + incl - c, rows)
+        e = np.minimum(row_base + incl, rows)
+        tiles = (e - s + tm - 1) // tm
+        t0 = tile_base + np.cumsum(tiles) - tiles
+        for lane in range(c.size):
+            if t0[lane] <= slot < t0[lane] + tiles[lane]:
+                assert found is None
+                found = (g0 + lane, int(s[lane] + (slot - t0[lane]) * tm), int(e[lane]))
+        row_base = min(row_base + int(incl[-1]), rows)
+        tile_base += int(tiles.sum())
+        if tile_base > slot:
+            break
+    return found
+
+
+@pytest.mark.parametrize("rows,k,n,counts", [
+    (1000, 320, 300, "owned:900:5"),
+    (830, 128, 128, [0, 300, -5, 1, 0, 517]),
+    (3, 16, 16, [0, 1, 0]),
+    (2000, 64, 128, "owned:2000:130"),
+    (1000, 96, 48, [400, 400, 400]),
+    (257, 48, 1, [257]),
+    (4096, 7168, 512, "owned:4096:16"),
+])
+def test_grid_covers_owned_outputs_once_and_loads_stay_in_bounds(rows, k, n, counts):
+    tm, tn, wm, wn, sk = _shape()
+    if isinstance(counts, str):
+        _, owned, groups = counts.split(":")
+        pick = (W.u64(1, 0, int(owned)) % np.uint64(int(groups))).astype(np.int64)
+        counts = np.bincount(pick, minlength=int(groups))
+    counts = list(counts)
+    stride = (k + 31) // 32 * 32 + 32
+    threads, pieces = 64 * wm * wn, sk // 16
+    rows_per_pass = threads // pieces
+    tid = np.arange(threads)
+    piece, r0 = tid % pieces, tid // pieces
+    lane, wave = tid % 64, tid // 64
+    slots = (rows + tm - 1) // tm + len(counts)
+    n_tiles = (n + tn - 1) // tn
+    written = np.zeros((rows, n), np.int32)
+    a_end, w_end = (rows - 1) * stride + k, len(counts) * n * k
+    for b in range(slots * n_tiles):
+        slot, col_tile = divmod(b, n_tiles)
+        hit = _slot(counts, rows, slot, tm)
+        if hit is None:
+            continue
+        g, row0, row_end = hit
+        assert 0 <= row0 < row_end <= rows
+        col0 = col_tile * tn
+        for k0 in sorted({0, (k - 1) // sk * sk}):
+            ok = k0 + piece * 16 < k
+            for p in range(tm // rows_per_pass):
+                row = np.minimum(row0 + r0 + p * rows_per_pass, row_end - 1)
+                addr = row * stride + piece * 16 + k0
+                assert (addr[ok] >= 0).all() and (addr[ok] + 16 <= a_end).all()
+            for p in range(tn // rows_per_pass):
+                col = np.minimum(col0 + r0 + p * rows_per_pass, n - 1)
+                addr = (g * n + col) * k + piece * 16 + k0
+                assert (addr[ok] + 16 <= w_end).all()
+        wr, wc = wave // wn, wave % wn
+        for i in range(tm // wm // 16):
+            for j in range(tn // wn // 16):
+                col = col0 + wc * (tn // wn) + j * 16 + lane % 16
+                for r in range(4):
+                    row = row0 + wr * (tm // wm) + i * 16 + (lane // 16) * 4 + r
+                    m = (row < row_end) & (col < n)
+                    np.add.at(written, (row[m], col[m]), 1)
+    owner = np.full(rows, -1)
+    start = 0
+    for g, c in enumerate(counts):
+        c = max(int(c), 0)
+        owner[start:min(start + c, rows)] = g
+        start += c
+    assert (written[owner >= 0] == 1).all() and (written[owner < 0] == 0).all()
