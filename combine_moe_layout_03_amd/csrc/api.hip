@@ -237,10 +237,7 @@ int moe_combine_src(const void* recv_x, moe_dtype recv_type, size_t recv_x_bytes
 namespace {
 
 // Whether the one-kernel form applies (host logic only).
-bool fused_applies(int32_t bs, int32_t hidden, int32_t topk) {
-  return bs >= 1 && hidden <= moe::kFusedMaxHidden &&
-         static_cast<int64_t>(bs) * topk <= moe::kFusedMaxEntries;
-}
+bool fused_applies(int32_t bs, int32_t hidden, int32_t topk) { return moe::select::fused_applies(bs, hidden, topk); }
 
 // Tokens per workgroup, LDS histogram copies and workgroups of the one
 // kernel: one workgroup per CU (fewer for small batches); as many histogram

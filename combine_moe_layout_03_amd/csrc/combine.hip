@@ -334,30 +334,35 @@ __global__ __launch_bounds__(kCombineThreads) void combine_rows_kernel(RouteArgs
     if (cidx[i] < chunks) store_out<kOut, kElems, kNt>(out, out_base + static_cast<size_t>(cidx[i]) * kElems, acc[i]);
 }
 
+// One case per entry of select::kCombineRowsChunks: kC chunks per lane, four
+// waves, 256 kC chunks of 8 elements per token.
 template <Recv kRecv, Out kOut, int kMaxK>
 hipError_t launch_rows_c(const RouteArgs& a, const uint8_t* recv, const float* w, void* out,
                          hipStream_t stream) {
-  // kC chunks per lane, four waves: 256 kC chunks of 8 elements per token
-  const int chunks = a.hidden / 8;
 #define MOE_ROWS_CASE(C)                                                                                   \
-  if (chunks <= 256 * (C)) {                                                                               \
+  case C:                                                                                                  \
     hipLaunchKernelGGL((combine_rows_kernel<kRecv, kOut, C, kMaxK>), dim3(a.bs), dim3(kCombineThreads), 0, stream, \
                        a, recv, w, out);                                                                   \
-    return hipGetLastError();                                                                              \
+    return hipGetLastError();
+  switch (select::combine_rows_chunks(a.hidden)) {
+    MOE_ROWS_CASE(1)
+    MOE_ROWS_CASE(2)
+    MOE_ROWS_CASE(4)
+    MOE_ROWS_CASE(8)
   }
-  MOE_ROWS_CASE(1)
-  MOE_ROWS_CASE(2)
-  MOE_ROWS_CASE(4)
-  MOE_ROWS_CASE(8)
 #undef MOE_ROWS_CASE
   return hipErrorInvalidValue;
 }
 
+// k <= 8: the row-at-a-time kernel for at most 4 or 8 entries (one case per
+// entry of select::kCombineRowsMaxK); above: the chunk-parallel kernel.
 template <Recv kRecv, Out kOut>
 hipError_t launch_k(const RouteArgs& a, const uint8_t* recv, const float* w, void* out,
                     hipStream_t stream) {
-  if (a.k <= 4) return launch_rows_c<kRecv, kOut, 4>(a, recv, w, out, stream);
-  if (a.k <= 8) return launch_rows_c<kRecv, kOut, 8>(a, recv, w, out, stream);
+  switch (select::combine_rows_max_k(a.k)) {
+    case 4: return launch_rows_c<kRecv, kOut, 4>(a, recv, w, out, stream);
+    case 8: return launch_rows_c<kRecv, kOut, 8>(a, recv, w, out, stream);
+  }
   return launch_shape<kRecv, kOut, 32>(a, recv, w, out, stream);
 }
 

@@ -29,53 +29,28 @@ namespace moe {
 namespace {
 
 constexpr int kDispatchThreads = 256;
+constexpr int kTokensPerBlock = kDispatchThreads / kWave;  // one wave per token
 constexpr int kGroup = 8;  // destinations resolved together
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// 16- and 8-byte stores; kNt marks them non-temporal (streaming).
-template <bool kNt>
-__device__ __forceinline__ void put(uint4* p, const uint4& v) {
-  if constexpr (kNt) {
-    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
-  } else {
-    *p = v;
-  }
-}
-template <bool kNt>
-__device__ __forceinline__ void put(uint2* p, const uint2& v) {
-  if constexpr (kNt) {
-    __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
-  } else {
-    *p = v;
-  }
-}
-
-// kWpt waves per token (a workgroup holds kDispatchThreads / 64 / kWpt
-// tokens).  Wave part p of a token owns the 64-chunk groups p, p + kWpt,
-// p + 2 kWpt, ... of the row; a lane holds chunk lane + 64 * group, i.e.
-// kVpl chunks of 8 elements (16 bytes) each.  With kWpt > 1 the parts combine
-// their maxima through LDS.  kNt selects non-temporal stores.
-template <bool kFp16, bool kQuant, int kVpl, int kWpt, bool kNt>
+// One wave per token; a lane holds chunks lane + 64 i, i < kVpl, of the row
+// (8 elements, 16 bytes each).
+template <bool kFp16, bool kQuant, int kVpl>
 __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(RouteArgs a,
                                                                     const uint16_t* __restrict__ x,
                                                                     uint8_t* __restrict__ recv) {
-  constexpr int kTok = kDispatchThreads / kWave / kWpt;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform(static_cast<int>(threadIdx.x / kWave));
-  const int t = uniform(blockIdx.x * kTok + wave / kWpt);
-  const int part = wave % kWpt;
-  // No early return before the barrier below: inactive waves skip the work.
-  const bool active = t < a.bs;
+  const int t = uniform(blockIdx.x * kTokensPerBlock + wave);
+  if (t >= a.bs) return;
   const int chunks = a.hidden >> 3;
-  const uint4* src = reinterpret_cast<const uint4*>(x + static_cast<size_t>(active ? t : 0) * a.hidden);
+  const uint4* src = reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * a.hidden);
 
   uint4 v[kVpl];
 #pragma unroll
   for (int i = 0; i < kVpl; ++i) {
-    const int c = lane + (i * kWpt + part) * kWave;
-    if (active && c < chunks) {
+    const int c = lane + i * kWave;
+    if (c < chunks) {
       const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + c));
       v[i] = make_uint4(w.x, w.y, w.z, w.w);
     } else {
@@ -84,7 +59,6 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(RouteArgs a,
   }
 
   if constexpr (!kQuant) {
-    if (!active) return;
     for (int j0 = 0; j0 < a.k; j0 += kGroup) {
       int64_t row_off[kGroup];
       bool valid[kGroup];
@@ -95,8 +69,8 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(RouteArgs a,
         uint4* dst = reinterpret_cast<uint4*>(recv + row_off[j]);
 #pragma unroll
         for (int i = 0; i < kVpl; ++i) {
-          const int c = lane + (i * kWpt + part) * kWave;
-          if (c < chunks) put<kNt>(dst + c, v[i]);
+          const int c = lane + i * kWave;
+          if (c < chunks) dst[c] = v[i];
         }
       }
     }
@@ -104,19 +78,9 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(RouteArgs a,
     u16x2 m2 = {0, 0};
 #pragma unroll
     for (int i = 0; i < kVpl; ++i) m2 = max_magnitude(m2, v[i]);
-    uint32_t m = wave_max_u32(m2.x > m2.y ? m2.x : m2.y);
-    if constexpr (kWpt > 1) {
-      __shared__ uint32_t part_max[kDispatchThreads / kWave];
-      if (lane == 0) part_max[wave] = m;
-      __syncthreads();
-      const int first = (wave / kWpt) * kWpt;
-#pragma unroll
-      for (int q = 0; q < kWpt; ++q) m = m > part_max[first + q] ? m : part_max[first + q];
-    }
-    if (!active) return;
-    const float amax = half_to_f32<kFp16>(m);
-    const float s = 127.0f / (amax + 1e-12f);
-    const float inv = 1.0f / s;
+    const uint32_t m = wave_max_u32(m2.x > m2.y ? m2.x : m2.y);
+    float s, inv;
+    row_scale<kFp16>(m, s, inv);
     uint2 q[kVpl];
 #pragma unroll
     for (int i = 0; i < kVpl; ++i) q[i] = quantise_chunk<kFp16>(v[i], s);
@@ -130,34 +94,32 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(RouteArgs a,
         uint8_t* base = recv + row_off[j];
 #pragma unroll
         for (int i = 0; i < kVpl; ++i) {
-          const int c = lane + (i * kWpt + part) * kWave;
-          if (c < chunks) put<kNt>(reinterpret_cast<uint2*>(base) + c, q[i]);
+          const int c = lane + i * kWave;
+          if (c < chunks) reinterpret_cast<uint2*>(base)[c] = q[i];
         }
-        if (part == 0 && lane == 0) *reinterpret_cast<float*>(base + a.scale_off) = inv;
+        if (lane == 0) *reinterpret_cast<float*>(base + a.scale_off) = inv;
       }
     }
   }
 }
 
+// One case per entry of select::kDispatchVpl.
 template <bool kFp16, bool kQuant>
 hipError_t launch_vpl(const RouteArgs& a, const uint16_t* x, uint8_t* recv, hipStream_t stream) {
-  constexpr int kWpt = 1;
-  constexpr int kTok = kDispatchThreads / kWave / kWpt;
-  const int chunks = a.hidden / 8;
-  const int per_lane = (chunks + kWave * kWpt - 1) / (kWave * kWpt);
-  const dim3 grid((a.bs + kTok - 1) / kTok);
+  const dim3 grid((a.bs + kTokensPerBlock - 1) / kTokensPerBlock);
   const dim3 block(kDispatchThreads);
-#define MOE_DISPATCH_CASE(V)                                                                             \
-  if (per_lane <= V) {                                                                                   \
-    hipLaunchKernelGGL((dispatch_kernel<kFp16, kQuant, V, kWpt, false>), grid, block, 0, stream, a, x, recv); \
-    return hipGetLastError();                                                                            \
+#define MOE_DISPATCH_CASE(V)                                                                              \
+  case V:                                                                                                 \
+    hipLaunchKernelGGL((dispatch_kernel<kFp16, kQuant, V>), grid, block, 0, stream, a, x, recv);          \
+    return hipGetLastError();
+  switch (select::dispatch_vpl(a.hidden)) {
+    MOE_DISPATCH_CASE(1)
+    MOE_DISPATCH_CASE(2)
+    MOE_DISPATCH_CASE(4)
+    MOE_DISPATCH_CASE(8)
+    MOE_DISPATCH_CASE(16)
+    MOE_DISPATCH_CASE(32)
   }
-  MOE_DISPATCH_CASE(1)
-  MOE_DISPATCH_CASE(2)
-  MOE_DISPATCH_CASE(4)
-  MOE_DISPATCH_CASE(8)
-  MOE_DISPATCH_CASE(16)
-  MOE_DISPATCH_CASE(32)
 #undef MOE_DISPATCH_CASE
   return hipErrorInvalidValue;
 }

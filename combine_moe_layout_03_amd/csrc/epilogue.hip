@@ -158,16 +158,20 @@ hipError_t launch_shape(const EpilogueArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// Up to 1024 columns one wave per row with 1, 2 or 4 chunks per lane; up to
-// 2048 two waves and up to 4096 four waves per row, 4 chunks per lane.
+// The shape of select::kEpilogueShapes for n columns (one case per entry).
 hipError_t launch_deq_swiglu_quant(const EpilogueArgs& a, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;
-  const int chunks = a.n / 4;
-  if (chunks <= 64) return launch_shape<1, 1>(a, stream);
-  if (chunks <= 128) return launch_shape<2, 1>(a, stream);
-  if (chunks <= 256) return launch_shape<4, 1>(a, stream);
-  if (chunks <= 512) return launch_shape<4, 2>(a, stream);
-  if (chunks <= 1024) return launch_shape<4, 4>(a, stream);
+  const int i = select::epilogue_shape_index(a.n);
+  if (i < 0) return hipErrorInvalidValue;
+  const select::EpilogueShape sh = select::kEpilogueShapes[i];
+#define MOE_EPI_CASE(IT, W) \
+  if (sh.it == (IT) && sh.waves == (W)) return launch_shape<IT, W>(a, stream);
+  MOE_EPI_CASE(1, 1)
+  MOE_EPI_CASE(2, 1)
+  MOE_EPI_CASE(4, 1)
+  MOE_EPI_CASE(4, 2)
+  MOE_EPI_CASE(4, 4)
+#undef MOE_EPI_CASE
   return hipErrorInvalidValue;
 }
 

@@ -420,18 +420,20 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   }
 }
 
+// One case per entry of select::kFusedVpl.
 template <bool kFp16, bool kQuant>
 const void* pick_kernel(int hidden) {
-  const int per_lane = (hidden / 8 + kWave - 1) / kWave;
 #define MOE_FUSED_CASE(V) \
-  if (per_lane <= V) return reinterpret_cast<const void*>(&fused_kernel<kFp16, kQuant, V>);
-  MOE_FUSED_CASE(1)
-  MOE_FUSED_CASE(2)
-  MOE_FUSED_CASE(4)
-  MOE_FUSED_CASE(8)
-  MOE_FUSED_CASE(12)
-  MOE_FUSED_CASE(14)
-  MOE_FUSED_CASE(16)
+  case V: return reinterpret_cast<const void*>(&fused_kernel<kFp16, kQuant, V>);
+  switch (select::fused_vpl(hidden)) {
+    MOE_FUSED_CASE(1)
+    MOE_FUSED_CASE(2)
+    MOE_FUSED_CASE(4)
+    MOE_FUSED_CASE(8)
+    MOE_FUSED_CASE(12)
+    MOE_FUSED_CASE(14)
+    MOE_FUSED_CASE(16)
+  }
 #undef MOE_FUSED_CASE
   return nullptr;
 }

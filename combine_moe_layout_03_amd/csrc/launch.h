@@ -8,26 +8,24 @@
 #include <stdint.h>
 
 #include "moe_ep.h"
+#include "select.h"
 
 namespace moe {
 
 // ---- layout -------------------------------------------------------------------
 // The flat (token, k) entries are cut into tiles of 2048, one workgroup per
 // tile; a workgroup's waves each own a contiguous segment of its tile,
-// walked in rounds of 64 entries.  Up to 512 experts a workgroup has 16 waves
-// of 2 rounds, beyond that 4 waves of 8 rounds (the per-wave LDS counters,
-// waves x E ints, must fit).
+// walked in rounds of 64 entries (shape: select::layout_waves/rounds).
 struct LayoutShape {
   int waves, rounds;
   int64_t tile() const { return static_cast<int64_t>(waves) * rounds * 64; }
 };
-constexpr int kLayoutBigGroupMaxExperts = 512;
 inline LayoutShape layout_shape(int64_t num_experts) {
-  return num_experts <= kLayoutBigGroupMaxExperts ? LayoutShape{16, 2} : LayoutShape{4, 8};
+  const int e = static_cast<int>(num_experts);
+  return LayoutShape{select::layout_waves(e), select::layout_rounds(e)};
 }
 inline int64_t layout_num_tiles(int64_t n, int64_t num_experts) {
-  const int64_t tile = layout_shape(num_experts).tile();
-  return n <= 0 ? 1 : (n + tile - 1) / tile;
+  return select::layout_num_tiles(n, static_cast<int>(num_experts));
 }
 // Workspace: per-tile expert counts plus a bad-id count for every tile but
 // the last (the last tile's workgroup counts its own entries).
@@ -78,8 +76,8 @@ hipError_t launch_combine(const RouteArgs& r, const void* recv_x, Recv recv_type
 
 // ---- fused layout + notify + dispatch ------------------------------------------
 constexpr int kFusedWaves = 16;                 // waves per workgroup
-constexpr int kFusedMaxHidden = 16 * 64 * 8;    // row held in registers: 16 chunks per lane
-constexpr int64_t kFusedMaxEntries = 1 << 16;   // bs * k: every workgroup counts all ids
+constexpr int kFusedMaxHidden = select::kFusedMaxHidden;     // row held in registers
+constexpr int64_t kFusedMaxEntries = select::kFusedMaxEntries;  // bs * k: every workgroup counts all ids
 constexpr size_t kFusedMaxLds = 64 * 1024;
 constexpr int kFusedMaxCopiesLog2 = 3;          // up to 8 copies of each LDS histogram
 

@@ -219,12 +219,15 @@ hipError_t launch_layout(const int32_t* topk_idx, int32_t n, int32_t num_experts
                          int32_t* send_token_idx, int32_t* bad_count, void* workspace,
                          hipStream_t stream) {
   const LayoutShape shape = layout_shape(num_experts);
-  if (shape.waves == 16) {
+  if (shape.waves == 16 && shape.rounds == 2) {
     return launch_shape<16, 2>(topk_idx, n, num_experts, epr, ranks, token_per_expert, token_per_rank,
                                send_token_idx, bad_count, workspace, stream);
   }
-  return launch_shape<4, 8>(topk_idx, n, num_experts, epr, ranks, token_per_expert, token_per_rank,
-                            send_token_idx, bad_count, workspace, stream);
+  if (shape.waves == 4 && shape.rounds == 8) {
+    return launch_shape<4, 8>(topk_idx, n, num_experts, epr, ranks, token_per_expert, token_per_rank,
+                              send_token_idx, bad_count, workspace, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe

@@ -2,13 +2,17 @@
 the GPU against the CPU oracle, through the C ABI.
 
 Bar: bit-exact int32 outputs (integer sums, exact on both sides), rows owned
-by no expert left as they were, on every row of the small cases and on
-sampled rows of the shape the benchmark times and of the layer's second
-matmul.  The cases cover several row
-and column tiles with ragged ends, k that ends inside a 128-byte stage,
-empty and negative counts, counts past the row capacity, more experts than
-one wave scans at once, and the int8 receive buffer used in place.
+by no expert left as they were, on every row of the small cases; at the
+shape the benchmark times and at the layer's second matmul, on every row of
+each expert's first whole 128-row tile and of its last (partial) tile --
+so every row on both sides of every expert boundary, and the output's last
+rows -- plus rows drawn at random, all columns of each.  The cases cover
+several row and column tiles with ragged ends, k that ends inside a 256-byte
+stage, empty and negative counts, counts past the row capacity, more experts
+than one wave scans at once, and the int8 receive buffer used in place.
 """
+
+import concurrent.futures
 
 import numpy as np
 import pytest
@@ -45,14 +49,61 @@ def run_gpu(case, rows=None):
     return out.cpu().numpy()
 
 
+def oracle_rows(case, rows):
+    """The oracle on the listed rows, split over host threads (the oracle is
+    plain C called through ctypes, which releases the interpreter lock, and
+    keeps no state between calls)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    parts = [p for p in np.array_split(rows, 16) if p.size]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(parts)) as ex:
+        res = list(ex.map(lambda p: oracle.grouped_gemm_i8(case.a, case.k, case.group_count, case.w, rows=p),
+                          parts))
+    return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])
+
+
 def assert_same(case, got, what, rows=None):
-    exp, grp = oracle.grouped_gemm_i8(case.a, case.k, case.group_count, case.w, rows=rows)
+    if rows is None:
+        exp, grp = oracle.grouped_gemm_i8(case.a, case.k, case.group_count, case.w)
+    else:
+        exp, grp = oracle_rows(case, rows)
     sel = np.arange(case.rows) if rows is None else np.asarray(rows)
     got = got[sel]
     owned = grp >= 0
     bad = np.nonzero(np.any(got[owned] != exp[owned], axis=1))[0]
     assert bad.size == 0, f"{what}: rows {sel[owned][bad[:10]].tolist()} differ"
     assert (got[~owned] == SENTINEL).all(), f"{what}: a row of no expert was written"
+
+
+def _tile_m() -> int:
+    """Rows of one output tile, as the library's header sets it."""
+    import os
+    import re
+
+    hdr = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "combine_moe_layout_03_amd",
+                       "csrc", "gemm.h")
+    return int(re.search(r"kGemmTileM = (\d+)", open(hdr).read()).group(1))
+
+
+TILE_M = _tile_m()
+
+
+def boundary_tile_rows(case, seed, n_random=32):
+    """Every row of each expert's first whole tile and of its last tile (the
+    partial one when the count is not a multiple of the tile), the rows of
+    the buffer's last tile, and `n_random` random rows."""
+    counts = np.maximum(case.group_count.astype(np.int64), 0)
+    starts = np.cumsum(counts) - counts
+    sel = []
+    for s0, c in zip(starts, counts):
+        s0, c = int(min(s0, case.rows)), int(min(c, case.rows - min(s0, case.rows)))
+        if c == 0:
+            continue
+        sel.append(np.arange(s0, s0 + min(c, TILE_M)))
+        last = s0 + (c - 1) // TILE_M * TILE_M
+        sel.append(np.arange(last, s0 + c))
+    sel.append(np.arange(max(case.rows - TILE_M, 0), case.rows))
+    sel.append((W.u64(seed, 0, n_random) % np.uint64(case.rows)).astype(np.int64))
+    return np.unique(np.concatenate(sel))
 
 
 @pytest.mark.parametrize("rows,k,n,groups,counts,seed", [
@@ -80,34 +131,32 @@ def test_gemm_matches_oracle(rows, k, n, groups, counts, seed):
     assert_same(case, got, f"rows={rows} k={k} n={n}")
 
 
-def test_gemm_full_size_sampled_rows():
+def test_gemm_full_size_tile_rows():
     """The benchmark's shape (32768 rows of 7200 bytes, k = 7168, n = 4096,
-    16 experts) in the same launch; the oracle checks the first and last row
-    of every expert and 32 rows drawn at random."""
+    16 experts) in the same launch: every row of each expert's first and last
+    row tiles, the last rows of the buffer and 32 random rows, all 4096
+    columns (every column tile) of each."""
     cfg = W.GEMM_CONFIG
     case = W.gemm_case(cfg["seed"], cfg["rows"], cfg["k"], cfg["n"], cfg["groups"],
                        stride=align32(cfg["k"]) + 32)
     log("grouped gemm full size")
     got = run_gpu(case)
-    ends = np.cumsum(case.group_count)
-    starts = ends - case.group_count
-    pick = W.u64(7, 0, 32) % np.uint64(case.rows)
-    rows = np.unique(np.concatenate([starts, ends - 1, pick.astype(np.int64)]))
+    rows = boundary_tile_rows(case, 7)
+    assert rows.size >= 16 * TILE_M
+    log(f"grouped gemm full size: oracle on {rows.size} rows")
     assert_same(case, got, "full size", rows=rows)
 
 
-def test_gemm_second_matmul_shape_sampled_rows():
+def test_gemm_second_matmul_shape_tile_rows():
     """The shape of the layer's second expert matmul on the same share: the
     epilogue's int8 rows (k = 2048 codes in 2080-byte rows) times weights
-    [16][7168][2048]; first and last row of every expert and 32 random rows."""
+    [16][7168][2048]; the same row tiles as above, all 7168 columns."""
     rows, k, n, groups = 32768, 2048, 7168, 16
     case = W.gemm_case(3002, rows, k, n, groups, stride=align32(k) + 32)
     log("grouped gemm second-matmul shape")
     got = run_gpu(case)
-    ends = np.cumsum(case.group_count)
-    starts = ends - case.group_count
-    pick = W.u64(8, 0, 32) % np.uint64(rows)
-    sel = np.unique(np.concatenate([starts, ends - 1, pick.astype(np.int64)]))
+    sel = boundary_tile_rows(case, 8)
+    log(f"grouped gemm second-matmul shape: oracle on {sel.size} rows")
     assert_same(case, got, "second-matmul shape", rows=sel)
 
 

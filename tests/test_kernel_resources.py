@@ -11,57 +11,21 @@ few spilled scalars in the one instantiation that needs more registers than
 a 1024-thread workgroup allows (the fused int8 kernel for 7168 < h <= 8192).
 """
 
-import concurrent.futures
-import glob
-import os
 import re
-import runpy
-import shutil
-import subprocess
 
 import pytest
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-CSRC = os.path.join(ROOT, "combine_moe_layout_03_amd", "csrc")
+import kernel_remarks
 
 # fused_kernel<kFp16, kQuant = true, kVpl = 16>: up to 32 bytes of spilled scalars
 SPILL_ALLOWED = re.compile(r"fused_kernelILb[01]ELb1ELi16E")
 
 
-def _resource_remarks(src: str, hipcc: str, flags) -> str:
-    cmd = [hipcc, *flags, "-c", src, "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    assert r.returncode == 0, f"hipcc failed on {src}:\n{r.stderr[-2000:]}"
-    return r.stderr
-
-
-def _parse(text: str):
-    """{kernel symbol: {field: value}} from the remark lines."""
-    out, cur = {}, None
-    for line in text.splitlines():
-        m = re.search(r"remark: Function Name: (\S+)", line)
-        if m:
-            cur = out.setdefault(m.group(1), {})
-            continue
-        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^\]]*\])?: (\S+) \[-Rpass-analysis", line)
-        if m and cur is not None:
-            cur[m.group(1).strip()] = m.group(2)
-    return out
-
-
 @pytest.fixture(scope="module")
 def kernels():
-    b = runpy.run_path(os.path.join(ROOT, "combine_moe_layout_03_amd", "build.py"))
-    hipcc = b["HIPCC"]
-    if not (os.path.exists(hipcc) or shutil.which(hipcc)):
+    if not kernel_remarks.hipcc_available():
         pytest.skip("hipcc not available")
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(6, len(sources))) as ex:
-        texts = list(ex.map(lambda s: _resource_remarks(s, hipcc, b["CXXFLAGS"]), sources))
-    found = {}
-    for t in texts:
-        found.update(_parse(t))
-    return found
+    return kernel_remarks.kernel_remarks()
 
 
 def test_every_kernel_reports_resources(kernels):
