@@ -14,11 +14,16 @@ expert GEMMs).  HIP events recorded on the stream the kernels run on (created wi
 system-scope fence, which only serves host visibility) time each stage;
 flushes are outside the timed intervals.  ``ms_per_step`` is the mean
 of layout+notify+dispatch+combine over the K steps and ``value`` is bs divided
-by it (tokens/s, whole pipeline).  The un-flushed back-to-back rate (eager,
-and replayed from one captured HIP graph), the dispatch and combine kernels
-timed on their own (``dispatch_combine_kernels_alone``: dispatch + combine
-without the layout work the fused launch carries), a plain device copy and
-the CPU oracle are reported beside it, labelled.
+by it (tokens/s, whole pipeline).  Reported beside it, labelled:
+``steady_state``, the back-to-back step replayed from one captured HIP graph
+with nothing flushed (every write's cost inside the timed region, with the
+caches as a running pipeline leaves them); ``write_back_inclusive``, dispatch
+plus the flush after it minus the same flush on clean caches (dispatch's rows
+partly stay in the 256 MB Infinity Cache when the kernel ends and are written
+back during the next flush); per-stage GB/s beside a plain device copy;
+the dispatch and combine kernels timed on their own
+(``dispatch_combine_kernels_alone``: without the layout work the fused launch
+carries); and the CPU oracle.
 
 ``--stage epilogue`` times the expert-side epilogue kernel (dequantise the
 first expert GEMM's int32 output, SwiGLU, requantise to int8 rows) alone, on
@@ -54,7 +59,7 @@ METRIC = "dispatch+combine tokens/s and HBM GB/s (% of peak) at bs=4096 h=7168 t
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "combine_moe_layout_03_amd", "csrc")
 # A kernel's source: its own file and the headers every kernel file includes.
-KERNEL_HEADERS = [os.path.join(CSRC, f) for f in ("device_util.h", "launch.h", "quant.h")]
+KERNEL_HEADERS = [os.path.join(CSRC, f) for f in ("device_util.h", "launch.h", "quant.h", "select.h")]
 KERNEL_SOURCES = {
     "dispatch": [os.path.join(CSRC, "dispatch.hip")] + KERNEL_HEADERS,
     "combine": [os.path.join(CSRC, "combine.hip")] + KERNEL_HEADERS,
@@ -177,6 +182,18 @@ def gemm_bytes(rows: int, n: int, k: int, groups: int) -> int:
     return rows * k + groups * n * k + rows * n * 4 + groups * 4
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), else what platform reports."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(w, quant: bool, budget_s: float):
     """The oracle as it stands, single-threaded on a host core, over the full
     workload, repeated until about ``budget_s`` seconds have passed."""
@@ -195,7 +212,7 @@ def cpu_baseline(w, quant: bool, budget_s: float):
     return dict(value=w.bs * passes / el, unit="tokens/s", cores=1, kind="oracle",
                 sample=f"full {w.name} workload ({w.bs} tokens, all four stages), {passes} pass(es) "
                        f"in {el:.1f} s on one host thread",
-                host_cpu=platform.processor() or platform.machine(), host_nproc=os.cpu_count())
+                host_cpu=host_cpu_model(), host_nproc=os.cpu_count())
 
 
 def main(argv=None) -> int:
@@ -225,10 +242,19 @@ def main(argv=None) -> int:
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, then WRITE_SIZE) of a bench "
                          "run into profiles/traffic_*.json and exit")
+    ap.add_argument("--counters", choices=["flushed", "unflushed"],
+                    help="a short run for rocprofv3 --pmc: W + K steps of the fused path, then K steps of the "
+                         "separate stages, flushed before each stage or back to back, then the 1 GiB copy "
+                         "kernel the counters are calibrated on; prints what it ran and exits")
+    ap.add_argument("--ingest-dram", nargs=2, metavar=("FLUSHED_CSV", "UNFLUSHED_CSV"),
+                    help="turn the DRAM request counters of two --counters runs (flushed, unflushed) into "
+                         "profiles/dram_requests_<workload>_<mode>.json and exit")
     args = ap.parse_args(argv)
 
     if args.ingest_pmc:
         return ingest_pmc(args, *args.ingest_pmc)
+    if args.ingest_dram:
+        return ingest_dram(args, *args.ingest_dram)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -269,6 +295,8 @@ def main(argv=None) -> int:
     if args.sources > 1:
         del buf
         return bench_sources(args, M, torch, w, x, idx, wts, quant, do_flush, stream)
+    if args.counters:
+        return counter_run(args, torch, w, buf, x, idx, wts, flush, do_flush)
 
     fused = args.path == "fused"
     if fused and not M.moe_fused_supported(w.bs, w.hidden, w.topk, w.expert_num_per_rank, w.rank_size,
@@ -322,8 +350,24 @@ def main(argv=None) -> int:
     lay_ms = [0.0 if fused else hev.ms(e[0], e[1]) for e in ev]
     dis_ms = [hev.ms(e[1], e[2]) for e in ev]
     com_ms = [hev.ms(e[3], e[4]) for e in ev]
+    # the dispatch launch plus the flush after it: the flush also writes back
+    # whatever dispatch left dirty in the caches
+    dis_flush_ms = [hev.ms(e[1], e[3]) for e in ev]
     step_ms = [a + b + c for a, b, c in zip(lay_ms, dis_ms, com_ms)]
     ms_per_step = sum(step_ms) / len(step_ms)
+
+    # the same flush on caches holding only clean lines (a flush after a
+    # flush): subtracted from the above, it leaves dispatch with its
+    # write-back
+    log(f"flush on clean caches x{args.steps}")
+    fev = [(hev.new(), hev.new()) for _ in range(args.steps)]
+    for f0, f1 in fev:
+        do_flush()
+        hev.record(f0, stream)
+        do_flush()
+        hev.record(f1, stream)
+    torch.cuda.synchronize()
+    flush_clean_ms = [hev.ms(f0, f1) for f0, f1 in fev]
 
     # un-flushed back-to-back pipeline (labelled; combine may hit the Infinity Cache)
     log("un-flushed back-to-back")
@@ -413,9 +457,11 @@ def main(argv=None) -> int:
     dis_mean = statistics.mean(dis_ms)
     com_mean = statistics.mean(com_ms)
     # the launch that carries the dispatch: the dispatch kernel, or the fused
-    # kernel (which also reads the ids for the layout and writes the slots)
+    # kernel, which reads the ids once from HBM (dispatch's own index read;
+    # its other workgroups' reads of them hit L2) and writes the slots (in
+    # place of dispatch's slot read), so its bytes are dispatch's
     first = "fused" if fused else "dispatch"
-    b_first = b_dis + b_lay if fused else b_dis
+    b_first = b_dis
     dom = first if dis_mean >= com_mean else "combine"
     dom_ms = dis_mean if dom == first else com_mean
     dom_bytes = b_first if dom == first else b_com
@@ -427,6 +473,38 @@ def main(argv=None) -> int:
         stages = (("layout+notify+dispatch", dis_ms), ("combine", com_ms))
     else:
         stages = (("layout+notify", lay_ms), ("dispatch", dis_ms), ("combine", com_ms))
+
+    # write-back-inclusive dispatch, and the steady state (graph replay of
+    # back-to-back steps, nothing flushed): the whole step with every write's
+    # cost paid inside the timed region
+    dis_wb_mean = statistics.mean(dis_flush_ms) - statistics.mean(flush_clean_ms)
+    gb = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
+    write_back = {
+        "dispatch_us": dis_wb_mean * 1e3,
+        "dispatch_plus_flush_us": statistics.mean(dis_flush_ms) * 1e3,
+        "flush_on_clean_caches_us": statistics.mean(flush_clean_ms) * 1e3,
+        "dispatch_combine_us": (dis_wb_mean + com_mean) * 1e3,
+        "dispatch_combine_tokens_per_s": w.bs / ((dis_wb_mean + com_mean) * 1e-3),
+        "dispatch_combine_hbm_frac": gb(b_dis + b_com, dis_wb_mean + com_mean) / HBM_PEAK_GBPS,
+        "how": "dispatch launch + the 1 GiB read-flush after it, minus the same flush on clean caches",
+    }
+    steady = None
+    if graph_ms is not None:
+        steady = {
+            "ms_per_step": graph_ms,
+            "tokens_per_s": w.bs / (graph_ms * 1e-3),
+            "hbm_gbps": gb(b_dis + b_com, graph_ms),
+            "hbm_frac": gb(b_dis + b_com, graph_ms) / HBM_PEAK_GBPS,
+            "eager_ms_per_step": unflushed_ms,
+            "how": f"{GRAPH_STEPS} back-to-back steps (layout + notify + dispatch + combine) captured in one "
+                   "HIP graph and replayed, nothing flushed; bytes are the step's algorithmic bytes",
+        }
+    stage_gbps = {
+        "dispatch_flushed": gb(b_first, dis_mean),
+        "dispatch_write_back_inclusive": gb(b_first, dis_wb_mean),
+        "combine_flushed": gb(b_com, com_mean),
+        "copy_ceiling": copy_gbps,
+    }
 
     cpu = None
     if args.cpu_budget > 0:
@@ -472,6 +550,9 @@ def main(argv=None) -> int:
         "unflushed_ms_per_step": unflushed_ms,
         "unflushed_tokens_per_s": w.bs / (unflushed_ms * 1e-3),
         "graph_unflushed_ms_per_step": graph_ms,
+        "steady_state": steady,
+        "write_back_inclusive": write_back,
+        "stage_gbps": stage_gbps,
         "dispatch_combine_kernels_alone": kernels_only,
         "copy_ceiling_gbps": copy_gbps,
         "wall_ms_per_step_incl_flush": wall / args.steps * 1e3,
@@ -543,7 +624,7 @@ def bench_epilogue(args, M, torch, W, dev) -> int:
                 break
         cpu = dict(value=case.rows * passes / el, unit="rows/s", cores=1, kind="oracle",
                    sample=f"all {case.rows} rows x n={case.n}, {passes} pass(es) in {el:.1f} s on one host thread",
-                   host_cpu=platform.processor() or platform.machine(), host_nproc=os.cpu_count())
+                   host_cpu=host_cpu_model(), host_nproc=os.cpu_count())
     line = {
         "metric": EPILOGUE_METRIC,
         "value": case.rows / (mean_us * 1e-6),
@@ -578,7 +659,7 @@ def bench_epilogue(args, M, torch, W, dev) -> int:
 
 def bench_gemm(args, M, torch, W, dev) -> int:
     """The first expert matmul alone on one GPU's share of the large shape on
-    a 16-rank expert-parallel group: 32768 int8 rows (7200-byte receive rows)
+    a 16-rank expert-parallel group: 32768 int8 rows (7296-byte receive rows)
     spread over 16 experts as uniform routing spreads them, k = 7168, n = 4096
     (gate and up columns of an FFN of width 2048).  The caches are flushed
     before each timed launch."""
@@ -658,7 +739,7 @@ def bench_gemm(args, M, torch, W, dev) -> int:
         cpu = dict(value=done / el, unit="rows/s", cores=1, kind="oracle",
                    sample=f"{done} random rows of the {rows} (each: {n} x {k} products), {el:.1f} s on one "
                           "host thread",
-                   host_cpu=platform.processor() or platform.machine(), host_nproc=os.cpu_count())
+                   host_cpu=host_cpu_model(), host_nproc=os.cpu_count())
     line = {
         "metric": GEMM_METRIC,
         "value": owned / (mean_us * 1e-6),
@@ -802,6 +883,112 @@ def bench_sources(args, M, torch, w, x, idx, wts, quant: bool, do_flush, stream)
     return 0
 
 
+def counter_run(args, torch, w, buf, x, idx, wts, flush, do_flush) -> int:
+    """Launches for a rocprofv3 --pmc run: the fused path and the separate
+    stages, each K times, either flushed before every stage or back to back,
+    then the copy kernel (torch.neg over the 1 GiB flush buffer: 1 GiB read,
+    1 GiB written) on which the counters are calibrated."""
+    flushed = args.counters == "flushed"
+    maybe_flush = do_flush if flushed else (lambda: None)
+    log(f"counter run ({args.counters}): warm-up x{args.warmup}")
+    for _ in range(args.warmup):
+        maybe_flush()
+        buf.run(x, idx, wts, fused=True)
+    log(f"fused path x{args.steps}")
+    for _ in range(args.steps):
+        maybe_flush()
+        buf.layout_notify_dispatch(x, idx)
+        maybe_flush()
+        buf.combine(idx, wts)
+    log(f"separate stages x{args.steps}")
+    for _ in range(args.steps):
+        maybe_flush()
+        buf.layout(idx)
+        buf.notify()
+        buf.dispatch(x, idx)
+        maybe_flush()
+        buf.combine(idx, wts)
+    dst = torch.empty_like(flush)
+    for _ in range(3):
+        torch.neg(flush, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"counter_run": args.counters, "workload": args.workload, "mode": args.mode,
+                      "steps": args.steps, "warmup": args.warmup, "copy_bytes_each_way": flush.numel() * 4}),
+          flush=True)
+    return 0
+
+
+DRAM_COUNTERS = ("TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum", "TCC_EA0_RDREQ_DRAM_sum",
+                 "TCC_EA0_WRREQ_DRAM_sum")
+
+
+def _read_counters(path: str):
+    """{(kernel name, counter name): [value per dispatch]} from a rocprofv3
+    counter_collection.csv."""
+    import csv
+
+    out = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            name = row.get("Kernel_Name") or row.get("Kernel-Name") or ""
+            ctr = row.get("Counter_Name") or row.get("Counter-Name") or ""
+            val = row.get("Counter_Value") or row.get("Counter-Value")
+            if val is None:
+                continue
+            out.setdefault((name, ctr), []).append(float(val))
+    return out
+
+
+def ingest_dram(args, flushed_csv: str, unflushed_csv: str) -> int:
+    """Per-kernel DRAM-bound request counts of the fused, dispatch and
+    combine kernels (median per dispatch) in both modes, in bytes: the 32-byte
+    counters times 32, each scaled by what it reads for the 1 GiB copy kernel
+    against the copy's bytes.  These are requests leaving L2 for the memory
+    side; the 256 MB Infinity Cache sits behind them, so they bound HBM
+    traffic from above rather than measure it."""
+    import workloads as W
+
+    c = W.CONFIGS[args.workload]
+    quant = args.mode == "int8"
+    b_dis, b_com, _ = algorithmic_bytes(c["bs"], c["hidden"], c["topk"], quant)
+    copy_bytes = args.flush_mib * (1 << 20)
+    kernels = (("fused", "fused_kernel", b_dis), ("dispatch", "dispatch_kernel", b_dis),
+               ("combine", "combine_rows_kernel", b_com))
+    rec = {"workload": args.workload, "mode": args.mode, "counters": list(DRAM_COUNTERS),
+           "copy_bytes_each_way": copy_bytes, "runs": {},
+           "note": "L2-to-memory-side requests destined for DRAM; the Infinity Cache is behind them"}
+    for run, path in (("flushed", flushed_csv), ("unflushed", unflushed_csv)):
+        t = _read_counters(path)
+
+        def med(sym, ctr):
+            vals = [v for (k, cn), vs in t.items() if sym in k and cn == ctr for v in vs]
+            return statistics.median(vals) if vals else None
+
+        rd_copy = med("neg", "TCC_EA0_RDREQ_DRAM_32B_sum")
+        wr_copy = med("neg", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum")
+        cal = {"read_bytes_per_unit": copy_bytes / rd_copy if rd_copy else None,
+               "write_bytes_per_unit": copy_bytes / wr_copy if wr_copy else None}
+        out = {"copy_calibration": {"read_32B_units": rd_copy, "write_32B_units": wr_copy, **cal}}
+        for name, sym, alg in kernels:
+            rd, wr = med(sym, "TCC_EA0_RDREQ_DRAM_32B_sum"), med(sym, "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum")
+            if rd is None or wr is None:
+                continue
+            rb = rd * (cal["read_bytes_per_unit"] or 32.0)
+            wb = wr * (cal["write_bytes_per_unit"] or 32.0)
+            out[name] = {"rdreq_dram_32B": rd, "wrreq_write_dram_32B": wr,
+                         "rdreq_dram": med(sym, "TCC_EA0_RDREQ_DRAM_sum"),
+                         "wrreq_dram": med(sym, "TCC_EA0_WRREQ_DRAM_sum"),
+                         "read_bytes": rb, "write_bytes": wb, "algorithmic_bytes": alg,
+                         "over_algorithmic": (rb + wb) / alg}
+        rec["runs"][run] = out
+    rec["source_sha256_16"] = {k: source_hash(KERNEL_SOURCES[k]) for k in ("fused", "dispatch", "combine")}
+    path = os.path.join(PROFILES, f"dram_requests_{args.workload}_{args.mode}.json")
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(path, json.dumps(rec))
+    return 0
+
+
 def _read_counter_csv(path: str):
     """{kernel name: [value per dispatch]} from a rocprofv3 counter_collection.csv."""
     import csv
@@ -859,7 +1046,7 @@ def ingest_pmc(args, fetch_csv: str, write_csv: str) -> int:
         b_dis, b_com, b_lay = algorithmic_bytes(c["bs"], c["hidden"], c["topk"], quant)
         kernels = (("dispatch", ("dispatch_kernel",), b_dis),
                    ("combine", ("combine_rows_kernel", "combine_kernel"), b_com),
-                   ("fused", ("fused_kernel",), b_dis + b_lay))
+                   ("fused", ("fused_kernel",), b_dis))
     for kernel, symbols, alg in kernels:
         if isinstance(symbols, str):
             symbols = (symbols,)

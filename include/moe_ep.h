@@ -81,10 +81,14 @@ enum {
 /* Bytes of one receive-buffer row for hidden size `hidden` and receive type
  * `recv` (page 2.5 and 2.2.1):
  *   MOE_BF16, MOE_FP16:   2 * hidden (the row as is);
- *   MOE_INT8_ROWSCALE:    align32(hidden) + 32 -- int8 codes at bytes
- *                         [0, hidden), the float inverse scale 1/s at byte
- *                         align32(hidden) (UB_ALIGN_SIZE = 32), the other
- *                         bytes are padding with unspecified contents.
+ *   MOE_INT8_ROWSCALE:    align32(hidden) + 32 rounded up to a multiple of
+ *                         128 -- int8 codes at bytes [0, hidden), the float
+ *                         inverse scale 1/s at byte align32(hidden)
+ *                         (UB_ALIGN_SIZE = 32); the other bytes are padding
+ *                         with unspecified contents.  The page places the
+ *                         scale but leaves the row stride open; rows here
+ *                         start on 128-byte cache-line boundaries (7296 bytes
+ *                         at hidden = 7168).
  * Host only; writes *bytes.  Errors: NULL_PTR, BAD_SHAPE (hidden < 1),
  * BAD_DTYPE. */
 int moe_recv_row_bytes(int32_t hidden, moe_dtype recv, size_t* bytes);

@@ -39,15 +39,22 @@ def host_bits(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def int8_row_bytes(hidden: int) -> int:
+    """Bytes of an int8 receive row, as the library sizes it (moe_recv_row_bytes)."""
+    import combine_moe_layout_03_amd as M
+
+    return M.moe_recv_row_bytes(hidden, M.MOE_INT8_ROWSCALE)
+
+
 def unpack_recv(recv_x: torch.Tensor, hidden: int, kind: str) -> Dict[str, np.ndarray]:
     """Receive buffer bytes -> canonical rows (passthrough) or codes + inv.
 
     Layout (include/moe_ep.h): passthrough rows are 2*hidden bytes; int8 rows
-    are align32(hidden) + 32 bytes with the codes first and the float inverse
-    scale at byte align32(hidden)."""
+    are moe_recv_row_bytes(hidden) bytes with the codes first and the float
+    inverse scale at byte align32(hidden)."""
     raw = recv_x.cpu().numpy()
     if kind == "int8":
-        rb = align32(hidden) + 32
+        rb = int8_row_bytes(hidden)
         m = raw.reshape(-1, rb)
         codes = np.ascontiguousarray(m[:, :hidden]).view(np.int8)
         off = align32(hidden)
@@ -62,7 +69,7 @@ def pack_recv(canon: Dict[str, np.ndarray], hidden: int, kind: str) -> np.ndarra
     GPU combine an oracle-made buffer)."""
     if kind == "int8":
         rows = canon["codes"].shape[0]
-        rb = align32(hidden) + 32
+        rb = int8_row_bytes(hidden)
         m = np.zeros((rows, rb), np.uint8)
         m[:, :hidden] = canon["codes"].view(np.uint8)
         off = align32(hidden)

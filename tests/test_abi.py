@@ -41,7 +41,8 @@ def test_header_constants_match_binding(M):
         assert getattr(M, name) == val
 
 
-@pytest.mark.parametrize("hidden,dtype,expect", [(7168, 3, 7200), (1000, 3, 1056), (8, 3, 64),
+@pytest.mark.parametrize("hidden,dtype,expect", [(7168, 3, 7296), (1000, 3, 1152), (8, 3, 128),
+                                                 (2048, 3, 2176), (4064, 3, 4096),
                                                  (8, 0, 16), (7168, 1, 14336)])
 def test_recv_row_bytes(M, hidden, dtype, expect):
     assert M.moe_recv_row_bytes(hidden, dtype) == expect
@@ -253,7 +254,7 @@ def test_rank_division_by_multiply_high_is_exact():
 
 def test_epilogue_rejects_on_host(M):
     L = M._lib
-    rb = 2048 + 32  # moe_recv_row_bytes(2048, int8)
+    rb = 2176  # moe_recv_row_bytes(2048, int8)
     ok = dict(rows=16, n=2048, stride=4, out_bytes=16 * rb)
 
     def call(acc=P, rows=ok["rows"], n=ok["n"], ws=P, ts=P, stride=ok["stride"], out=P,

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_util import GpuRun, align32, dev_f32, dev_i32, log
+from gpu_util import GpuRun, align32, dev_f32, dev_i32, int8_row_bytes, log
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,7 @@ def M():
 
 
 def unpack_rows(out: torch.Tensor, rows: int, n: int):
-    rb = align32(n) + 32
+    rb = int8_row_bytes(n)
     raw = out.cpu().numpy()[: rows * rb].reshape(rows, rb)
     codes = np.ascontiguousarray(raw[:, :n]).view(np.int8)
     inv = np.ascontiguousarray(raw[:, align32(n):align32(n) + 4]).view(np.float32).reshape(-1)
@@ -66,7 +66,7 @@ def test_epilogue_matches_oracle(rows, n, seed):
     log(f"epilogue rows={rows} n={n} seed={seed}")
     out = run_gpu(case, guard_rows=2)
     assert_same(case, out, f"rows={rows} n={n}")
-    rb = align32(n) + 32
+    rb = int8_row_bytes(n)
     tail = out.cpu().numpy()[rows * rb:]
     assert np.all(tail == 0xA5), "bytes past the last row were written"
 

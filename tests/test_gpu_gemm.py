@@ -20,7 +20,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_util import GpuRun, align32, dev_i32, log
+from gpu_util import GpuRun, align32, dev_i32, int8_row_bytes, log
 
 pytestmark = pytest.mark.gpu
 
@@ -132,13 +132,13 @@ def test_gemm_matches_oracle(rows, k, n, groups, counts, seed):
 
 
 def test_gemm_full_size_tile_rows():
-    """The benchmark's shape (32768 rows of 7200 bytes, k = 7168, n = 4096,
+    """The benchmark's shape (32768 receive rows of 7296 bytes, k = 7168, n = 4096,
     16 experts) in the same launch: every row of each expert's first and last
     row tiles, the last rows of the buffer and 32 random rows, all 4096
     columns (every column tile) of each."""
     cfg = W.GEMM_CONFIG
     case = W.gemm_case(cfg["seed"], cfg["rows"], cfg["k"], cfg["n"], cfg["groups"],
-                       stride=align32(cfg["k"]) + 32)
+                       stride=int8_row_bytes(cfg["k"]))
     log("grouped gemm full size")
     got = run_gpu(case)
     rows = boundary_tile_rows(case, 7)
@@ -149,10 +149,10 @@ def test_gemm_full_size_tile_rows():
 
 def test_gemm_second_matmul_shape_tile_rows():
     """The shape of the layer's second expert matmul on the same share: the
-    epilogue's int8 rows (k = 2048 codes in 2080-byte rows) times weights
+    epilogue's int8 rows (k = 2048 codes in 2176-byte rows) times weights
     [16][7168][2048]; the same row tiles as above, all 7168 columns."""
     rows, k, n, groups = 32768, 2048, 7168, 16
-    case = W.gemm_case(3002, rows, k, n, groups, stride=align32(k) + 32)
+    case = W.gemm_case(3002, rows, k, n, groups, stride=int8_row_bytes(k))
     log("grouped gemm second-matmul shape")
     got = run_gpu(case)
     sel = boundary_tile_rows(case, 8)
