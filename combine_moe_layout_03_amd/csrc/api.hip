@@ -4,6 +4,7 @@
 // allocates, frees or waits.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <limits>
 
 #include "launch.h"
@@ -21,6 +22,26 @@ int hip_status(hipError_t err) {
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Compute units of the current device, queried once per device (the fused
+// kernel's grid is one workgroup per CU); later calls only read the cache.
+constexpr int kMaxCachedDevices = 64;
+std::atomic<int> g_device_cus[kMaxCachedDevices];  // 0: not queried yet
+
+hipError_t current_device_cus(int* cus) {
+  int device = 0;
+  hipError_t err = hipGetDevice(&device);
+  if (err != hipSuccess) return err;
+  const bool cached = device >= 0 && device < kMaxCachedDevices;
+  int c = cached ? g_device_cus[device].load(std::memory_order_relaxed) : 0;
+  if (c == 0) {
+    err = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, device);
+    if (err != hipSuccess) return err;
+    if (cached) g_device_cus[device].store(c, std::memory_order_relaxed);
+  }
+  *cus = c;
+  return hipSuccess;
+}
 
 size_t align32(int64_t v) { return static_cast<size_t>((v + 31) / 32 * 32); }
 
@@ -329,9 +350,8 @@ int moe_layout_notify_dispatch(const void* x, moe_dtype x_type, int32_t bs, int3
                         ranks, quant_int8, recv_x, recv_x_bytes, stream);
   }
 
-  int device = 0, cus = 0;
-  hipError_t err = hipGetDevice(&device);
-  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  int cus = 0;
+  const hipError_t err = current_device_cus(&cus);
   if (err != hipSuccess) return hip_status(err);
   moe::FusedArgs a{};
   a.x = static_cast<const uint16_t*>(x);

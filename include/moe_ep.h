@@ -24,7 +24,9 @@
  * Conventions for every entry point:
  *  - Pointers named as device pointers must point to device memory (or to
  *    memory the device can address); the library never allocates, frees or
- *    keeps device memory, and keeps no state of its own between calls.
+ *    keeps device memory.  Between calls it keeps only the compute-unit
+ *    count of each device it has launched the fused kernel on (read once,
+ *    the one device-property query) and, per thread, the last HIP error.
  *  - Arrays are dense, row-major, in the element types given below.
  *  - Work is only enqueued on `stream` (a hipStream_t; NULL means the null
  *    stream) and the call returns without waiting.  Stage order on one stream
@@ -33,8 +35,8 @@
  *    small, unsupported size) are found on the host before anything is
  *    enqueued; the call then returns the error code and enqueues nothing.
  *    MOE_ERR_HIP means a launch failed (see moe_last_hip_error()).
- *  - Calls on different streams that share output buffers race; the library
- *    has no global state, so calls on different buffers may run concurrently.
+ *  - Calls on different streams that share output buffers race; calls on
+ *    different buffers may run concurrently.
  */
 #ifndef MOE_EP_H
 #define MOE_EP_H
@@ -94,8 +96,12 @@ enum {
 int moe_recv_row_bytes(int32_t hidden, moe_dtype recv, size_t* bytes);
 
 /* Device workspace that moe_layout needs for `bs` tokens, `topk` entries per
- * token and `numExperts` experts (a per-tile count table).  May be 0, in
- * which case moe_layout accepts a NULL workspace.  Host only. */
+ * token and `numExperts` experts (a per-tile count table).  This follows the
+ * page's operator-call convention (section 6.7, EXEC_NPU_CMD: ask the
+ * operator for its workspace size, let the caller allocate that many bytes,
+ * then submit the operator with the workspace on a stream); here the caller
+ * allocates through its own allocator (torch) and passes the pointer.  May
+ * be 0, in which case moe_layout accepts a NULL workspace.  Host only. */
 int moe_layout_workspace_bytes(int32_t bs, int32_t topk, int32_t numExperts, size_t* bytes);
 
 /* Stage 1, dispatch layout (page 2.3).
@@ -195,7 +201,8 @@ int moe_notify_multi(const int32_t* tokenPerExpert, int32_t numSrc, int32_t expe
                      int32_t rankSize, int32_t* putOffset, int32_t* recvCount, int32_t* recvBase,
                      int32_t* recvTokenPerExpert, void* stream);
 
-/* moe_dispatch for source srcRank of numSrc: entry (t, j) with a valid id e
+/* moe_dispatch (page section 2.5) for source srcRank of numSrc, at the
+ * offsets of section 2.6's index: entry (t, j) with a valid id e
  * and slot s >= 0 writes to receive row
  *     recvBase[e / EPR] + putOffset[e][srcRank] + s
  * with putOffset [E][numSrc] and recvBase from moe_notify_multi.  The
@@ -209,9 +216,10 @@ int moe_dispatch_src(const void* x, moe_dtype xType, int32_t bs, int32_t hidden,
                      int32_t numSrc, int32_t srcRank, int quantInt8, void* recvX,
                      size_t recvXBytes, void* stream);
 
-/* moe_combine for source srcRank of numSrc: reads the rows moe_dispatch_src
- * wrote for that source (same row formula), with the same arithmetic and
- * bit-exactness as moe_combine.  Other arguments as moe_combine. */
+/* moe_combine (page section 2.6) for source srcRank of numSrc: reads the
+ * rows moe_dispatch_src wrote for that source (same row formula), with the
+ * same arithmetic and bit-exactness as moe_combine.  Other arguments as
+ * moe_combine. */
 int moe_combine_src(const void* recvX, moe_dtype recvType, size_t recvXBytes, int32_t bs,
                     int32_t hidden, int32_t topk, const int32_t* topkIdx, const float* topkWeights,
                     const int32_t* sendTokenIdx, const int32_t* putOffset, const int32_t* recvBase,
@@ -220,11 +228,11 @@ int moe_combine_src(const void* recvX, moe_dtype recvType, size_t recvXBytes, in
 
 /* ---- Fused layout + notify + dispatch ------------------------------------ */
 
-/* *supported = 1 if moe_layout_notify_dispatch runs as one kernel for this
- * shape, 0 if it runs the three stages one after another (bs == 0, hidden
- * above 8192, or bs * topk above 2^16: every workgroup of the one kernel
- * reads all bs * topk ids).  Host only; the answer does not depend on the
- * device. */
+/* *supported = 1 if moe_layout_notify_dispatch (the single-kernel form of
+ * section 3.2) runs as one kernel for this shape, 0 if it runs the three
+ * stages one after another (bs == 0, hidden above 8192, or bs * topk above
+ * 2^16: every workgroup of the one kernel reads all bs * topk ids).  Host
+ * only; the answer does not depend on the device. */
 int moe_fused_supported(int32_t bs, int32_t hidden, int32_t topk, int32_t expertNumPerRank,
                         int32_t rankSize, moe_dtype xType, int quantInt8, int* supported);
 
@@ -315,11 +323,13 @@ int moe_grouped_gemm_i8(const void* a, int64_t aRowBytes, int32_t rows, int32_t 
                         const int32_t* groupCount, int32_t groups, const void* w, int32_t n,
                         int32_t* out, size_t outBytes, void* stream);
 
-/* Text for a status code (static storage). */
+/* Diagnostics.  No counterpart on the pages (their operator calls report
+ * failure through the framework's own status; section 6.7 does not show it):
+ * the text of one of this library's status codes (static storage). */
 const char* moe_status_str(int status);
 
-/* The hipError_t value of the last MOE_ERR_HIP returned on this thread
- * (0 if none). */
+/* Diagnostics, no counterpart on the pages: the hipError_t value of the last
+ * MOE_ERR_HIP returned on this thread (0 if none). */
 int moe_last_hip_error(void);
 
 #ifdef __cplusplus

@@ -33,6 +33,39 @@ def test_header_symbols_exported(M):
         assert hasattr(lib, n), f"{n} declared in moe_ep.h but not exported"
 
 
+def declarations():
+    """{name: (preceding comment, parameter count)} for every function the
+    header declares."""
+    text = open(HEADER).read()
+    out = {}
+    for m in re.finditer(r"(/\*(?:(?!\*/).)*\*/)\s*(?:const char\*|int)\s+(moe_[a-z0-9_]+)\s*\(([^)]*)\)\s*;",
+                         text, flags=re.S):
+        params = [p for p in m.group(3).split(",") if p.strip() and p.strip() != "void"]
+        out[m.group(2)] = (m.group(1), len(params))
+    return out
+
+
+def test_every_declaration_cites_its_passage_or_says_it_has_none():
+    decls = declarations()
+    assert set(decls) == set(declared_functions()), "a declaration without its own comment block"
+    for name, (comment, _) in decls.items():
+        assert re.search(r"section \d|page \d|\bpage's\b|No counterpart on the pages|no counterpart on the pages",
+                         comment), f"{name}: its comment cites no passage of the pages"
+
+
+def test_binding_signatures_match_header(M):
+    for name, (_, nparams) in declarations().items():
+        assert name in M._SIGS, f"{name} has no binding"
+        assert len(M._SIGS[name][0]) == nparams, f"{name}: binding takes {len(M._SIGS[name][0])} arguments"
+
+
+def test_design_boundary_table_lists_every_entry_point():
+    text = open(os.path.join(ROOT, "DESIGN.md")).read()
+    section = text[text.index("## 2. The boundary"):text.index("## 3. ")]
+    for name in declared_functions():
+        assert f"`{name}`" in section, f"{name} missing from the boundary table"
+
+
 def test_header_constants_match_binding(M):
     text = open(HEADER).read()
     for name in ("MOE_MAX_EXPERTS", "MOE_MAX_HIDDEN", "MOE_MAX_TOPK", "MOE_MAX_SOURCES",
