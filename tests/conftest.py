@@ -18,6 +18,10 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def orc():
+    """The oracle the pins run against: the default build, or the build named
+    by MOE_ORACLE_LIB (test_oracle_sanitized.py runs the pins on an
+    ASan/UBSan build that way)."""
     import oracle
 
-    return oracle.default()
+    path = os.environ.get("MOE_ORACLE_LIB")
+    return oracle.Oracle(path) if path else oracle.default()
