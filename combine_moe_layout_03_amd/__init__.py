@@ -29,13 +29,15 @@ __all__ = [
     "dtype_code", "moe_fused_supported", "moe_layout_notify_dispatch", "moe_notify_multi",
     "moe_dispatch_src", "moe_combine_src", "EpMultiBuffers", "MOE_MAX_SOURCES",
     "moe_deq_swiglu_quant", "token_scales_of", "MOE_EPILOGUE_MAX_N", "moe_grouped_gemm_i8",
-    "MOE_GEMM_MAX_K", "MOE_GEMM_MAX_N", "MOE_GEMM_MAX_GROUPS",
+    "MOE_GEMM_MAX_K", "MOE_GEMM_MAX_N", "MOE_GEMM_MAX_GROUPS", "moe_layout_no_alloc",
+    "MOE_NO_ALLOC_SCRATCH_BYTES",
 ]
 
 MOE_BF16, MOE_FP16, MOE_FP32, MOE_INT8_ROWSCALE = 0, 1, 2, 3
 MOE_MAX_EXPERTS, MOE_MAX_HIDDEN, MOE_MAX_TOPK, MOE_MAX_SOURCES = 2048, 16384, 32, 384
 MOE_EPILOGUE_MAX_N = 4096
 MOE_GEMM_MAX_K = MOE_GEMM_MAX_N = MOE_GEMM_MAX_GROUPS = 65536
+MOE_NO_ALLOC_SCRATCH_BYTES = 1 << 20
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_ep.so")
 
@@ -49,6 +51,7 @@ _SIGS = {
     "moe_recv_row_bytes": ([_I32, _INT, ctypes.POINTER(_SZ)], _INT),
     "moe_layout_workspace_bytes": ([_I32, _I32, _I32, ctypes.POINTER(_SZ)], _INT),
     "moe_layout": ([_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P], _INT),
+    "moe_layout_no_alloc": ([_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P], _INT),
     "moe_notify": ([_P, _I32, _I32, _P, _P, _P, _P, _P], _INT),
     "moe_dispatch": ([_P, _INT, _I32, _I32, _I32, _P, _P, _P, _P, _I32, _I32, _INT, _P, _SZ, _P],
                      _INT),
@@ -166,6 +169,22 @@ def moe_layout(topk_idx: torch.Tensor, expert_num_per_rank: int, rank_size: int,
         _dev(send_token_idx, "send_token_idx", torch.int32),
         _dev(bad_id_count, "bad_id_count", torch.int32, optional=True),
         _dev(workspace, "workspace", optional=True), ws_bytes, _stream(stream)))
+
+
+def moe_layout_no_alloc(topk_idx: torch.Tensor, expert_num_per_rank: int, rank_size: int,
+                        token_per_expert: torch.Tensor, token_per_rank: torch.Tensor,
+                        send_token_idx: torch.Tensor, bad_id_count: Optional[torch.Tensor] = None,
+                        stream=None) -> None:
+    """moe_layout with the library's static workspace (no allocation)."""
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [bs, topk]")
+    bs, topk = topk_idx.shape
+    _check("moe_layout_no_alloc", _lib.moe_layout_no_alloc(
+        _dev(topk_idx, "topk_idx", torch.int32), bs, topk, expert_num_per_rank, rank_size,
+        _dev(token_per_expert, "token_per_expert", torch.int32),
+        _dev(token_per_rank, "token_per_rank", torch.int32),
+        _dev(send_token_idx, "send_token_idx", torch.int32),
+        _dev(bad_id_count, "bad_id_count", torch.int32, optional=True), _stream(stream)))
 
 
 def moe_notify(token_per_expert: torch.Tensor, expert_num_per_rank: int, rank_size: int,

@@ -175,6 +175,29 @@ int moe_layout(const int32_t* topk_idx, int32_t bs, int32_t topk, int32_t epr, i
                                        bad_id_count, workspace, static_cast<hipStream_t>(stream)));
 }
 
+int moe_layout_no_alloc(const int32_t* topk_idx, int32_t bs, int32_t topk, int32_t epr, int32_t ranks,
+                        int32_t* token_per_expert, int32_t* token_per_rank, int32_t* send_token_idx,
+                        int32_t* bad_id_count, void* stream) {
+  int st = check_tokens(bs, topk);
+  if (st) return st;
+  if ((st = check_experts(epr, ranks))) return st;
+  if (!token_per_expert || !token_per_rank) return MOE_ERR_NULL_PTR;
+  if (bs > 0 && (!topk_idx || !send_token_idx)) return MOE_ERR_NULL_PTR;
+  if (!aligned(token_per_expert, 4) || !aligned(token_per_rank, 4) || !aligned(send_token_idx, 4) ||
+      !aligned(topk_idx, 4) || !aligned(bad_id_count, 4))
+    return MOE_ERR_BAD_ALIGN;
+  const int32_t e = epr * ranks;
+  const int64_t n = static_cast<int64_t>(bs) * topk;
+  const size_t need = moe::layout_workspace_bytes(n, e);
+  if (need > moe::kLayoutScratchBytes) return MOE_ERR_SCRATCH_LIMIT;
+  void* scratch = nullptr;
+  const hipError_t err = moe::layout_scratch_address(&scratch);
+  if (err != hipSuccess) return hip_status(err);
+  return hip_status(moe::launch_layout(topk_idx, static_cast<int32_t>(n), e, epr, ranks, token_per_expert,
+                                       token_per_rank, send_token_idx, bad_id_count, scratch,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 int moe_notify(const int32_t* token_per_expert, int32_t epr, int32_t ranks, int32_t* put_offset,
                int32_t* recv_count, int32_t* recv_base, int32_t* recv_token_per_expert,
                void* stream) {
@@ -446,6 +469,9 @@ const char* moe_status_str(int status) {
     case MOE_ERR_BUFFER_TOO_SMALL: return "receive buffer smaller than bs * topk rows";
     case MOE_ERR_UNSUPPORTED: return "size not supported by the library (see MOE_MAX_* and hidden % 8)";
     case MOE_ERR_HIP: return "HIP launch failed (see moe_last_hip_error)";
+    case MOE_ERR_SCRATCH_LIMIT:
+      return "shape needs more workspace than the static scratch of the no-alloc entry point "
+             "(MOE_NO_ALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -39,6 +39,11 @@ hipError_t launch_layout(const int32_t* topk_idx, int32_t n, int32_t num_experts
                          int32_t* send_token_idx, int32_t* bad_count, void* workspace,
                          hipStream_t stream);
 
+// The static layout workspace of moe_layout_no_alloc: its size, and its
+// device address on the current device (looked up once per device).
+constexpr size_t kLayoutScratchBytes = MOE_NO_ALLOC_SCRATCH_BYTES;
+hipError_t layout_scratch_address(void** ptr);
+
 // ---- notify -------------------------------------------------------------------
 hipError_t launch_notify(const int32_t* token_per_expert, int32_t epr, int32_t ranks,
                          int32_t* put_offset, int32_t* recv_count, int32_t* recv_base,

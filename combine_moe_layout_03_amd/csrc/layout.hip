@@ -23,6 +23,8 @@
 // results are shuffled to the group members, so the rounds do not wait on
 // each other.  A scan over the waves and the tile base turn wave-local ranks
 // into global slots.  No result depends on scheduling.
+#include <mutex>
+
 #include "device_util.h"
 #include "launch.h"
 
@@ -228,6 +230,39 @@ hipError_t launch_layout(const int32_t* topk_idx, int32_t n, int32_t num_experts
                               send_token_idx, bad_count, workspace, stream);
   }
   return hipErrorInvalidValue;
+}
+
+// ---- the layout workspace without allocation --------------------------------
+// For callers that cannot allocate: a file-scope device array serves as the
+// per-tile count table.  In host code `layout_scratch` names a host-side
+// stand-in, not device memory; its device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is ever passed to a kernel.  Every call on a device shares
+// the device's array (calls that overlap on one device race).  Nothing in it
+// needs clearing: the count kernel writes every entry the rank kernel reads.
+namespace {
+static __device__ __align__(256) int32_t layout_scratch[kLayoutScratchBytes / sizeof(int32_t)];
+
+constexpr int kScratchMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kScratchMaxDevices];  // device address of layout_scratch on each device
+}  // namespace
+
+hipError_t layout_scratch_address(void** ptr) {
+  int device = 0;
+  hipError_t err = hipGetDevice(&device);
+  if (err != hipSuccess) return err;
+  if (device < 0 || device >= kScratchMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[device] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(layout_scratch));
+    if (err != hipSuccess) return err;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = p;
+  }
+  *ptr = g_scratch_ptr[device];
+  return hipSuccess;
 }
 
 }  // namespace moe

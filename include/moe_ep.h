@@ -66,7 +66,8 @@ enum {
   MOE_ERR_WORKSPACE_TOO_SMALL = 5,
   MOE_ERR_BUFFER_TOO_SMALL = 6,
   MOE_ERR_UNSUPPORTED = 7,
-  MOE_ERR_HIP = 8
+  MOE_ERR_HIP = 8,
+  MOE_ERR_SCRATCH_LIMIT = 9
 };
 
 /* Limits of the library. */
@@ -79,6 +80,7 @@ enum {
 #define MOE_GEMM_MAX_K 65536    /* k of the first expert matmul: sums stay below 2^31 */
 #define MOE_GEMM_MAX_N 65536    /* n of the first expert matmul */
 #define MOE_GEMM_MAX_GROUPS 65536 /* experts of one first-expert-matmul call */
+#define MOE_NO_ALLOC_SCRATCH_BYTES (1u << 20) /* moe_layout_no_alloc's static workspace */
 
 /* Bytes of one receive-buffer row for hidden size `hidden` and receive type
  * `recv` (page 2.5 and 2.2.1):
@@ -122,6 +124,24 @@ int moe_layout(const int32_t* topkIdx, int32_t bs, int32_t topk, int32_t expertN
                int32_t rankSize, int32_t* tokenPerExpert, int32_t* tokenPerRank,
                int32_t* sendTokenIdx, int32_t* badIdCount, void* workspace,
                size_t workspaceBytes, void* stream);
+
+/* moe_layout for callers that cannot allocate device memory -- code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc:
+ * the same stage, the same outputs bit for bit, with no workspace argument.
+ * The per-tile count table lives in a static device array of
+ * MOE_NO_ALLOC_SCRATCH_BYTES that the library holds on each device it runs
+ * on until the process ends; the call allocates and frees nothing.  Shapes
+ * whose table (moe_layout_workspace_bytes) would exceed it return
+ * MOE_ERR_SCRATCH_LIMIT before anything is enqueued (1 MiB: bs * topk up to
+ * about 2.09 million entries at 256 experts, 262144 at 2048).  Every call on
+ * one device shares that device's array: calls that overlap in time on one
+ * device (other streams, other threads) race and must be serialised by the
+ * caller.  The first call on a device looks up the array's device address
+ * (a runtime symbol query, no allocation).  Other arguments and errors as
+ * moe_layout. */
+int moe_layout_no_alloc(const int32_t* topkIdx, int32_t bs, int32_t topk, int32_t expertNumPerRank,
+                        int32_t rankSize, int32_t* tokenPerExpert, int32_t* tokenPerRank,
+                        int32_t* sendTokenIdx, int32_t* badIdCount, void* stream);
 
 /* Stage 2, notify (page 2.4).  With a single source the page's all-gather of
  * tokenPerExpert is the identity and the prefix sums remain:
