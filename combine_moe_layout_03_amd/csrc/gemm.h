@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "select.h"
+
 namespace moe {
 
 struct GemmArgs {
@@ -18,7 +20,14 @@ struct GemmArgs {
   int32_t n;
   int32_t* out;                // [rows][n]
 };
-constexpr int kGemmTileM = 128, kGemmTileN = 128;
+// Workgroup tile (rows x output columns), its waves, the LDS ring, and the
+// XCD-aware tile order (see gemm.hip).
+constexpr int kGemmTileM = 128, kGemmTileN = 256;
+constexpr int kGemmWavesM = 2, kGemmWavesN = 4;
+constexpr int kGemmStageK = select::kGemmStageK;  // bytes of k per LDS stage
+constexpr int kGemmRing = 3;                       // LDS stages in the ring
+constexpr int kGemmXcdColGroups = 4;               // column groups of the tile order
+constexpr int kGemmXcdRows = 8;                    // row slots per XCD block
 constexpr int64_t kGemmMaxBlocks = int64_t(1) << 24;
 // Workgroups of one launch (row slots x column tiles).
 int64_t grouped_gemm_blocks(int64_t rows, int32_t groups, int32_t n);

@@ -10,28 +10,49 @@
 // with w stored [groups][n][k].  Every partial sum is bounded by
 // k * 2^14 < 2^31, so the int32 accumulation is exact in any order.
 //
-// Tiling (gfx950, wave64, v_mfma_i32_16x16x64_i8): a workgroup of WM x WN
-// waves computes a TM x TN tile of one expert's output; each wave owns a
-// (TM/WM) x (TN/WN) block of 16 x 16 MFMA tiles (the library launches
-// 128 x 128 tiles of 2 x 2 waves, two workgroups per CU).  K is walked in
-// stages of SK = 256 bytes: every thread loads its 16-byte pieces of the
-// next stage's A rows and B rows (weight rows, k contiguous) into registers
-// while the waves run the current stage's MFMAs out of LDS.  In LDS a row's
-// 16-byte pieces are XOR-swizzled by the row index (piece p of row r at
-// position p ^ (r % 16)), so the 16 rows one fragment read touches hit 16
-// different positions: no bank conflicts (the hardware counter reads zero;
-// rows padded to 272 bytes instead conflicted on a third of the LDS cycles).
-// A lane's fragment of A and of B takes the same 16 bytes of k (logical
-// piece kk / 16 + lane / 16 of the stage), so each product pairs a[m][i]
-// with w[g][j][i].
+// Tiling (gfx950, wave64, v_mfma_i32_16x16x64_i8): a workgroup of 2 x 4
+// waves computes a 128 x 256 tile of one expert's output, each wave a 64 x 64
+// block of 16 x 16 MFMA tiles.  K is walked in stages of 128 bytes held in a
+// ring of three LDS buffers: while the waves multiply stage s, the loads of
+// stages s + 1 and s + 2 are in flight straight from global memory into LDS
+// (the LDS-destination form of the global load, 16 bytes per lane; lane l of
+// one load writes bytes [16 l, 16 l + 16) of a 1 KB block, at the address
+// the wave puts in M0).  No register holds the data on the way.  Each ring
+// buffer is its own LDS array, so the compiler's wait analysis tells them
+// apart: before reading stage s a wave waits only for its own loads of that
+// stage (an explicit vmcnt that leaves the next stage's loads in flight),
+// then a workgroup barrier covers the other waves' loads and also
+// guarantees that no wave still reads the buffer the next loads overwrite.
+// The barrier is the plain s_barrier (the fence that __syncthreads adds
+// would wait for every load in flight, collapsing the ring).  Every step
+// issues exactly one stage (past the last stage it re-loads the last stage
+// into a buffer that is not read again), so the wait count is the same on
+// every path and the compiler adds no wait of its own.
+//
+// In LDS a stage row (A rows, then B rows) is 8 pieces of 16 bytes; piece p
+// of row r sits at position p ^ ((r / 2) % 8).  A fragment read touches 16
+// consecutive rows at one piece; that swizzle spreads them over all 16
+// 16-byte bank groups of a 256-byte LDS line (no bank conflicts).  The loads
+// apply it on the global side: lane l of a load fetches the piece that
+// belongs at LDS position l.  When k ends inside a stage (a separate
+// instance), the pieces past k are loaded from the row's first piece (a
+// valid address) and their B fragments are zeroed in registers.
+//
+// Tile order: the hardware deals workgroup g to XCD g % 8.  With the column
+// tiles in groups of 4, XCD x takes column group x % 4 of every other block
+// of 8 row slots (x / 4 picks which), so each XCD's L2 serves an 8 x
+// (n_tiles / 4) block of tiles and each row tile is fetched by two XCDs
+// rather than all eight (at n_tiles % 4 != 0: row slots in order, column
+// tiles innermost).
 //
 // The counts live on the device and the host does not read them, so the
-// launch has ceil(rows / TM) + groups row slots (enough for any counts whose
-// total is at most rows: expert g needs at most c_g / TM + 1 tiles) times
-// the column tiles.  A workgroup finds its expert and first row by a prefix
-// sum over the counts; slots past the last tile exit at once.  Rows past an
-// expert's end are loaded from its last row and never stored; weight rows
-// past n repeat row n - 1 and are never stored.
+// launch has ceil(rows / 128) + groups row slots (enough for any counts whose
+// total is at most rows: expert g needs at most c_g / 128 + 1 tiles), rounded
+// up to the tile order's blocks, times the column tiles.  A workgroup finds
+// its expert and first row by a prefix sum over the counts; slots past the
+// last tile exit at once.  Rows past an expert's end are loaded from its last
+// row and never stored; weight rows past n repeat row n - 1 and are never
+// stored.
 #include "device_util.h"
 #include "launch.h"
 #include "gemm.h"
@@ -40,6 +61,12 @@ namespace moe {
 namespace {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+#define MOE_LDS __attribute__((address_space(3)))
+
+constexpr int kSK = kGemmStageK;               // bytes of k per stage
+constexpr int kPieces = kSK / 16;              // 16-byte pieces of a row per stage
+constexpr int kRowsPerLoad = kWave / kPieces;  // stage rows one load instruction fills
+static_assert(kPieces == 8, "the LDS swizzle is written for 8 pieces per stage row");
 
 struct TileSlot {
   int32_t group, row0, row_end;
@@ -79,41 +106,54 @@ __device__ void find_slot(const GemmArgs& a, int64_t slot, int lane, TileSlot* o
   }
 }
 
-template <int TM, int TN, int WM, int WN, int SK, int kDepth>
+// s_waitcnt with vmcnt(n) (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_wait(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
+
+// Row slots of one launch: enough for any counts, rounded up to whole pairs
+// of XCD blocks when the XCD-aware order applies.
+int64_t launch_slots(int64_t rows, int32_t groups, int64_t n_tiles) {
+  int64_t slots = (rows + kGemmTileM - 1) / kGemmTileM + groups;
+  if (n_tiles % kGemmXcdColGroups == 0)
+    slots = (slots + 2 * kGemmXcdRows - 1) / (2 * kGemmXcdRows) * (2 * kGemmXcdRows);
+  return slots;
+}
+
+template <int TM, int TN, int WM, int WN, int NS, bool kTail>
 __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs a) {
-  static_assert(kDepth == 1 || kDepth == 2, "stages held in registers ahead of the LDS stage");
-  constexpr int kStageK = SK;              // bytes of k per stage
-  constexpr int kPieces = kStageK / 16;    // 16-byte pieces of a row per stage
-  // LDS rows are kStageK bytes apart; the 16-byte piece p of tile row r
-  // sits at position p ^ (r % kPieces) of its row
-  constexpr bool kSwizzle = true;
-  constexpr int kLdsPitch = kStageK + (kSwizzle ? 0 : 16);
-  constexpr int kSwz = kSwizzle ? kPieces - 1 : 0;
-  static_assert(kPieces <= 16, "a fragment's 16 rows cover every swizzle position");
-  constexpr int kThreads = kWave * WM * WN;
+  constexpr int kWaves = WM * WN;
   constexpr int kWaveM = TM / WM, kWaveN = TN / WN;
   constexpr int kMI = kWaveM / 16, kNI = kWaveN / 16;
-  constexpr int kRowsPerPass = kThreads / kPieces;  // tile rows one load pass covers
-  constexpr int kAPasses = TM / kRowsPerPass, kBPasses = TN / kRowsPerPass;
+  constexpr int kStageBytes = (TM + TN) * kSK;
+  constexpr int kLoadsA = TM / kRowsPerLoad / kWaves;  // load instructions per thread and stage
+  constexpr int kLoadsB = TN / kRowsPerLoad / kWaves;
+  constexpr int kLoads = kLoadsA + kLoadsB;
+  static_assert(TM % (kRowsPerLoad * kWaves) == 0 && TN % (kRowsPerLoad * kWaves) == 0,
+                "every wave issues whole loads of A and of B");
   static_assert(kWaveM % 16 == 0 && kWaveN % 16 == 0, "wave tile of whole MFMA tiles");
-  static_assert(kThreads % kPieces == 0 && TM % kRowsPerPass == 0 && TN % kRowsPerPass == 0,
-                "load passes cover the tile");
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[TM * kLdsPitch];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[TN * kLdsPitch];
+  static_assert(NS == 3, "a ring of three stages");
+  static_assert((NS - 2) * kLoads < 64, "vmcnt counts the loads in flight");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[kStageBytes];
   __shared__ TileSlot slot_info;
 
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = uniform(tid / kWave);
 
-  // workgroup -> (row slot, column tile), column tiles innermost.  The
-  // hardware deals consecutive workgroups round-robin to the 8 XCDs, so with
-  // 32 column tiles each XCD holds the same 4 column tiles of every row slot
-  // it runs: their weight rows (4 x 0.9 MB at k = 7168) stay in its L2 while
-  // the whole GPU works through one expert's row slots.  (A contiguous range
-  // of the order per XCD, or bands of several row slots, measured 6-15 %
-  // slower at the benchmark shape.)
+  // workgroup -> (row slot, column tile)
   const int64_t n_tiles = (a.n + TN - 1) / TN;
-  const int64_t slot = blockIdx.x / n_tiles;
-  const int64_t col_tile = blockIdx.x - slot * n_tiles;
+  int64_t slot, col_tile;
+  if (n_tiles % kGemmXcdColGroups == 0) {
+    const int64_t g = blockIdx.x, x = g % 8, l = g / 8;
+    const int64_t cols = n_tiles / kGemmXcdColGroups;
+    const int64_t per_block = kGemmXcdRows * cols;
+    const int64_t b = 2 * (l / per_block) + x / kGemmXcdColGroups;
+    const int64_t w = l % per_block;
+    slot = b * kGemmXcdRows + w / cols;
+    col_tile = (x % kGemmXcdColGroups) * cols + w % cols;
+  } else {
+    slot = blockIdx.x / n_tiles;
+    col_tile = blockIdx.x - slot * n_tiles;
+  }
 
   if (wave == 0) {
     if (lane == 0) slot_info.group = -1;
@@ -125,71 +165,76 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
   const int row0 = slot_info.row0, row_end = slot_info.row_end;
   const int col0 = static_cast<int>(col_tile) * TN;
 
-  // this thread's 16-byte pieces: piece `piece` of tile rows r0 + p * kRowsPerPass
-  const int piece = tid % kPieces, r0 = tid / kPieces;
-  const int8_t* a_src[kAPasses];
-  const int8_t* b_src[kBPasses];
+  // This lane's piece of each of its loads: load q of this wave fills stage
+  // rows [kRowsPerLoad * (q * kWaves + wave), + kRowsPerLoad); lane l writes
+  // position l % 8 of row l / 8, which holds piece (l % 8) ^ ((row / 2) % 8).
+  const int8_t* src_a[kLoadsA];
+  const int8_t* src_b[kLoadsB];
+  int piece_a[kLoadsA], piece_b[kLoadsB];
 #pragma unroll
-  for (int p = 0; p < kAPasses; ++p) {
-    const int row = min(row0 + r0 + p * kRowsPerPass, row_end - 1);
-    a_src[p] = a.a + static_cast<int64_t>(row) * a.a_stride + piece * 16;
+  for (int q = 0; q < kLoadsA; ++q) {
+    const int r = kRowsPerLoad * (q * kWaves + wave) + lane / kPieces;
+    const int p = (lane % kPieces) ^ ((r >> 1) & (kPieces - 1));
+    const int row = min(row0 + r, row_end - 1);
+    piece_a[q] = p;
+    src_a[q] = a.a + static_cast<int64_t>(row) * a.a_stride + p * 16;
   }
 #pragma unroll
-  for (int p = 0; p < kBPasses; ++p) {
-    const int col = min(col0 + r0 + p * kRowsPerPass, a.n - 1);
-    b_src[p] = a.w + (static_cast<int64_t>(group) * a.n + col) * a.k + piece * 16;
+  for (int q = 0; q < kLoadsB; ++q) {
+    const int r = kRowsPerLoad * (q * kWaves + wave) + lane / kPieces;
+    const int p = (lane % kPieces) ^ ((r >> 1) & (kPieces - 1));
+    const int col = min(col0 + r, a.n - 1);
+    piece_b[q] = p;
+    src_b[q] = a.w + (static_cast<int64_t>(group) * a.n + col) * a.k + p * 16;
   }
 
-  using ARegs = i32x4[kAPasses];
-  using BRegs = i32x4[kBPasses];
-  auto load_stage = [&](int k0, ARegs& ra, BRegs& rb) {
-    if (k0 + piece * 16 < a.k) {
+  // The loads of stage s into ring buffer `buf` (stages past the last one
+  // load the last stage again).
+  const int stages = (a.k + kSK - 1) / kSK;
+  auto issue = [&](int s, uint8_t* buf) {
+    const int k0 = min(s, stages - 1) * kSK;
 #pragma unroll
-      for (int p = 0; p < kAPasses; ++p) ra[p] = *reinterpret_cast<const i32x4*>(a_src[p] + k0);
-#pragma unroll
-      for (int p = 0; p < kBPasses; ++p) rb[p] = *reinterpret_cast<const i32x4*>(b_src[p] + k0);
-    } else {
-#pragma unroll
-      for (int p = 0; p < kAPasses; ++p) ra[p] = i32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int p = 0; p < kBPasses; ++p) rb[p] = i32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_stage = [&](const ARegs& ra, const BRegs& rb) {
-#pragma unroll
-    for (int p = 0; p < kAPasses; ++p) {
-      const int r = r0 + p * kRowsPerPass;
-      *reinterpret_cast<i32x4*>(lds_a + r * kLdsPitch + ((piece ^ (r & kSwz)) * 16)) = ra[p];
+    for (int q = 0; q < kLoadsA; ++q) {
+      const int8_t* src = src_a[q] + k0;
+      if constexpr (kTail) src = (k0 + piece_a[q] * 16 < a.k) ? src : src_a[q] - piece_a[q] * 16;
+      __builtin_amdgcn_global_load_lds(src, (MOE_LDS void*)(buf + (q * kWaves + wave) * kRowsPerLoad * kSK), 16,
+                                       0, 0);
     }
 #pragma unroll
-    for (int p = 0; p < kBPasses; ++p) {
-      const int r = r0 + p * kRowsPerPass;
-      *reinterpret_cast<i32x4*>(lds_b + r * kLdsPitch + ((piece ^ (r & kSwz)) * 16)) = rb[p];
+    for (int q = 0; q < kLoadsB; ++q) {
+      const int8_t* src = src_b[q] + k0;
+      if constexpr (kTail) src = (k0 + piece_b[q] * 16 < a.k) ? src : src_b[q] - piece_b[q] * 16;
+      __builtin_amdgcn_global_load_lds(src, (MOE_LDS void*)(buf + (TM + (q * kWaves + wave) * kRowsPerLoad) * kSK),
+                                       16, 0, 0);
     }
   };
 
   const int wm = wave / WN, wn = wave % WN;
-  // a fragment's rows are 16-aligned, so row % kPieces is lane % kPieces
-  const uint8_t* fa = lds_a + (wm * kWaveM + lane % 16) * kLdsPitch;
-  const uint8_t* fb = lds_b + (wn * kWaveN + lane % 16) * kLdsPitch;
-  const int lane_swz = lane & kSwz;
+  // a fragment's 16 rows start at a multiple of 16, so the row's swizzle is the lane's
+  const int lane_swz = ((lane % 16) >> 1) & (kPieces - 1);
+  const int frag_a = (wm * kWaveM + lane % 16) * kSK;
+  const int frag_b = (TM + wn * kWaveN + lane % 16) * kSK;
   i32x4 acc[kMI][kNI];
 #pragma unroll
   for (int i = 0; i < kMI; ++i)
 #pragma unroll
     for (int j = 0; j < kNI; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
-  auto compute_stage = [&]() {
+  auto compute = [&](int s, const uint8_t* buf) {
 #pragma unroll
-    for (int kk = 0; kk < kStageK; kk += 64) {
+    for (int kk = 0; kk < kSK; kk += 64) {
       const int pos = ((kk / 16 + lane / 16) ^ lane_swz) * 16;
       i32x4 af[kMI], bf[kNI];
 #pragma unroll
-      for (int i = 0; i < kMI; ++i)
-        af[i] = *reinterpret_cast<const i32x4*>(fa + i * 16 * kLdsPitch + pos);
+      for (int i = 0; i < kMI; ++i) af[i] = *reinterpret_cast<const i32x4*>(buf + frag_a + i * 16 * kSK + pos);
 #pragma unroll
-      for (int j = 0; j < kNI; ++j)
-        bf[j] = *reinterpret_cast<const i32x4*>(fb + j * 16 * kLdsPitch + pos);
+      for (int j = 0; j < kNI; ++j) bf[j] = *reinterpret_cast<const i32x4*>(buf + frag_b + j * 16 * kSK + pos);
+      if constexpr (kTail) {
+        // this lane's 16 bytes of k in the fragments; past k they multiply by zero
+        const bool live = s * kSK + kk + (lane / 16) * 16 < a.k;
+#pragma unroll
+        for (int j = 0; j < kNI; ++j) bf[j] = live ? bf[j] : i32x4{0, 0, 0, 0};
+      }
 #pragma unroll
       for (int i = 0; i < kMI; ++i)
 #pragma unroll
@@ -198,38 +243,28 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
     }
   };
 
-  // One LDS stage; the next kDepth stages are in flight into registers while
-  // it is computed.  The barrier before a store waits for every wave to be
-  // done reading the stage it replaces.
-  const int stages = (a.k + kStageK - 1) / kStageK;
-  ARegs ra0, ra1;
-  BRegs rb0, rb1;
-  load_stage(0, ra0, rb0);
-  if (kDepth == 1) {
-    for (int s = 0; s < stages; ++s) {
-      if (s) __syncthreads();
-      store_stage(ra0, rb0);
-      __syncthreads();
-      if (s + 1 < stages) load_stage((s + 1) * kStageK, ra0, rb0);
-      compute_stage();
-    }
-  } else {
-    if (stages > 1) load_stage(kStageK, ra1, rb1);
-    for (int s = 0; s < stages; s += 2) {
-      if (s) __syncthreads();
-      store_stage(ra0, rb0);
-      __syncthreads();
-      if (s + 2 < stages) load_stage((s + 2) * kStageK, ra0, rb0);
-      compute_stage();
-      if (s + 1 < stages) {
-        __syncthreads();
-        store_stage(ra1, rb1);
-        __syncthreads();
-        if (s + 3 < stages) load_stage((s + 3) * kStageK, ra1, rb1);
-        compute_stage();
-      }
-    }
+  // Stage s: wait for this wave's loads of it, barrier, start the loads of
+  // stage s + 2 into the buffer stage s - 1 used, multiply.
+  auto step = [&](int s, const uint8_t* cur, uint8_t* refill) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait((NS - 2) * kLoads));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    issue(s + NS - 1, refill);
+    compute(s, cur);
+  };
+  issue(0, lds0);
+  issue(1, lds1);
+  const int rounds = stages / 3, rest = stages - rounds * 3;
+  for (int r = 0; r < rounds; ++r) {
+    step(3 * r, lds0, lds2);
+    step(3 * r + 1, lds1, lds0);
+    step(3 * r + 2, lds2, lds1);
   }
+  if (rest > 0) step(3 * rounds, lds0, lds2);
+  if (rest > 1) step(3 * rounds + 1, lds1, lds0);
+  // no load may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
 
   // 16 x 16 result tile: lane l holds column l % 16 of rows 4 * (l / 16) + 0..3
 #pragma unroll
@@ -246,26 +281,27 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
   }
 }
 
-template <int TM, int TN, int WM, int WN, int SK, int kDepth>
-hipError_t launch_shape(const GemmArgs& a, hipStream_t stream) {
-  const int64_t slots = (a.rows + TM - 1) / TM + a.groups;
-  const int64_t n_tiles = (a.n + TN - 1) / TN;
-  const int64_t blocks = slots * n_tiles;
-  if (blocks > kGemmMaxBlocks) return hipErrorInvalidValue;
-  grouped_gemm_kernel<TM, TN, WM, WN, SK, kDepth>
-      <<<dim3(static_cast<uint32_t>(blocks)), dim3(kWave * WM * WN), 0, stream>>>(a);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 int64_t grouped_gemm_blocks(int64_t rows, int32_t groups, int32_t n) {
-  return ((rows + kGemmTileM - 1) / kGemmTileM + groups) * ((n + kGemmTileN - 1) / kGemmTileN);
+  const int64_t n_tiles = (n + kGemmTileN - 1) / kGemmTileN;
+  return launch_slots(rows, groups, n_tiles) * n_tiles;
 }
 
+// One case per value of select::gemm_k_tail.
 hipError_t launch_grouped_gemm_i8(const GemmArgs& a, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;
-  return launch_shape<kGemmTileM, kGemmTileN, 2, 2, 256, 1>(a, stream);
+  const int64_t blocks = grouped_gemm_blocks(a.rows, a.groups, a.n);
+  if (blocks > kGemmMaxBlocks) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>(blocks)), block(kWave * kGemmWavesM * kGemmWavesN);
+  if (select::gemm_k_tail(a.k)) {
+    grouped_gemm_kernel<kGemmTileM, kGemmTileN, kGemmWavesM, kGemmWavesN, kGemmRing, true>
+        <<<grid, block, 0, stream>>>(a);
+  } else {
+    grouped_gemm_kernel<kGemmTileM, kGemmTileN, kGemmWavesM, kGemmWavesN, kGemmRing, false>
+        <<<grid, block, 0, stream>>>(a);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace moe

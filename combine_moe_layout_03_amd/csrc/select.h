@@ -80,5 +80,10 @@ constexpr int epilogue_shape_index(int n) {
   return -1;
 }
 
+// ---- first expert matmul: k is walked in 128-byte LDS stages ----------------
+// A k that ends inside a stage runs the instance that masks the tail.
+constexpr int kGemmStageK = 128;
+constexpr bool gemm_k_tail(int k) { return k % kGemmStageK != 0; }
+
 }  // namespace select
 }  // namespace moe

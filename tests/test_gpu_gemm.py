@@ -119,6 +119,10 @@ def boundary_tile_rows(case, seed, n_random=32):
     (1000, 96, 48, 3, [400, 400, 400], 505),
     # n = 1 and a single expert
     (257, 48, 1, 1, [257], 506),
+    # 4 and 8 column tiles (the XCD-aware tile order), empty and negative counts,
+    # k ending 64 bytes into a stage
+    (1000, 320, 1024, 6, [0, 300, -5, 1, 0, 517], 507),
+    (1500, 1088, 2048, 9, "owned:1490", 508),
 ])
 def test_gemm_matches_oracle(rows, k, n, groups, counts, seed):
     if isinstance(counts, str):

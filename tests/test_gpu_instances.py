@@ -43,3 +43,12 @@ def test_instance_epilogue(rows, n):
     log(f"instance epilogue rows={rows} n={n}")
     out = run_gpu(case, guard_rows=1)
     assert_same(case, out, f"rows={rows} n={n}")
+
+
+@pytest.mark.parametrize("rows,k,n,groups,counts", IC.GEMM_CASES, ids=[f"k{c[1]}" for c in IC.GEMM_CASES])
+def test_instance_grouped_gemm(rows, k, n, groups, counts):
+    from test_gpu_gemm import assert_same, run_gpu
+
+    case = W.gemm_case(950 + k, rows, k, n, groups, stride=(k + 31) // 32 * 32 + 32, counts=counts)
+    log(f"instance grouped gemm rows={rows} k={k} n={n}")
+    assert_same(case, run_gpu(case), f"k={k}")

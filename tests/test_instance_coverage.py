@@ -52,6 +52,10 @@ int main() {
                   fused_vpl(int(h)), dispatch_vpl(int(h)), combine_rows_max_k(int(k)),
                   combine_rows_chunks(int(h)), layout_waves(int(e)), layout_rounds(int(e)),
                   (long long)layout_num_tiles(bs * k, int(e)));
+    } else if (kind == 'g') {
+      int k;
+      if (std::scanf("%d", &k) != 1) return 1;
+      std::printf("g %d\n", gemm_k_tail(k) ? 1 : 0);
     } else if (kind == 'e') {
       int n;
       if (std::scanf("%d", &n) != 1) return 1;
@@ -78,6 +82,7 @@ def selection():
         subprocess.run(["g++", "-std=c++17", "-O1", f"-I{CSRC}", src, "-o", exe], check=True)
         lines = [f"p {c[1]} {c[2]} {c[3]} {c[4]}" for c in IC.PIPELINE_CASES]
         lines += [f"e {n}" for _, n in IC.EPILOGUE_NS]
+        lines += [f"g {c[1]}" for c in IC.GEMM_CASES]
         r = subprocess.run([exe], input="\n".join(lines) + "\n", capture_output=True, text=True, check=True)
     out = r.stdout.splitlines()
     tables = {}
@@ -86,8 +91,10 @@ def selection():
         tables[name] = [tuple(int(p) for p in v.split(":")) if ":" in v else int(v) for v in vals]
     pipe = [list(map(int, line.split()[1:])) for line in out[6:] if line.startswith("p ")]
     epi = [tuple(map(int, line.split()[1:])) for line in out[6:] if line.startswith("e ")]
+    gemm = [int(line.split()[1]) for line in out[6:] if line.startswith("g ")]
     assert len(pipe) == len(IC.PIPELINE_CASES) and len(epi) == len(IC.EPILOGUE_NS)
-    return tables, pipe, epi
+    assert len(gemm) == len(IC.GEMM_CASES)
+    return tables, pipe, epi, gemm
 
 
 def _arg(v: str) -> int:
@@ -125,14 +132,18 @@ def expected(tables):
         "deq_swiglu_quant_kernel": set(t["epilogue"]),
         "layout_count_kernel": set(t["layout"]),
         "layout_rank_kernel": set(t["layout"]),
+        "grouped_gemm_kernel": {(0,), (1,)},
     }
     return exp
 
 
 def reached(selection):
-    _, pipe, epi = selection
+    _, pipe, epi, gemm = selection
     got = {k: set() for k in ("fused_kernel", "dispatch_kernel", "combine_rows_kernel", "combine_kernel",
-                              "deq_swiglu_quant_kernel", "layout_count_kernel", "layout_rank_kernel")}
+                              "deq_swiglu_quant_kernel", "layout_count_kernel", "layout_rank_kernel",
+                              "grouped_gemm_kernel")}
+    for tail in gemm:
+        got["grouped_gemm_kernel"].add((tail,))
     for case, ans in zip(IC.PIPELINE_CASES, pipe):
         seed, bs, h, k, e, r, route, bad, xk, q = case
         applies, fvpl, dvpl, kmax, chunks, lw, lr, tiles = ans
@@ -157,18 +168,20 @@ def reached(selection):
 
 
 def test_tables_list_exactly_the_compiled_instances(selection, compiled):
-    tables, _, _ = selection
+    tables = selection[0]
     for family, want in expected(tables).items():
         have = compiled.get(family, set())
         if family == "combine_kernel":  # <Recv, Out, 32 entries, 8 elements, 4 waves, nt load, nt store>
             have = {a[:2] for a in have}
+        elif family == "grouped_gemm_kernel":  # <tile M, tile N, waves M, waves N, ring, k tail>
+            have = {a[-1:] for a in have}
         elif family == "dispatch_kernel":
             assert all(len(a) == 3 for a in have), f"dispatch_kernel template arguments changed: {have}"
         assert have == want, f"{family}: compiled {sorted(have)} but the tables give {sorted(want)}"
 
 
 def test_every_instance_has_a_gpu_case(selection):
-    tables, _, _ = selection
+    tables = selection[0]
     got = reached(selection)
     for family, want in expected(tables).items():
         missing = sorted(want - got[family])
