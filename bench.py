@@ -717,6 +717,9 @@ def bench_gemm(args, M, torch, W, dev) -> int:
     torch.cuda.synchronize()
     copy_gbps = 2 * flush.numel() * 4 * 10 / (hev.ms(c0, c1) * 1e-3) / 1e9
     del dst
+    log("vendor library reference (torch._int_mm)")
+    library = library_int8_reference(torch, hev, stream, flush, flush_out, rows, k, n, case.group_count,
+                                     min(args.steps, 10))
     hev.close()
     mean_us = statistics.mean(us)
     ops = gemm_ops(owned, n, k)
@@ -771,10 +774,56 @@ def bench_gemm(args, M, torch, W, dev) -> int:
                      "traffic": load_traffic("gemm", "gemm", f"n{n}")},
         "unflushed_us_per_launch": unflushed_us,
         "copy_ceiling_gbps": copy_gbps,
+        "library_reference": library,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def library_int8_reference(torch, hev, stream, flush, flush_out, rows, k, n, group_count, reps):
+    """The vendor library's int8 x int8 -> int32 GEMM (torch._int_mm, which
+    calls hipBLASLt on this stack) at the same sizes, after the same flush,
+    for scale: one dense GEMM over all rows with one weight matrix (no
+    grouping), and one GEMM per expert at that expert's row count (the host
+    knows the counts here; the library entry point does not need them).
+    Weights column-major (each output column's k contiguous, as the
+    library's [groups][n][k] layout).  Inputs are random bytes; only the
+    time is used.  None when the call is not available."""
+    try:
+        g = torch.Generator(device="cuda").manual_seed(5)
+        a = torch.randint(-128, 127, (rows, k), dtype=torch.int8, device="cuda", generator=g)
+        w = torch.randint(-128, 127, (n, k), dtype=torch.int8, device="cuda", generator=g).t()
+        counts = [int(c) for c in group_count]
+
+        def timed(fn):
+            fn()
+            torch.cuda.synchronize()
+            ev = [(hev.new(), hev.new()) for _ in range(reps)]
+            for e0, e1 in ev:
+                torch.sum(flush, dim=0, out=flush_out)
+                hev.record(e0, stream)
+                fn()
+                hev.record(e1, stream)
+            torch.cuda.synchronize()
+            return statistics.mean(hev.ms(e0, e1) for e0, e1 in ev) * 1e3
+
+        def per_expert():
+            start = 0
+            for c in counts:
+                if c > 0:
+                    torch._int_mm(a[start:start + c], w)
+                start += max(c, 0)
+
+        dense_us = timed(lambda: torch._int_mm(a, w))
+        grouped_us = timed(per_expert)
+        ops = 2 * rows * n * k
+        return {"call": "torch._int_mm (hipBLASLt)", "dense_us": dense_us,
+                "dense_tops": ops / (dense_us * 1e-6) / 1e12, "per_expert_calls_us": grouped_us,
+                "per_expert_calls_tops": ops / (grouped_us * 1e-6) / 1e12}
+    except (RuntimeError, AttributeError) as exc:
+        log(f"library reference unavailable: {exc}")
+        return None
 
 
 def bench_sources(args, M, torch, w, x, idx, wts, quant: bool, do_flush, stream) -> int:
