@@ -75,3 +75,58 @@ def test_no_alloc_layout_rejects_shapes_beyond_its_scratch():
     assert ei.value.status == 9
     torch.cuda.synchronize()
     assert (out["token_per_expert"] == -7).all().item()
+
+
+def test_no_alloc_layout_in_a_replayed_hip_graph():
+    """The callers the no-allocation entry point exists for: the whole step
+    (no-alloc layout, notify, dispatch, combine) captured once in a HIP
+    graph and replayed on new routings written into the captured inputs,
+    with eager work of the program (including the workspace form of the
+    layout on other buffers) between replays; every replay against the
+    oracle."""
+    import combine_moe_layout_03_amd as M
+
+    bs, h, k, e, r = 3000, 256, 8, 64, 8   # 24000 entries: 12 layout tiles
+    epr = e // r
+    w0 = W.random_case(620, bs, h, k, e, r, routing="dup", bad_frac=0.01)
+    buf = M.EpBuffers(bs, h, k, epr, r, quant_int8=True)
+    x = torch.from_numpy(w0.x.view(np.int16)).cuda().view(torch.bfloat16)
+    idx = torch.from_numpy(w0.topk_idx).cuda()
+    wts = torch.from_numpy(w0.topk_w).cuda()
+
+    def step():
+        M.moe_layout_no_alloc(idx, epr, r, buf.token_per_expert, buf.token_per_rank, buf.send_token_idx,
+                              buf.bad_id_count)
+        buf.notify()
+        buf.dispatch(x, idx)
+        buf.combine(idx, wts)
+
+    def check(w, what):
+        torch.cuda.synchronize()
+        ref = oracle.pipeline(w.x, "bf16", w.topk_idx, w.topk_w, epr, r, True, "bf16")
+        np.testing.assert_array_equal(buf.send_token_idx.cpu().numpy(), ref["layout"]["send_token_idx"], err_msg=what)
+        np.testing.assert_array_equal(buf.token_per_expert.cpu().numpy(), ref["layout"]["token_per_expert"],
+                                      err_msg=what)
+        np.testing.assert_array_equal(buf.out.view(torch.int16).cpu().numpy().view(np.uint16), ref["out"],
+                                      err_msg=what)
+
+    log("no-alloc step eager (first call on the device looks up the scratch)")
+    step()
+    check(w0, "eager")
+    graph = torch.cuda.CUDAGraph()
+    log("no-alloc step: capture")
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    other = M.EpBuffers(500, h, k, epr, r)
+    other_idx = torch.from_numpy(W.random_case(630, 500, h, k, e, r).topk_idx).cuda()
+    for rep in range(3):
+        w = W.random_case(621 + rep, bs, h, k, e, r, routing="uniform" if rep % 2 else "dup", bad_frac=0.02)
+        x.copy_(torch.from_numpy(w.x.view(np.int16)).view(torch.bfloat16))
+        idx.copy_(torch.from_numpy(w.topk_idx))
+        wts.copy_(torch.from_numpy(w.topk_w))
+        other.layout(other_idx)   # eager work between replays
+        torch.cuda.synchronize()
+        log(f"no-alloc step: replay {rep}")
+        graph.replay()
+        check(w, f"replay {rep}")
