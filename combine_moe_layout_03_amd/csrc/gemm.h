@@ -22,10 +22,10 @@ struct GemmArgs {
 };
 // Workgroup tile (rows x output columns), its waves, the LDS ring, and the
 // XCD-aware tile order (see gemm.hip).
-constexpr int kGemmTileM = 128, kGemmTileN = 256;
-constexpr int kGemmWavesM = 2, kGemmWavesN = 4;
+constexpr int kGemmTileM = 256, kGemmTileN = 256;
+constexpr int kGemmWavesM = 4, kGemmWavesN = 2;
 constexpr int kGemmStageK = select::kGemmStageK;  // bytes of k per LDS stage
-constexpr int kGemmRing = 3;                       // LDS stages in the ring
+constexpr int kGemmRing = select::kGemmRingStages;  // LDS stages in the ring
 constexpr int kGemmXcdColGroups = 4;               // column groups of the tile order
 constexpr int kGemmXcdRows = 8;                    // row slots per XCD block
 constexpr int64_t kGemmMaxBlocks = int64_t(1) << 24;

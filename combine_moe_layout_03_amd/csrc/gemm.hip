@@ -10,33 +10,44 @@
 // with w stored [groups][n][k].  Every partial sum is bounded by
 // k * 2^14 < 2^31, so the int32 accumulation is exact in any order.
 //
-// Tiling (gfx950, wave64, v_mfma_i32_16x16x64_i8): a workgroup of 2 x 4
-// waves computes a 128 x 256 tile of one expert's output, each wave a 64 x 64
-// block of 16 x 16 MFMA tiles.  K is walked in stages of 128 bytes held in a
-// ring of three LDS buffers: while the waves multiply stage s, the loads of
-// stages s + 1 and s + 2 are in flight straight from global memory into LDS
-// (the LDS-destination form of the global load, 16 bytes per lane; lane l of
-// one load writes bytes [16 l, 16 l + 16) of a 1 KB block, at the address
-// the wave puts in M0).  No register holds the data on the way.  Each ring
-// buffer is its own LDS array, so the compiler's wait analysis tells them
-// apart: before reading stage s a wave waits only for its own loads of that
-// stage (an explicit vmcnt that leaves the next stage's loads in flight),
-// then a workgroup barrier covers the other waves' loads and also
-// guarantees that no wave still reads the buffer the next loads overwrite.
-// The barrier is the plain s_barrier (the fence that __syncthreads adds
-// would wait for every load in flight, collapsing the ring).  Every step
-// issues exactly one stage (past the last stage it re-loads the last stage
-// into a buffer that is not read again), so the wait count is the same on
-// every path and the compiler adds no wait of its own.
+// Tiling (gfx950, wave64, v_mfma_i32_16x16x64_i8): a workgroup of 4 x 2
+// waves computes a 256 x 256 tile of one expert's output, each wave a
+// 64 x 128 block of 16 x 16 MFMA tiles.  K is walked in stages of 64 bytes
+// held in a ring of four LDS buffers (32 KB each), filled straight from
+// global memory by the LDS-destination form of the global load (16 bytes per
+// lane; lane l of one load writes bytes [16 l, 16 l + 16) of a 1 KB block, at
+// the address the wave puts in M0): no register holds the data on the way.
+// Each ring buffer is its own LDS array, so the compiler's wait analysis
+// tells them apart, and every step issues exactly one stage (past the last
+// stage it re-loads the last stage into a buffer that is not read again), so
+// the explicit vmcnt waits are the same on every path and the compiler adds
+// none of its own.
 //
-// In LDS a stage row (A rows, then B rows) is 8 pieces of 16 bytes; piece p
-// of row r sits at position p ^ ((r / 2) % 8).  A fragment read touches 16
-// consecutive rows at one piece; that swizzle spreads them over all 16
-// 16-byte bank groups of a 256-byte LDS line (no bank conflicts).  The loads
-// apply it on the global side: lane l of a load fetches the piece that
-// belongs at LDS position l.  When k ends inside a stage (a separate
+// Schedule (ping-pong): the waves 0-3 and 4-7 (one of each per SIMD)
+// alternate between a memory phase (start the loads of stage j + 3 into the
+// buffer stage j - 1 used, wait for this wave's loads of stage j + 1, read
+// the fragments of stage j into registers) and a compute phase (the stage's
+// 32 MFMAs), the two groups half a step apart, with a workgroup barrier
+// between phases.  While one wave of a SIMD multiplies, the other issues its
+// loads and LDS reads.  The barriers make it safe: a wave reads stage j only
+// after a barrier that every wave reached after waiting for its own loads of
+// stage j (one memory phase earlier), and refills a buffer only after a
+// barrier that every wave reached after its last read of it.  The barrier is
+// the plain s_barrier (the fence that __syncthreads adds would wait for
+// every load in flight), and scheduling barriers keep the compiler from
+// moving work across it.
+//
+// In LDS a stage row (A rows, then B rows) is 4 pieces of 16 bytes; piece p
+// of row r sits at position p ^ ((r / 4) % 4).  A fragment read touches 16
+// consecutive rows at one piece, 4 rows to a 256-byte LDS line; that swizzle
+// puts them in all 16 16-byte bank groups of the line (no bank conflicts).
+// The loads apply it on the global side: lane l of a load fetches the piece
+// that belongs at LDS position l.  When k ends inside a stage (a separate
 // instance), the pieces past k are loaded from the row's first piece (a
-// valid address) and their B fragments are zeroed in registers.
+// valid address) and their A fragments are zeroed in registers; that
+// instance also runs whole rounds of the ring, the steps past the last
+// stage multiplying zeros (it serves every k that is not a multiple of
+// four stages).
 //
 // Tile order: the hardware deals workgroup g to XCD g % 8.  With the column
 // tiles in groups of 4, XCD x takes column group x % 4 of every other block
@@ -46,8 +57,8 @@
 // tiles innermost).
 //
 // The counts live on the device and the host does not read them, so the
-// launch has ceil(rows / 128) + groups row slots (enough for any counts whose
-// total is at most rows: expert g needs at most c_g / 128 + 1 tiles), rounded
+// launch has ceil(rows / 256) + groups row slots (enough for any counts whose
+// total is at most rows: expert g needs at most c_g / 256 + 1 tiles), rounded
 // up to the tile order's blocks, times the column tiles.  A workgroup finds
 // its expert and first row by a prefix sum over the counts; slots past the
 // last tile exit at once.  Rows past an expert's end are loaded from its last
@@ -66,7 +77,8 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kSK = kGemmStageK;               // bytes of k per stage
 constexpr int kPieces = kSK / 16;              // 16-byte pieces of a row per stage
 constexpr int kRowsPerLoad = kWave / kPieces;  // stage rows one load instruction fills
-static_assert(kPieces == 8, "the LDS swizzle is written for 8 pieces per stage row");
+constexpr int kSwzRows = 16 / kPieces;         // rows of one 256-byte LDS line
+static_assert(kPieces == 4, "the LDS swizzle and the k step are written for 64-byte stages");
 
 struct TileSlot {
   int32_t group, row0, row_end;
@@ -108,6 +120,8 @@ __device__ void find_slot(const GemmArgs& a, int64_t slot, int lane, TileSlot* o
 
 // s_waitcnt with vmcnt(n) (expcnt and lgkmcnt left at their maxima).
 constexpr int vmcnt_wait(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
+// s_waitcnt with lgkmcnt(0) (vmcnt and expcnt left at their maxima).
+constexpr int kLgkmWait0 = 0xc07f;
 
 // Row slots of one launch: enough for any counts, rounded up to whole pairs
 // of XCD blocks when the XCD-aware order applies.
@@ -130,11 +144,13 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
   static_assert(TM % (kRowsPerLoad * kWaves) == 0 && TN % (kRowsPerLoad * kWaves) == 0,
                 "every wave issues whole loads of A and of B");
   static_assert(kWaveM % 16 == 0 && kWaveN % 16 == 0, "wave tile of whole MFMA tiles");
-  static_assert(NS == 3, "a ring of three stages");
+  static_assert(NS == 4, "a ring of four stages");
+  static_assert(kWaves == 8, "two groups of four waves, one wave of each per SIMD");
   static_assert((NS - 2) * kLoads < 64, "vmcnt counts the loads in flight");
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds3[kStageBytes];
   __shared__ TileSlot slot_info;
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = uniform(tid / kWave);
@@ -167,14 +183,14 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
 
   // This lane's piece of each of its loads: load q of this wave fills stage
   // rows [kRowsPerLoad * (q * kWaves + wave), + kRowsPerLoad); lane l writes
-  // position l % 8 of row l / 8, which holds piece (l % 8) ^ ((row / 2) % 8).
+  // position l % 4 of row l / 4, which holds piece (l % 4) ^ ((row / 4) % 4).
   const int8_t* src_a[kLoadsA];
   const int8_t* src_b[kLoadsB];
   int piece_a[kLoadsA], piece_b[kLoadsB];
 #pragma unroll
   for (int q = 0; q < kLoadsA; ++q) {
     const int r = kRowsPerLoad * (q * kWaves + wave) + lane / kPieces;
-    const int p = (lane % kPieces) ^ ((r >> 1) & (kPieces - 1));
+    const int p = (lane % kPieces) ^ ((r / kSwzRows) & (kPieces - 1));
     const int row = min(row0 + r, row_end - 1);
     piece_a[q] = p;
     src_a[q] = a.a + static_cast<int64_t>(row) * a.a_stride + p * 16;
@@ -182,7 +198,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
 #pragma unroll
   for (int q = 0; q < kLoadsB; ++q) {
     const int r = kRowsPerLoad * (q * kWaves + wave) + lane / kPieces;
-    const int p = (lane % kPieces) ^ ((r >> 1) & (kPieces - 1));
+    const int p = (lane % kPieces) ^ ((r / kSwzRows) & (kPieces - 1));
     const int col = min(col0 + r, a.n - 1);
     piece_b[q] = p;
     src_b[q] = a.w + (static_cast<int64_t>(group) * a.n + col) * a.k + p * 16;
@@ -195,15 +211,17 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
     const int k0 = min(s, stages - 1) * kSK;
 #pragma unroll
     for (int q = 0; q < kLoadsA; ++q) {
-      const int8_t* src = src_a[q] + k0;
-      if constexpr (kTail) src = (k0 + piece_a[q] * 16 < a.k) ? src : src_a[q] - piece_a[q] * 16;
+      int off = k0;
+      if constexpr (kTail) off = (k0 + piece_a[q] * 16 < a.k) ? off : -piece_a[q] * 16;
+      const int8_t* src = src_a[q] + off;
       __builtin_amdgcn_global_load_lds(src, (MOE_LDS void*)(buf + (q * kWaves + wave) * kRowsPerLoad * kSK), 16,
                                        0, 0);
     }
 #pragma unroll
     for (int q = 0; q < kLoadsB; ++q) {
-      const int8_t* src = src_b[q] + k0;
-      if constexpr (kTail) src = (k0 + piece_b[q] * 16 < a.k) ? src : src_b[q] - piece_b[q] * 16;
+      int off = k0;
+      if constexpr (kTail) off = (k0 + piece_b[q] * 16 < a.k) ? off : -piece_b[q] * 16;
+      const int8_t* src = src_b[q] + off;
       __builtin_amdgcn_global_load_lds(src, (MOE_LDS void*)(buf + (TM + (q * kWaves + wave) * kRowsPerLoad) * kSK),
                                        16, 0, 0);
     }
@@ -211,7 +229,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
 
   const int wm = wave / WN, wn = wave % WN;
   // a fragment's 16 rows start at a multiple of 16, so the row's swizzle is the lane's
-  const int lane_swz = ((lane % 16) >> 1) & (kPieces - 1);
+  const int lane_swz = ((lane % 16) / kSwzRows) & (kPieces - 1);
   const int frag_a = (wm * kWaveM + lane % 16) * kSK;
   const int frag_b = (TM + wn * kWaveN + lane % 16) * kSK;
   i32x4 acc[kMI][kNI];
@@ -220,49 +238,55 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
 #pragma unroll
     for (int j = 0; j < kNI; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
-  auto compute = [&](int s, const uint8_t* buf) {
-#pragma unroll
-    for (int kk = 0; kk < kSK; kk += 64) {
-      const int pos = ((kk / 16 + lane / 16) ^ lane_swz) * 16;
-      i32x4 af[kMI], bf[kNI];
-#pragma unroll
-      for (int i = 0; i < kMI; ++i) af[i] = *reinterpret_cast<const i32x4*>(buf + frag_a + i * 16 * kSK + pos);
-#pragma unroll
-      for (int j = 0; j < kNI; ++j) bf[j] = *reinterpret_cast<const i32x4*>(buf + frag_b + j * 16 * kSK + pos);
-      if constexpr (kTail) {
-        // this lane's 16 bytes of k in the fragments; past k they multiply by zero
-        const bool live = s * kSK + kk + (lane / 16) * 16 < a.k;
-#pragma unroll
-        for (int j = 0; j < kNI; ++j) bf[j] = live ? bf[j] : i32x4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int i = 0; i < kMI; ++i)
-#pragma unroll
-        for (int j = 0; j < kNI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  // Stage s: wait for this wave's loads of it, barrier, start the loads of
-  // stage s + 2 into the buffer stage s - 1 used, multiply.
-  auto step = [&](int s, const uint8_t* cur, uint8_t* refill) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_wait((NS - 2) * kLoads));
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    issue(s + NS - 1, refill);
-    compute(s, cur);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Step j: the memory phase, a barrier, the compute phase, a barrier.
+  auto step = [&](int j, const uint8_t* cur, uint8_t* refill) {
+    issue(j + NS - 1, refill);
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait((NS - 2) * kLoads));  // this wave's loads of stage j + 1
+    const int pos = ((lane / 16) ^ lane_swz) * 16;
+    i32x4 af[kMI], bf[kNI];
+#pragma unroll
+    for (int i = 0; i < kMI; ++i) af[i] = *reinterpret_cast<const i32x4*>(cur + frag_a + i * 16 * kSK + pos);
+#pragma unroll
+    for (int q = 0; q < kNI; ++q) bf[q] = *reinterpret_cast<const i32x4*>(cur + frag_b + q * 16 * kSK + pos);
+    if constexpr (kTail) {
+      // this lane's 16 bytes of k in the fragments; past k the A side is zero
+      const bool live = j * kSK + (lane / 16) * 16 < a.k;
+#pragma unroll
+      for (int i = 0; i < kMI; ++i) af[i] = live ? af[i] : i32x4{0, 0, 0, 0};
+    }
+    __builtin_amdgcn_s_waitcnt(kLgkmWait0);  // the fragments are in registers
+    barrier();
+#pragma unroll
+    for (int i = 0; i < kMI; ++i)
+#pragma unroll
+      for (int q = 0; q < kNI; ++q)
+        acc[i][q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[q], acc[i][q], 0, 0, 0);
+    barrier();
   };
   issue(0, lds0);
   issue(1, lds1);
-  const int rounds = stages / 3, rest = stages - rounds * 3;
+  issue(2, lds2);
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait((NS - 2) * kLoads));  // this wave's loads of stage 0
+  barrier();
+  const int grp = wave / 4;
+  if (grp == 1) barrier();  // the second group runs half a step behind
+  // Whole rounds of the ring: without the tail, k is a multiple of NS
+  // stages; with it, the steps past the last stage multiply zeros.
+  const int rounds = (stages + NS - 1) / NS;
   for (int r = 0; r < rounds; ++r) {
-    step(3 * r, lds0, lds2);
-    step(3 * r + 1, lds1, lds0);
-    step(3 * r + 2, lds2, lds1);
+    step(NS * r, lds0, lds3);
+    step(NS * r + 1, lds1, lds0);
+    step(NS * r + 2, lds2, lds1);
+    step(NS * r + 3, lds3, lds2);
   }
-  if (rest > 0) step(3 * rounds, lds0, lds2);
-  if (rest > 1) step(3 * rounds + 1, lds1, lds0);
+  if (grp == 0) barrier();  // every wave passes the same number of barriers
   // no load may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
 

@@ -118,13 +118,13 @@ def test_grid_covers_owned_outputs_once_and_loads_stay_in_bounds(rows, k, n, cou
                 k0 = min(s, stages - 1) * sk
                 for q in range(tm // rows_per_load // waves):
                     r = rows_per_load * (q * waves + wave) + lane // pieces
-                    p = (lane % pieces) ^ ((r >> 1) & (pieces - 1))
+                    p = (lane % pieces) ^ ((r // (16 // pieces)) & (pieces - 1))
                     row = np.minimum(row0 + r, row_end - 1)
                     addr = row * stride + np.where(k0 + p * 16 < k, p * 16 + k0, 0)
                     assert (addr >= 0).all() and (addr + 16 <= a_end).all()
                 for q in range(tn // rows_per_load // waves):
                     r = rows_per_load * (q * waves + wave) + lane // pieces
-                    p = (lane % pieces) ^ ((r >> 1) & (pieces - 1))
+                    p = (lane % pieces) ^ ((r // (16 // pieces)) & (pieces - 1))
                     col = np.minimum(col0 + r, n - 1)
                     addr = (g * n + col) * k + np.where(k0 + p * 16 < k, p * 16 + k0, 0)
                     assert (addr >= 0).all() and (addr + 16 <= w_end).all()
