@@ -80,6 +80,7 @@ def _slot(counts, rows, slot, tm):
     (1000, 320, 1024, [0, 300, -5, 1, 0, 517]),
     (2000, 64, 2048, "owned:1990:130"),
     (300, 144, 7168, [100, 0, 200]),
+    (900, 1008, 520, "owned:880:4"),
 ])
 def test_grid_covers_owned_outputs_once_and_loads_stay_in_bounds(rows, k, n, counts):
     tm, tn, wm, wn, sk, groups_c, xrows = _shape()

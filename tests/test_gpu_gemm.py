@@ -4,12 +4,13 @@ the GPU against the CPU oracle, through the C ABI.
 Bar: bit-exact int32 outputs (integer sums, exact on both sides), rows owned
 by no expert left as they were, on every row of the small cases; at the
 shape the benchmark times and at the layer's second matmul, on every row of
-each expert's first whole 128-row tile and of its last (partial) tile --
-so every row on both sides of every expert boundary, and the output's last
+each expert's first whole row tile and of its last (partial) tile -- so
+every row on both sides of every expert boundary, and the output's last
 rows -- plus rows drawn at random, all columns of each.  The cases cover
-several row and column tiles with ragged ends, k that ends inside a 256-byte
-stage, empty and negative counts, counts past the row capacity, more experts
-than one wave scans at once, and the int8 receive buffer used in place.
+several row and column tiles with ragged ends, k that ends inside a 64-byte
+stage and k that is not a whole number of ring rounds (4 stages), empty and
+negative counts, counts past the row capacity, more experts than one wave
+scans at once, and the int8 receive buffer used in place.
 """
 
 import concurrent.futures
@@ -107,7 +108,7 @@ def boundary_tile_rows(case, seed, n_random=32):
 
 
 @pytest.mark.parametrize("rows,k,n,groups,counts,seed", [
-    # 4 row tiles and 3 column tiles, both ragged; k ends 64 bytes into a stage
+    # 4 row tiles and 2 column tiles, both ragged; k is 5 stages (one past a ring round)
     (1000, 320, 300, 5, "owned:900", 501),
     # empty and negative counts; one expert spans three row tiles
     (830, 128, 128, 6, [0, 300, -5, 1, 0, 517], 502),
@@ -120,9 +121,11 @@ def boundary_tile_rows(case, seed, n_random=32):
     # n = 1 and a single expert
     (257, 48, 1, 1, [257], 506),
     # 4 and 8 column tiles (the XCD-aware tile order), empty and negative counts,
-    # k ending 64 bytes into a stage
+    # k one stage past a whole ring round
     (1000, 320, 1024, 6, [0, 300, -5, 1, 0, 517], 507),
     (1500, 1088, 2048, 9, "owned:1490", 508),
+    # k ending 48 bytes into the last stage of whole ring rounds; 3 ragged column tiles
+    (900, 1008, 520, 4, "owned:880", 509),
 ])
 def test_gemm_matches_oracle(rows, k, n, groups, counts, seed):
     if isinstance(counts, str):
