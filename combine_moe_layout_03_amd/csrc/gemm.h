@@ -20,12 +20,12 @@ struct GemmArgs {
   int32_t n;
   int32_t* out;                // [rows][n]
 };
-// Workgroup tile (rows x output columns), its waves, the LDS ring, and the
+// Workgroup tile (rows x output columns), its waves, the LDS slots, and the
 // XCD-aware tile order (see gemm.hip).
 constexpr int kGemmTileM = 256, kGemmTileN = 256;
 constexpr int kGemmWavesM = 4, kGemmWavesN = 2;
 constexpr int kGemmStageK = select::kGemmStageK;  // bytes of k per LDS stage
-constexpr int kGemmRing = select::kGemmRingStages;  // LDS stages in the ring
+constexpr int kGemmSlotsA = 2, kGemmSlotsB = 3;    // LDS slots of a stage's A and B rows
 constexpr int kGemmXcdColGroups = 4;               // column groups of the tile order
 constexpr int kGemmXcdRows = 8;                    // row slots per XCD block
 constexpr int64_t kGemmMaxBlocks = int64_t(1) << 24;

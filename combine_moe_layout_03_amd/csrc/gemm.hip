@@ -12,49 +12,50 @@
 //
 // Tiling (gfx950, wave64, v_mfma_i32_16x16x64_i8): a workgroup of 4 x 2
 // waves computes a 256 x 256 tile of one expert's output, each wave a
-// 64 x 128 block of 16 x 16 MFMA tiles.  K is walked in stages of 64 bytes
-// held in a ring of four LDS buffers (32 KB each), filled straight from
-// global memory by the LDS-destination form of the global load (16 bytes per
-// lane; lane l of one load writes bytes [16 l, 16 l + 16) of a 1 KB block, at
-// the address the wave puts in M0): no register holds the data on the way.
-// Each ring buffer is its own LDS array, so the compiler's wait analysis
-// tells them apart, and every step issues exactly one stage (past the last
-// stage it re-loads the last stage into a buffer that is not read again), so
-// the explicit vmcnt waits are the same on every path and the compiler adds
-// none of its own.
+// 64 x 128 block of 16 x 16 MFMA tiles.  K is walked in stages of 128 bytes:
+// the A rows of a stage (32 KB) go to one of two LDS slots, its B rows
+// (32 KB) to one of three, filled straight from global memory by the
+// LDS-destination form of the global load (16 bytes per lane; lane l of one
+// load writes bytes [16 l, 16 l + 16) of a 1 KB block, at the address the
+// wave puts in M0): no register holds the data on the way, and every load
+// covers 8 rows x 128 bytes, whole cache lines (loads of half lines move
+// about half as many bytes per CU and cycle).  Each slot is its own LDS
+// array, so the compiler's wait analysis tells them apart, and every step
+// issues the same loads (past the last stage it re-loads the last stage
+// into a slot that is not read again), so the explicit vmcnt waits are the
+// same on every path and the compiler adds none of its own.
 //
-// Schedule (ping-pong): the waves 0-3 and 4-7 (one of each per SIMD)
-// alternate between a memory phase (start the loads of stage j + 3 into the
-// buffer stage j - 1 used, wait for this wave's loads of stage j + 1, read
-// the fragments of stage j into registers) and a compute phase (the stage's
-// 32 MFMAs), the two groups half a step apart, with a workgroup barrier
-// between phases.  While one wave of a SIMD multiplies, the other issues its
-// loads and LDS reads.  The barriers make it safe: a wave reads stage j only
-// after a barrier that every wave reached after waiting for its own loads of
-// stage j (one memory phase earlier), and refills a buffer only after a
-// barrier that every wave reached after its last read of it.  The barrier is
-// the plain s_barrier (the fence that __syncthreads adds would wait for
-// every load in flight), and scheduling barriers keep the compiler from
-// moving work across it.
+// Schedule (ping-pong): the waves 0-3 and 4-7 (one of each per SIMD) run
+// half a step apart and alternate, between workgroup barriers, a memory
+// phase (fragment reads into registers) and a compute phase (32 MFMAs).  A
+// stage is consumed in two such steps, k bytes [0, 64) and [64, 128) of its
+// rows.  In the first step of stage S the loads of A(S + 1) and B(S + 2)
+// start, into the slots that A(S - 1) and B(S - 1) used; in the second
+// step each wave waits for its own loads of A(S + 1) and B(S + 1).  While
+// one wave of a SIMD multiplies, the other reads and loads.  The barriers
+// make it safe: a wave reads a stage only after a barrier that every wave
+// reached after waiting for its own loads of it, and refills a slot only
+// after a barrier that every wave reached after its last read of it.  The
+// barrier is the plain s_barrier (the fence that __syncthreads adds would
+// wait for every load in flight), and scheduling barriers keep the compiler
+// from moving work across it.  The five slots fill the 160 KB of LDS, so
+// the tile's slot record lives in the third B slot until its first load.
 //
-// In LDS a stage row (A rows, then B rows) is 4 pieces of 16 bytes; piece p
-// of row r sits at position p ^ ((r / 4) % 4).  A fragment read touches 16
-// consecutive rows at one piece, 4 rows to a 256-byte LDS line; that swizzle
-// puts them in all 16 16-byte bank groups of the line (no bank conflicts).
-// The loads apply it on the global side: lane l of a load fetches the piece
-// that belongs at LDS position l.  When k ends inside a stage (a separate
+// In LDS a stage row is 8 pieces of 16 bytes; piece p of row r sits at
+// position p ^ ((r / 2) % 8).  A fragment read touches 16 consecutive rows
+// at one piece, 2 rows to a 256-byte LDS line; that swizzle puts them in all
+// 16 16-byte bank groups of the 8 lines (no bank conflicts).  The loads
+// apply it on the global side: lane l of a load fetches the piece that
+// belongs at LDS position l.  When k ends inside a stage (a separate
 // instance), the pieces past k are loaded from the row's first piece (a
-// valid address) and their A fragments are zeroed in registers; that
-// instance also runs whole rounds of the ring, the steps past the last
-// stage multiplying zeros (it serves every k that is not a multiple of
-// four stages).
+// valid address) and their A fragments are zeroed in registers.
 //
 // Tile order: the hardware deals workgroup g to XCD g % 8.  With the column
 // tiles in groups of 4, XCD x takes column group x % 4 of every other block
 // of 8 row slots (x / 4 picks which), so each XCD's L2 serves an 8 x
-// (n_tiles / 4) block of tiles and each row tile is fetched by two XCDs
-// rather than all eight (at n_tiles % 4 != 0: row slots in order, column
-// tiles innermost).
+// (n_tiles / 4) block of tiles: each row tile is fetched by four XCDs and
+// each weight column tile by two, rather than all eight (at n_tiles % 4 !=
+// 0: row slots in order, column tiles innermost).
 //
 // The counts live on the device and the host does not read them, so the
 // launch has ceil(rows / 256) + groups row slots (enough for any counts whose
@@ -78,7 +79,7 @@ constexpr int kSK = kGemmStageK;               // bytes of k per stage
 constexpr int kPieces = kSK / 16;              // 16-byte pieces of a row per stage
 constexpr int kRowsPerLoad = kWave / kPieces;  // stage rows one load instruction fills
 constexpr int kSwzRows = 16 / kPieces;         // rows of one 256-byte LDS line
-static_assert(kPieces == 4, "the LDS swizzle and the k step are written for 64-byte stages");
+static_assert(kPieces == 8, "the LDS swizzle and the two k steps are written for 128-byte stages");
 
 struct TileSlot {
   int32_t group, row0, row_end;
@@ -132,26 +133,27 @@ int64_t launch_slots(int64_t rows, int32_t groups, int64_t n_tiles) {
   return slots;
 }
 
-template <int TM, int TN, int WM, int WN, int NS, bool kTail>
+template <int TM, int TN, int WM, int WN, bool kTail>
 __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs a) {
   constexpr int kWaves = WM * WN;
   constexpr int kWaveM = TM / WM, kWaveN = TN / WN;
   constexpr int kMI = kWaveM / 16, kNI = kWaveN / 16;
-  constexpr int kStageBytes = (TM + TN) * kSK;
   constexpr int kLoadsA = TM / kRowsPerLoad / kWaves;  // load instructions per thread and stage
   constexpr int kLoadsB = TN / kRowsPerLoad / kWaves;
-  constexpr int kLoads = kLoadsA + kLoadsB;
   static_assert(TM % (kRowsPerLoad * kWaves) == 0 && TN % (kRowsPerLoad * kWaves) == 0,
                 "every wave issues whole loads of A and of B");
   static_assert(kWaveM % 16 == 0 && kWaveN % 16 == 0, "wave tile of whole MFMA tiles");
-  static_assert(NS == 4, "a ring of four stages");
   static_assert(kWaves == 8, "two groups of four waves, one wave of each per SIMD");
-  static_assert((NS - 2) * kLoads < 64, "vmcnt counts the loads in flight");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds2[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds3[kStageBytes];
-  __shared__ TileSlot slot_info;
+  static_assert(kGemmSlotsA == 2 && kGemmSlotsB == 3, "the slot rotation below");
+  static_assert(kLoadsA + 2 * kLoadsB < 64, "vmcnt counts the loads in flight");
+  static_assert(sizeof(TileSlot) <= TN * kSK, "the slot record fits in a B slot");
+  __shared__ __attribute__((aligned(1024))) uint8_t sa0[TM * kSK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa1[TM * kSK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb0[TN * kSK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb1[TN * kSK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb2[TN * kSK];
+  // read by every wave before the workgroup barrier that precedes sb2's first load
+  TileSlot& slot_info = *reinterpret_cast<TileSlot*>(sb2);
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = uniform(tid / kWave);
 
@@ -183,47 +185,52 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
 
   // This lane's piece of each of its loads: load q of this wave fills stage
   // rows [kRowsPerLoad * (q * kWaves + wave), + kRowsPerLoad); lane l writes
-  // position l % 4 of row l / 4, which holds piece (l % 4) ^ ((row / 4) % 4).
+  // position l % 8 of row l / 8, which holds piece (l % 8) ^ ((row / 2) % 8).
+  // The first row of every load of a wave is the same modulo 16, so the
+  // piece is the same for all of them.
+  static_assert(kRowsPerLoad * kWaves % (kSwzRows * kPieces) == 0, "one piece per lane for all loads");
+  const int piece = (lane % kPieces) ^ (((kRowsPerLoad * wave + lane / kPieces) / kSwzRows) & (kPieces - 1));
   const int8_t* src_a[kLoadsA];
   const int8_t* src_b[kLoadsB];
-  int piece_a[kLoadsA], piece_b[kLoadsB];
 #pragma unroll
   for (int q = 0; q < kLoadsA; ++q) {
     const int r = kRowsPerLoad * (q * kWaves + wave) + lane / kPieces;
-    const int p = (lane % kPieces) ^ ((r / kSwzRows) & (kPieces - 1));
     const int row = min(row0 + r, row_end - 1);
-    piece_a[q] = p;
-    src_a[q] = a.a + static_cast<int64_t>(row) * a.a_stride + p * 16;
+    src_a[q] = a.a + static_cast<int64_t>(row) * a.a_stride + piece * 16;
   }
 #pragma unroll
   for (int q = 0; q < kLoadsB; ++q) {
     const int r = kRowsPerLoad * (q * kWaves + wave) + lane / kPieces;
-    const int p = (lane % kPieces) ^ ((r / kSwzRows) & (kPieces - 1));
     const int col = min(col0 + r, a.n - 1);
-    piece_b[q] = p;
-    src_b[q] = a.w + (static_cast<int64_t>(group) * a.n + col) * a.k + p * 16;
+    src_b[q] = a.w + (static_cast<int64_t>(group) * a.n + col) * a.k + piece * 16;
   }
-
-  // The loads of stage s into ring buffer `buf` (stages past the last one
-  // load the last stage again).
   const int stages = (a.k + kSK - 1) / kSK;
-  auto issue = [&](int s, uint8_t* buf) {
+  // Byte offset of stage s in every source row; where this lane's piece of
+  // the stage lies past k it reads the row's first piece instead.
+  auto stage_offset = [&](int s) {
     const int k0 = min(s, stages - 1) * kSK;
+    if constexpr (kTail) return (k0 + piece * 16 < a.k) ? k0 : -piece * 16;
+    return k0;
+  };
+
+  // The loads of stage s's A rows (B rows) into slot `buf` (stages past the
+  // last one load the last stage again).
+  auto issue_a = [&](int s, uint8_t* buf) {
+    const int off = stage_offset(s);
 #pragma unroll
     for (int q = 0; q < kLoadsA; ++q) {
-      int off = k0;
-      if constexpr (kTail) off = (k0 + piece_a[q] * 16 < a.k) ? off : -piece_a[q] * 16;
       const int8_t* src = src_a[q] + off;
       __builtin_amdgcn_global_load_lds(src, (MOE_LDS void*)(buf + (q * kWaves + wave) * kRowsPerLoad * kSK), 16,
                                        0, 0);
     }
+  };
+  auto issue_b = [&](int s, uint8_t* buf) {
+    const int off = stage_offset(s);
 #pragma unroll
     for (int q = 0; q < kLoadsB; ++q) {
-      int off = k0;
-      if constexpr (kTail) off = (k0 + piece_b[q] * 16 < a.k) ? off : -piece_b[q] * 16;
       const int8_t* src = src_b[q] + off;
-      __builtin_amdgcn_global_load_lds(src, (MOE_LDS void*)(buf + (TM + (q * kWaves + wave) * kRowsPerLoad) * kSK),
-                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (MOE_LDS void*)(buf + (q * kWaves + wave) * kRowsPerLoad * kSK), 16,
+                                       0, 0);
     }
   };
 
@@ -231,7 +238,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
   // a fragment's 16 rows start at a multiple of 16, so the row's swizzle is the lane's
   const int lane_swz = ((lane % 16) / kSwzRows) & (kPieces - 1);
   const int frag_a = (wm * kWaveM + lane % 16) * kSK;
-  const int frag_b = (TM + wn * kWaveN + lane % 16) * kSK;
+  const int frag_b = (wn * kWaveN + lane % 16) * kSK;
   i32x4 acc[kMI][kNI];
 #pragma unroll
   for (int i = 0; i < kMI; ++i)
@@ -245,22 +252,27 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Step j: the memory phase, a barrier, the compute phase, a barrier.
-  auto step = [&](int j, const uint8_t* cur, uint8_t* refill) {
-    issue(j + NS - 1, refill);
-    __builtin_amdgcn_s_waitcnt(vmcnt_wait((NS - 2) * kLoads));  // this wave's loads of stage j + 1
-    const int pos = ((lane / 16) ^ lane_swz) * 16;
+  // Step h (k bytes [64 h, 64 h + 64)) of stage S, its A rows in `ca` and B
+  // rows in `cb`: the memory phase, a barrier, the compute phase, a barrier.
+  auto step = [&](int S, int h, const uint8_t* ca, const uint8_t* cb, uint8_t* fill_a, uint8_t* fill_b) {
+    if (h == 0) {
+      issue_a(S + 1, fill_a);  // the slot A(S - 1) used
+      issue_b(S + 2, fill_b);  // the slot B(S - 1) used
+    }
+    const int pos = ((4 * h + lane / 16) ^ lane_swz) * 16;
     i32x4 af[kMI], bf[kNI];
 #pragma unroll
-    for (int i = 0; i < kMI; ++i) af[i] = *reinterpret_cast<const i32x4*>(cur + frag_a + i * 16 * kSK + pos);
+    for (int i = 0; i < kMI; ++i) af[i] = *reinterpret_cast<const i32x4*>(ca + frag_a + i * 16 * kSK + pos);
 #pragma unroll
-    for (int q = 0; q < kNI; ++q) bf[q] = *reinterpret_cast<const i32x4*>(cur + frag_b + q * 16 * kSK + pos);
+    for (int q = 0; q < kNI; ++q) bf[q] = *reinterpret_cast<const i32x4*>(cb + frag_b + q * 16 * kSK + pos);
     if constexpr (kTail) {
       // this lane's 16 bytes of k in the fragments; past k the A side is zero
-      const bool live = j * kSK + (lane / 16) * 16 < a.k;
+      const int keep = S * kSK + h * 64 + (lane / 16) * 16 < a.k ? -1 : 0;
 #pragma unroll
-      for (int i = 0; i < kMI; ++i) af[i] = live ? af[i] : i32x4{0, 0, 0, 0};
+      for (int i = 0; i < kMI; ++i) af[i] &= keep;
     }
+    // this wave's loads of A(S + 1) and B(S + 1); those of B(S + 2) may still run
+    if (h == 1) __builtin_amdgcn_s_waitcnt(vmcnt_wait(kLoadsB));
     __builtin_amdgcn_s_waitcnt(kLgkmWait0);  // the fragments are in registers
     barrier();
 #pragma unroll
@@ -270,21 +282,36 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
         acc[i][q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[q], acc[i][q], 0, 0, 0);
     barrier();
   };
-  issue(0, lds0);
-  issue(1, lds1);
-  issue(2, lds2);
-  __builtin_amdgcn_s_waitcnt(vmcnt_wait((NS - 2) * kLoads));  // this wave's loads of stage 0
+  // Stage S: A in sa[S % 2] (refilling sa[(S + 1) % 2]), B in sb[S % 3]
+  // (refilling sb[(S + 2) % 3]).
+  auto stage = [&](int S, const uint8_t* ca, const uint8_t* cb, uint8_t* fill_a, uint8_t* fill_b) {
+    step(S, 0, ca, cb, fill_a, fill_b);
+    step(S, 1, ca, cb, fill_a, fill_b);
+  };
+  issue_b(0, sb0);
+  issue_a(0, sa0);
+  issue_b(1, sb1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(kLoadsB));  // this wave's loads of stage 0
   barrier();
   const int grp = wave / 4;
   if (grp == 1) barrier();  // the second group runs half a step behind
-  // Whole rounds of the ring: without the tail, k is a multiple of NS
-  // stages; with it, the steps past the last stage multiply zeros.
-  const int rounds = (stages + NS - 1) / NS;
+  // Whole rounds of the rotation (its period is six stages), then the rest.
+  const int rounds = stages / 6;
   for (int r = 0; r < rounds; ++r) {
-    step(NS * r, lds0, lds3);
-    step(NS * r + 1, lds1, lds0);
-    step(NS * r + 2, lds2, lds1);
-    step(NS * r + 3, lds3, lds2);
+    stage(6 * r, sa0, sb0, sa1, sb2);
+    stage(6 * r + 1, sa1, sb1, sa0, sb0);
+    stage(6 * r + 2, sa0, sb2, sa1, sb1);
+    stage(6 * r + 3, sa1, sb0, sa0, sb2);
+    stage(6 * r + 4, sa0, sb1, sa1, sb0);
+    stage(6 * r + 5, sa1, sb2, sa0, sb1);
+  }
+  {
+    const int rest = stages - rounds * 6;
+    if (rest > 0) stage(6 * rounds, sa0, sb0, sa1, sb2);
+    if (rest > 1) stage(6 * rounds + 1, sa1, sb1, sa0, sb0);
+    if (rest > 2) stage(6 * rounds + 2, sa0, sb2, sa1, sb1);
+    if (rest > 3) stage(6 * rounds + 3, sa1, sb0, sa0, sb2);
+    if (rest > 4) stage(6 * rounds + 4, sa0, sb1, sa1, sb0);
   }
   if (grp == 0) barrier();  // every wave passes the same number of barriers
   // no load may still be writing this workgroup's LDS when it exits
@@ -319,10 +346,10 @@ hipError_t launch_grouped_gemm_i8(const GemmArgs& a, hipStream_t stream) {
   if (blocks > kGemmMaxBlocks) return hipErrorInvalidValue;
   const dim3 grid(static_cast<uint32_t>(blocks)), block(kWave * kGemmWavesM * kGemmWavesN);
   if (select::gemm_k_tail(a.k)) {
-    grouped_gemm_kernel<kGemmTileM, kGemmTileN, kGemmWavesM, kGemmWavesN, kGemmRing, true>
+    grouped_gemm_kernel<kGemmTileM, kGemmTileN, kGemmWavesM, kGemmWavesN, true>
         <<<grid, block, 0, stream>>>(a);
   } else {
-    grouped_gemm_kernel<kGemmTileM, kGemmTileN, kGemmWavesM, kGemmWavesN, kGemmRing, false>
+    grouped_gemm_kernel<kGemmTileM, kGemmTileN, kGemmWavesM, kGemmWavesN, false>
         <<<grid, block, 0, stream>>>(a);
   }
   return hipGetLastError();

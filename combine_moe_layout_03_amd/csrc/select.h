@@ -80,12 +80,10 @@ constexpr int epilogue_shape_index(int n) {
   return -1;
 }
 
-// ---- first expert matmul: k is walked in 64-byte LDS stages, a ring of 4 ----
-// A k that is not a whole number of ring rounds runs the instance that masks
-// the tail.
-constexpr int kGemmStageK = 64;
-constexpr int kGemmRingStages = 4;
-constexpr bool gemm_k_tail(int k) { return k % (kGemmStageK * kGemmRingStages) != 0; }
+// ---- first expert matmul: k is walked in 128-byte LDS stages ----------------
+// A k that ends inside a stage runs the instance that masks the tail.
+constexpr int kGemmStageK = 128;
+constexpr bool gemm_k_tail(int k) { return k % kGemmStageK != 0; }
 
 }  // namespace select
 }  // namespace moe
