@@ -56,8 +56,7 @@ OUT_KINDS = ["bf16", "fp16", "fp32"]
 # with a ragged tail where possible.
 EPILOGUE_NS = [(40, 200), (30, 500), (25, 1020), (20, 2044), (12, 4092)]  # (rows, n)
 
-# Grouped GEMM: k a whole number of ring rounds (4 stages of 64 bytes), and
-# k that is not (here ending inside a stage)
+# Grouped GEMM: k a whole number of 128-byte stages, and k ending inside one
 # (rows, k, n, groups, counts)
 GEMM_CASES = [(700, 1024, 1024, 4, [100, 0, 350, 240]), (650, 336, 512, 3, [300, -2, 340])]
 

@@ -81,6 +81,9 @@ def _slot(counts, rows, slot, tm):
     (2000, 64, 2048, "owned:1990:130"),
     (300, 144, 7168, [100, 0, 200]),
     (900, 1008, 520, "owned:880:4"),
+    (700, 384, 600, "owned:690:3"),
+    (600, 1536, 260, [300, 290]),
+    (300, 1392, 256, [300]),
 ])
 def test_grid_covers_owned_outputs_once_and_loads_stay_in_bounds(rows, k, n, counts):
     tm, tn, wm, wn, sk, groups_c, xrows = _shape()

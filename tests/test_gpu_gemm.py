@@ -7,8 +7,9 @@ shape the benchmark times and at the layer's second matmul, on every row of
 each expert's first whole row tile and of its last (partial) tile -- so
 every row on both sides of every expert boundary, and the output's last
 rows -- plus rows drawn at random, all columns of each.  The cases cover
-several row and column tiles with ragged ends, k that ends inside a 64-byte
-stage and k that is not a whole number of ring rounds (4 stages), empty and
+several row and column tiles with ragged ends; k a whole number of 128-byte
+stages and k ending inside one, each with every remainder of the stage
+count modulo 6 (the period of the kernel's LDS slot rotation); empty and
 negative counts, counts past the row capacity, more experts than one wave
 scans at once, and the int8 receive buffer used in place.
 """
@@ -108,7 +109,7 @@ def boundary_tile_rows(case, seed, n_random=32):
 
 
 @pytest.mark.parametrize("rows,k,n,groups,counts,seed", [
-    # 4 row tiles and 2 column tiles, both ragged; k is 5 stages (one past a ring round)
+    # 4 row tiles and 2 column tiles, both ragged; k ends inside the 3rd stage
     (1000, 320, 300, 5, "owned:900", 501),
     # empty and negative counts; one expert spans three row tiles
     (830, 128, 128, 6, [0, 300, -5, 1, 0, 517], 502),
@@ -121,11 +122,18 @@ def boundary_tile_rows(case, seed, n_random=32):
     # n = 1 and a single expert
     (257, 48, 1, 1, [257], 506),
     # 4 and 8 column tiles (the XCD-aware tile order), empty and negative counts,
-    # k one stage past a whole ring round
-    (1000, 320, 1024, 6, [0, 300, -5, 1, 0, 517], 507),
+    # k 5 whole stages
+    (1000, 640, 1024, 6, [0, 300, -5, 1, 0, 517], 507),
+    # k ending inside the 9th stage
     (1500, 1088, 2048, 9, "owned:1490", 508),
-    # k ending 48 bytes into the last stage of whole ring rounds; 3 ragged column tiles
+    # k ending inside the 8th stage; 3 ragged column tiles
     (900, 1008, 520, 4, "owned:880", 509),
+    # k 3, 12 whole stages; k ending inside the 6th, 10th, 11th stage
+    (700, 384, 600, 3, "owned:690", 510),
+    (600, 1536, 260, 2, [300, 290], 511),
+    (500, 656, 256, 3, "owned:500", 512),
+    (400, 1264, 384, 2, [150, 250], 513),
+    (300, 1392, 256, 1, [300], 514),
 ])
 def test_gemm_matches_oracle(rows, k, n, groups, counts, seed):
     if isinstance(counts, str):

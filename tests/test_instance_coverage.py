@@ -173,7 +173,7 @@ def test_tables_list_exactly_the_compiled_instances(selection, compiled):
         have = compiled.get(family, set())
         if family == "combine_kernel":  # <Recv, Out, 32 entries, 8 elements, 4 waves, nt load, nt store>
             have = {a[:2] for a in have}
-        elif family == "grouped_gemm_kernel":  # <tile M, tile N, waves M, waves N, ring, k tail>
+        elif family == "grouped_gemm_kernel":  # <tile M, tile N, waves M, waves N, k tail>
             have = {a[-1:] for a in have}
         elif family == "dispatch_kernel":
             assert all(len(a) == 3 for a in have), f"dispatch_kernel template arguments changed: {have}"
