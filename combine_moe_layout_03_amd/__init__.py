@@ -30,6 +30,7 @@ __all__ = [
     "moe_dispatch_src", "moe_combine_src", "EpMultiBuffers", "MOE_MAX_SOURCES",
     "moe_deq_swiglu_quant", "token_scales_of", "MOE_EPILOGUE_MAX_N", "moe_grouped_gemm_i8",
     "MOE_GEMM_MAX_K", "MOE_GEMM_MAX_N", "MOE_GEMM_MAX_GROUPS", "moe_layout_no_alloc",
+    "moe_gemm_swiglu_quant_workspace_bytes", "moe_grouped_gemm_swiglu_quant_i8",
     "MOE_NO_ALLOC_SCRATCH_BYTES",
 ]
 
@@ -67,6 +68,9 @@ _SIGS = {
                                     _P, _P, _P, _SZ, _P, _SZ, _P], _INT),
     "moe_deq_swiglu_quant": ([_P, _I32, _I32, _P, _P, ctypes.c_int64, _P, _SZ, _P], _INT),
     "moe_grouped_gemm_i8": ([_P, ctypes.c_int64, _I32, _I32, _P, _I32, _P, _I32, _P, _SZ, _P], _INT),
+    "moe_gemm_swiglu_quant_workspace_bytes": ([_I32, _I32, ctypes.POINTER(_SZ)], _INT),
+    "moe_grouped_gemm_swiglu_quant_i8": ([_P, ctypes.c_int64, _I32, _I32, _P, _I32, _P, _I32, _P, _P,
+                                          ctypes.c_int64, _P, _SZ, _P, _SZ, _P], _INT),
     "moe_status_str": ([_INT], ctypes.c_char_p),
     "moe_last_hip_error": ([], _INT),
 }
@@ -357,6 +361,44 @@ def moe_grouped_gemm_i8(a: torch.Tensor, a_row_bytes: int, rows: int, k: int,
         _dev(a, "a"), a_row_bytes, rows, k, _dev(group_count, "group_count", torch.int32), groups,
         _dev(w, "w"), n, _dev(out, "out", torch.int32), out.numel() * out.element_size(),
         _stream(stream)))
+
+
+def moe_gemm_swiglu_quant_workspace_bytes(rows: int, n: int) -> int:
+    out = _SZ(0)
+    _check("moe_gemm_swiglu_quant_workspace_bytes",
+           _lib.moe_gemm_swiglu_quant_workspace_bytes(rows, n, ctypes.byref(out)))
+    return out.value
+
+
+def moe_grouped_gemm_swiglu_quant_i8(a: torch.Tensor, a_row_bytes: int, rows: int, k: int,
+                                     group_count: torch.Tensor, w: torch.Tensor, weight_scale: torch.Tensor,
+                                     token_scale: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                                     token_scale_stride: int = 4, stream=None) -> None:
+    """The first expert matmul with its epilogue fused: ``a``, a_row_bytes,
+    rows, k and group_count as for ``moe_grouped_gemm_i8``; w int8 [groups,
+    2n, k] (gate rows, then up rows); weight_scale float32 [groups, 2n];
+    token_scale and token_scale_stride as for ``moe_deq_swiglu_quant``; out a
+    uint8 buffer of int8 rows (moe_recv_row_bytes(n, MOE_INT8_ROWSCALE) bytes
+    each; rows no expert owns are not written); workspace a device buffer of
+    moe_gemm_swiglu_quant_workspace_bytes(rows, n) bytes."""
+    if w.dim() != 3 or w.shape[2] != k or w.shape[1] % 2 or w.dtype not in (torch.int8, torch.uint8):
+        raise ValueError("w must be int8 [groups, 2n, k]")
+    groups, n = w.shape[0], w.shape[1] // 2
+    if group_count.numel() != groups:
+        raise ValueError("group_count must hold one count per group")
+    if weight_scale.numel() != groups * 2 * n:
+        raise ValueError("weight_scale must hold groups * 2n floats")
+    if a.dtype not in (torch.int8, torch.uint8):
+        raise ValueError("a must be a byte buffer")
+    if rows > 0 and a.numel() < (rows - 1) * a_row_bytes + k:
+        raise ValueError("a is smaller than (rows - 1) * a_row_bytes + k bytes")
+    if not token_scale.is_cuda:
+        raise ValueError("token_scale must be a device tensor")
+    _check("moe_grouped_gemm_swiglu_quant_i8", _lib.moe_grouped_gemm_swiglu_quant_i8(
+        _dev(a, "a"), a_row_bytes, rows, k, _dev(group_count, "group_count", torch.int32), groups,
+        _dev(w, "w"), n, _dev(weight_scale, "weight_scale", torch.float32), token_scale.data_ptr(),
+        token_scale_stride, _dev(out, "out"), out.numel() * out.element_size(), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def token_scales_of(recv_x: torch.Tensor, hidden: int) -> Tuple[torch.Tensor, int]:

@@ -458,6 +458,66 @@ int moe_grouped_gemm_i8(const void* a, int64_t a_row_bytes, int32_t rows, int32_
   return hip_status(moe::launch_grouped_gemm_i8(g, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+constexpr size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+size_t swiglu_act_bytes(int32_t rows, int32_t n) {
+  return align256(static_cast<size_t>(rows) * static_cast<size_t>(n) * 4u);
+}
+}  // namespace
+
+int moe_gemm_swiglu_quant_workspace_bytes(int32_t rows, int32_t n, size_t* bytes) {
+  if (!bytes) return MOE_ERR_NULL_PTR;
+  if (rows < 0 || n < 1) return MOE_ERR_BAD_SHAPE;
+  *bytes = swiglu_act_bytes(rows, n) + align256(static_cast<size_t>(rows) * 4u);
+  return MOE_OK;
+}
+
+int moe_grouped_gemm_swiglu_quant_i8(const void* a, int64_t a_row_bytes, int32_t rows, int32_t k,
+                                     const int32_t* group_count, int32_t groups, const void* w, int32_t n,
+                                     const float* weight_scale, const void* token_scale,
+                                     int64_t token_scale_stride, void* out, size_t out_bytes, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (rows < 0 || k < 1 || n < 1 || groups < 1 || a_row_bytes < k || token_scale_stride < 4 ||
+      token_scale_stride % 4 != 0)
+    return MOE_ERR_BAD_SHAPE;
+  if (k % 16 != 0 || k > MOE_GEMM_MAX_K || n % 4 != 0 || n > MOE_GEMM_MAX_N / 2 || groups > MOE_GEMM_MAX_GROUPS)
+    return MOE_ERR_UNSUPPORTED;
+  if (a_row_bytes % 16 != 0) return MOE_ERR_BAD_ALIGN;
+  if (rows == 0) return MOE_OK;
+  if (!a || !group_count || !w || !weight_scale || !token_scale || !out || !workspace) return MOE_ERR_NULL_PTR;
+  if (!aligned(a, 16) || !aligned(w, 16) || !aligned(group_count, 4) || !aligned(weight_scale, 4) ||
+      !aligned(token_scale, 4) || !aligned(out, 16) || !aligned(workspace, 16))
+    return MOE_ERR_BAD_ALIGN;
+  size_t rb = 0;
+  int st = row_bytes(n, MOE_INT8_ROWSCALE, &rb);
+  if (st) return st;
+  if (out_bytes / rb < static_cast<size_t>(rows)) return MOE_ERR_BUFFER_TOO_SMALL;
+  size_t need = 0;
+  st = moe_gemm_swiglu_quant_workspace_bytes(rows, n, &need);
+  if (st) return st;
+  if (workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (moe::grouped_gemm_swiglu_blocks(rows, groups, n) > moe::kGemmMaxBlocks) return MOE_ERR_UNSUPPORTED;
+  moe::GemmArgs g{};
+  g.a = static_cast<const int8_t*>(a);
+  g.a_stride = a_row_bytes;
+  g.rows = rows;
+  g.k = k;
+  g.group_count = group_count;
+  g.groups = groups;
+  g.w = static_cast<const int8_t*>(w);
+  g.n = 2 * n;
+  g.sn = n;
+  g.weight_scale = weight_scale;
+  g.token_scale = static_cast<const uint8_t*>(token_scale);
+  g.ts_stride = token_scale_stride;
+  g.act = static_cast<float*>(workspace);
+  g.amax = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + swiglu_act_bytes(rows, n));
+  g.q_out = static_cast<uint8_t*>(out);
+  g.q_row_bytes = static_cast<int64_t>(rb);
+  g.q_scale_off = static_cast<int32_t>(align32(n));
+  return hip_status(moe::launch_grouped_gemm_swiglu_quant(g, static_cast<hipStream_t>(stream)));
+}
+
 const char* moe_status_str(int status) {
   switch (status) {
     case MOE_OK: return "ok";

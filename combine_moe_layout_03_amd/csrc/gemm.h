@@ -17,8 +17,19 @@ struct GemmArgs {
   const int32_t* group_count;  // [groups]: rows of each expert, in order
   int32_t groups;
   const int8_t* w;             // [groups][n][k]
-  int32_t n;
-  int32_t* out;                // [rows][n]
+  int32_t n;                   // weight rows per expert (output columns of the plain form)
+  int32_t* out;                // [rows][n] (the plain form)
+  // The fused form: the SwiGLU epilogue on the accumulators (weights hold 2 sn
+  // rows per expert: gate rows 0 .. sn-1, then up rows sn .. 2 sn - 1).
+  int32_t sn;                  // activation columns
+  const float* weight_scale;   // [groups][2 sn]
+  const uint8_t* token_scale;  // float of row m at byte m * ts_stride
+  int64_t ts_stride;
+  float* act;                  // [rows][sn] activations (workspace)
+  uint32_t* amax;              // [rows] largest |activation| of each row, as bits (workspace)
+  uint8_t* q_out;              // int8 rows: codes [0, sn), inverse scale at q_scale_off
+  int64_t q_row_bytes;
+  int32_t q_scale_off;
 };
 // Workgroup tile (rows x output columns), its waves, the LDS slots, and the
 // XCD-aware tile order (see gemm.hip).
@@ -29,8 +40,12 @@ constexpr int kGemmSlotsA = 2, kGemmSlotsB = 3;    // LDS slots of a stage's A a
 constexpr int kGemmXcdColGroups = 4;               // column groups of the tile order
 constexpr int kGemmXcdRows = 8;                    // row slots per XCD block
 constexpr int64_t kGemmMaxBlocks = int64_t(1) << 24;
-// Workgroups of one launch (row slots x column tiles).
+// Workgroups of one launch (row slots x column tiles), plain and fused.
 int64_t grouped_gemm_blocks(int64_t rows, int32_t groups, int32_t n);
+int64_t grouped_gemm_swiglu_blocks(int64_t rows, int32_t groups, int32_t sn);
 hipError_t launch_grouped_gemm_i8(const GemmArgs& a, hipStream_t stream);
+// The fused form: clears the row maxima, runs the matmul with the SwiGLU
+// epilogue into the workspace, then quantises the owned rows.
+hipError_t launch_grouped_gemm_swiglu_quant(const GemmArgs& a, hipStream_t stream);
 
 }  // namespace moe

@@ -67,14 +67,21 @@
 // last tile exit at once.  Rows past an expert's end are loaded from its last
 // row and never stored; weight rows past n repeat row n - 1 and are never
 // stored.
+#include <type_traits>
+
 #include "device_util.h"
 #include "launch.h"
 #include "gemm.h"
+#include "quant.h"
+#include "swiglu.h"
+
+#pragma clang fp contract(off)
 
 namespace moe {
 namespace {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define MOE_LDS __attribute__((address_space(3)))
 
 constexpr int kSK = kGemmStageK;               // bytes of k per stage
@@ -135,7 +142,7 @@ int64_t launch_slots(int64_t rows, int32_t groups, int64_t n_tiles) {
   return slots;
 }
 
-template <int TM, int TN, int WM, int WN, bool kTail>
+template <int TM, int TN, int WM, int WN, bool kTail, bool kFused>
 __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs a) {
   constexpr int kWaves = WM * WN;
   constexpr int kWaveM = TM / WM, kWaveN = TN / WN;
@@ -160,7 +167,9 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
   const int tid = threadIdx.x, lane = tid % kWave, wave = uniform(tid / kWave);
 
   // workgroup -> (row slot, column tile)
-  const int64_t n_tiles = (a.n + TN - 1) / TN;
+  // The fused form's column tile j covers gate rows [j TN/2, (j+1) TN/2) of
+  // the weights and the up rows sn above them.
+  const int64_t n_tiles = kFused ? (a.sn + TN / 2 - 1) / (TN / 2) : (a.n + TN - 1) / TN;
   int64_t slot, col_tile;
   if (n_tiles % kGemmXcdColGroups == 0) {
     const int64_t g = blockIdx.x, x = g % 8, l = g / 8;
@@ -203,7 +212,11 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
 #pragma unroll
   for (int q = 0; q < kLoadsB; ++q) {
     const int r = kRowsPerLoad * (q * kWaves + wave) + lane / kPieces;
-    const int col = min(col0 + r, a.n - 1);
+    int col = min(col0 + r, a.n - 1);
+    if constexpr (kFused) {
+      const int j = static_cast<int>(col_tile) * (TN / 2) + r % (TN / 2);
+      col = (r < TN / 2 ? 0 : a.sn) + min(j, a.sn - 1);
+    }
     src_b[q] = a.w + (static_cast<int64_t>(group) * a.n + col) * a.k + piece * 16;
   }
   const int stages = (a.k + kSK - 1) / kSK;
@@ -318,24 +331,146 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
 
   // 16 x 16 result tile: lane l holds column l % 16 of rows 4 * (l / 16) + 0..3
+  if constexpr (!kFused) {
 #pragma unroll
-  for (int i = 0; i < kMI; ++i) {
+    for (int i = 0; i < kMI; ++i) {
 #pragma unroll
-    for (int j = 0; j < kNI; ++j) {
-      const int col = col0 + wn * kWaveN + j * 16 + lane % 16;
+      for (int j = 0; j < kNI; ++j) {
+        const int col = col0 + wn * kWaveN + j * 16 + lane % 16;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = row0 + wm * kWaveM + i * 16 + (lane / 16) * 4 + r;
-        if (row < row_end && col < a.n) a.out[static_cast<int64_t>(row) * a.n + col] = acc[i][j][r];
+        for (int r = 0; r < 4; ++r) {
+          const int row = row0 + wm * kWaveM + i * 16 + (lane / 16) * 4 + r;
+          if (row < row_end && col < a.n) a.out[static_cast<int64_t>(row) * a.n + col] = acc[i][j][r];
+        }
       }
     }
+  } else {
+    // The waves wn = 0 hold gate sums and wn = 1 the up sums of the same
+    // rows and activation columns.  Each wave of such a pair (wave ^ 1)
+    // finishes half the pair's row tiles: it hands the other half of its
+    // sums to its partner through LDS (free once every wave is past this
+    // barrier), then computes the activations of its rows, folds their
+    // magnitudes into the rows' maxima and stores them.
+    static_assert(WN == 2 && kMI % 2 == 0, "gate and up halves of a pair of waves");
+    constexpr int kHalf = kMI / 2;
+    static_assert(2 * kHalf * kNI * kWave * 16 <= TM * kSK, "a pair's exchange fits in one slot");
+    barrier();
+    uint8_t* const pool = wave < 2 ? sa0 : wave < 4 ? sa1 : wave < 6 ? sb0 : sb1;
+    uint8_t* const mine = pool + (wave % 2) * (kHalf * kNI * kWave * 16);
+    const uint8_t* const theirs = pool + ((wave % 2) ^ 1) * (kHalf * kNI * kWave * 16);
+    const int j_base = static_cast<int>(col_tile) * (TN / 2) + lane % 16;
+    const float* ws = a.weight_scale + static_cast<int64_t>(group) * 2 * a.sn;
+    float wg[kNI], wu[kNI];
+#pragma unroll
+    for (int j = 0; j < kNI; ++j) {
+      const int jo = min(j_base + j * 16, a.sn - 1);
+      wg[j] = ws[jo];
+      wu[j] = ws[a.sn + jo];
+    }
+    // kKeep: the first row tile this wave finishes (0 for the gate wave); a
+    // compile-time index, so the accumulators stay in registers
+    auto finish = [&](auto keep_c) {
+      constexpr int kKeep = decltype(keep_c)::value;
+      constexpr int kGive = kHalf - kKeep;
+#pragma unroll
+      for (int ii = 0; ii < kHalf; ++ii)
+#pragma unroll
+        for (int j = 0; j < kNI; ++j)
+          *reinterpret_cast<i32x4*>(mine + ((ii * kNI + j) * kWave + lane) * 16) = acc[kGive + ii][j];
+      barrier();
+#pragma unroll
+      for (int ii = 0; ii < kHalf; ++ii) {
+        float ts[4];
+        int rows_[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          rows_[r] = row0 + wm * kWaveM + (kKeep + ii) * 16 + (lane / 16) * 4 + r;
+          const int rs = min(rows_[r], row_end - 1);
+          ts[r] = *reinterpret_cast<const float*>(a.token_scale + static_cast<int64_t>(rs) * a.ts_stride);
+        }
+        uint32_t mag[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < kNI; ++j) {
+          const i32x4 other = *reinterpret_cast<const i32x4*>(theirs + ((ii * kNI + j) * kWave + lane) * 16);
+          const i32x4 gate = kKeep == 0 ? acc[kKeep + ii][j] : other;
+          const i32x4 up = kKeep == 0 ? other : acc[kKeep + ii][j];
+          const int jo = j_base + j * 16;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float y = swiglu(gate[r], up[r], wg[j], wu[j], ts[r]);
+            if (rows_[r] < row_end && jo < a.sn) {
+              const uint32_t b = __float_as_uint(y) & 0x7fffffffu;  // |y| orders as an integer
+              mag[r] = mag[r] > b ? mag[r] : b;
+              a.act[static_cast<int64_t>(rows_[r]) * a.sn + jo] = y;
+            }
+          }
+        }
+        // the row's maximum over its 16 lanes (the tile's columns), then
+        // over the launch's column tiles through the global maximum
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+          for (int d = 1; d < 16; d <<= 1) {
+            const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(mag[r]), d, kWave));
+            mag[r] = mag[r] > o ? mag[r] : o;
+          }
+          if (lane % 16 == 0 && rows_[r] < row_end) atomicMax(a.amax + rows_[r], mag[r]);
+        }
+      }
+    };
+    if (wn == 0) finish(std::integral_constant<int, 0>{});
+    else finish(std::integral_constant<int, kHalf>{});
   }
+}
+
+// Clears the row maxima of the fused form.
+__global__ __launch_bounds__(256) void clear_u32_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = 0;
+}
+
+// Quantises the activations of the rows an expert owns, one wave per row,
+// exactly as the epilogue kernel quantises a row: s = 127 / (max|a| +
+// 1e-12f), codes rint(a * s), inverse scale 1 / s.  Rows past the owned
+// total are not written.
+constexpr int kQuantRows = 4;  // waves (rows) per workgroup
+__global__ __launch_bounds__(kWave * kQuantRows) void act_quant_kernel(GemmArgs a) {
+  const int lane = threadIdx.x % kWave, wave = uniform(static_cast<int>(threadIdx.x / kWave));
+  int64_t owned = 0;
+  for (int g0 = 0; g0 < a.groups; g0 += kWave) {
+    const int g = g0 + lane;
+    const int c = g < a.groups ? max(a.group_count[g], 0) : 0;
+    owned += __shfl(wave_inclusive_scan(c), kWave - 1, kWave);
+    if (owned >= a.rows) break;
+  }
+  owned = min(owned, a.rows);
+  const int64_t m = static_cast<int64_t>(blockIdx.x) * kQuantRows + wave;
+  if (m >= owned) return;
+  const float amax = __uint_as_float(a.amax[m]);
+  const float s = 127.0f / (amax + 1e-12f);
+  const float inv = 1.0f / s;
+  const f32x4* src = reinterpret_cast<const f32x4*>(a.act + m * a.sn);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(a.q_out + m * a.q_row_bytes);
+  for (int c = lane; c < a.sn / 4; c += kWave) {
+    const f32x4 v = __builtin_nontemporal_load(src + c);
+    const uint32_t b0 = code_bits(v[0], s) & 0xffu;
+    const uint32_t b1 = code_bits(v[1], s) & 0xffu;
+    const uint32_t b2 = code_bits(v[2], s) & 0xffu;
+    const uint32_t b3 = code_bits(v[3], s);
+    dst[c] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+  }
+  if (lane == 0) *reinterpret_cast<float*>(a.q_out + m * a.q_row_bytes + a.q_scale_off) = inv;
 }
 
 }  // namespace
 
 int64_t grouped_gemm_blocks(int64_t rows, int32_t groups, int32_t n) {
   const int64_t n_tiles = (n + kGemmTileN - 1) / kGemmTileN;
+  return launch_slots(rows, groups, n_tiles) * n_tiles;
+}
+
+int64_t grouped_gemm_swiglu_blocks(int64_t rows, int32_t groups, int32_t sn) {
+  const int64_t n_tiles = (sn + kGemmTileN / 2 - 1) / (kGemmTileN / 2);
   return launch_slots(rows, groups, n_tiles) * n_tiles;
 }
 
@@ -346,12 +481,36 @@ hipError_t launch_grouped_gemm_i8(const GemmArgs& a, hipStream_t stream) {
   if (blocks > kGemmMaxBlocks) return hipErrorInvalidValue;
   const dim3 grid(static_cast<uint32_t>(blocks)), block(kWave * kGemmWavesM * kGemmWavesN);
   if (select::gemm_k_tail(a.k)) {
-    grouped_gemm_kernel<kGemmTileM, kGemmTileN, kGemmWavesM, kGemmWavesN, true>
+    grouped_gemm_kernel<kGemmTileM, kGemmTileN, kGemmWavesM, kGemmWavesN, true, false>
         <<<grid, block, 0, stream>>>(a);
   } else {
-    grouped_gemm_kernel<kGemmTileM, kGemmTileN, kGemmWavesM, kGemmWavesN, false>
+    grouped_gemm_kernel<kGemmTileM, kGemmTileN, kGemmWavesM, kGemmWavesN, false, false>
         <<<grid, block, 0, stream>>>(a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_swiglu_quant(const GemmArgs& a, hipStream_t stream) {
+  if (a.rows == 0) return hipSuccess;
+  const int64_t blocks = grouped_gemm_swiglu_blocks(a.rows, a.groups, a.sn);
+  if (blocks > kGemmMaxBlocks) return hipErrorInvalidValue;
+  const int64_t clear_blocks = (a.rows + 255) / 256;
+  clear_u32_kernel<<<dim3(static_cast<uint32_t>(clear_blocks < 4096 ? clear_blocks : 4096)), dim3(256), 0, stream>>>(
+      a.amax, a.rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid(static_cast<uint32_t>(blocks)), block(kWave * kGemmWavesM * kGemmWavesN);
+  if (select::gemm_k_tail(a.k)) {
+    grouped_gemm_kernel<kGemmTileM, kGemmTileN, kGemmWavesM, kGemmWavesN, true, true>
+        <<<grid, block, 0, stream>>>(a);
+  } else {
+    grouped_gemm_kernel<kGemmTileM, kGemmTileN, kGemmWavesM, kGemmWavesN, false, true>
+        <<<grid, block, 0, stream>>>(a);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  act_quant_kernel<<<dim3(static_cast<uint32_t>((a.rows + kQuantRows - 1) / kQuantRows)), dim3(kWave * kQuantRows), 0,
+                     stream>>>(a);
   return hipGetLastError();
 }
 

@@ -343,6 +343,50 @@ int moe_grouped_gemm_i8(const void* a, int64_t aRowBytes, int32_t rows, int32_t 
                         const int32_t* groupCount, int32_t groups, const void* w, int32_t n,
                         int32_t* out, size_t outBytes, void* stream);
 
+/* Bytes of workspace that moe_grouped_gemm_swiglu_quant_i8 needs for `rows`
+ * rows and n activation columns (the query-size, caller-allocates convention
+ * of page section 6.7): the activations as floats [rows][n] and one word per
+ * row.  Requires rows >= 0 and n >= 1 (else MOE_ERR_BAD_SHAPE). */
+int moe_gemm_swiglu_quant_workspace_bytes(int32_t rows, int32_t n, size_t* bytes);
+
+/* The first expert matmul with its epilogue fused -- page section 4.8.1
+ * (GMM1 with the PerTokenDequantSwiGLU epilogue on its accumulators) and
+ * section 4.3 (stage 2, GMM1 then DeqSwigluQuant): the int32 sums never
+ * reach memory.  For every row m owned by expert g (as moe_grouped_gemm_i8
+ * defines ownership), out row m is bit for bit what moe_deq_swiglu_quant
+ * writes for row m of moe_grouped_gemm_i8's output with expert g's scales:
+ *   acc[j] = sum over i < k of a[m][i] * w[g][j][i], j < 2n (gate j < n, up n + j)
+ *   act_j  = Swish((float(acc[j]) * ws[g][j]) * ts_m) * ((float(acc[n+j]) * ws[g][n+j]) * ts_m)
+ *   codes rint(act_j * s), s = 127 / (max_j |act_j| + 1e-12f), inverse 1/s.
+ *
+ * a, aRowBytes, rows, k, groupCount, groups: as moe_grouped_gemm_i8.
+ * w          [groups][2n][k] int8, device, 16-byte aligned: expert g's gate
+ *            weights (output columns 0 .. n-1), then its up weights.
+ * weightScale [groups][2n] float, device, 4-byte aligned: per-expert,
+ *            per-column dequant scales.
+ * tokenScale, tokenScaleStride: as moe_deq_swiglu_quant (the int8 receive
+ *            buffer's inverse scales in place, or a dense float array).
+ * out        device, 16-byte aligned, outBytes >= rows * moe_recv_row_bytes(n,
+ *            MOE_INT8_ROWSCALE): int8 rows in the receive-buffer format.
+ *            Rows that no expert owns are not written.
+ * workspace  device, 16-byte aligned, workspaceBytes >=
+ *            moe_gemm_swiglu_quant_workspace_bytes(rows, n); caller-owned,
+ *            contents on return unspecified.
+ *
+ * Requires rows >= 0, k >= 1, n >= 1, groups >= 1, aRowBytes >= k,
+ * tokenScaleStride a multiple of 4 and >= 4 (else MOE_ERR_BAD_SHAPE);
+ * k % 16 == 0, k <= MOE_GEMM_MAX_K, n % 4 == 0, 2n <= MOE_GEMM_MAX_N, groups
+ * <= MOE_GEMM_MAX_GROUPS (else MOE_ERR_UNSUPPORTED); aRowBytes a multiple of
+ * 16 (else MOE_ERR_BAD_ALIGN); a small workspace gives
+ * MOE_ERR_WORKSPACE_TOO_SMALL.  rows == 0 enqueues nothing.  Enqueues three
+ * kernels (clear the row maxima, the matmul with the activation, the
+ * quantisation). */
+int moe_grouped_gemm_swiglu_quant_i8(const void* a, int64_t aRowBytes, int32_t rows, int32_t k,
+                                     const int32_t* groupCount, int32_t groups, const void* w, int32_t n,
+                                     const float* weightScale, const void* tokenScale,
+                                     int64_t tokenScaleStride, void* out, size_t outBytes, void* workspace,
+                                     size_t workspaceBytes, void* stream);
+
 /* Diagnostics.  No counterpart on the pages (their operator calls report
  * failure through the framework's own status; section 6.7 does not show it):
  * the text of one of this library's status codes (static storage). */

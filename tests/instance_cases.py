@@ -60,6 +60,10 @@ EPILOGUE_NS = [(40, 200), (30, 500), (25, 1020), (20, 2044), (12, 4092)]  # (row
 # (rows, k, n, groups, counts)
 GEMM_CASES = [(700, 1024, 1024, 4, [100, 0, 350, 240]), (650, 336, 512, 3, [300, -2, 340])]
 
+# The matmul with its fused epilogue, the same two k: (rows, k, n, groups,
+# counts), n the activation columns (the weights have 2n rows per expert)
+FUSED_GEMM_CASES = [(700, 1024, 512, 4, [100, 0, 350, 240]), (650, 336, 260, 3, [300, -2, 340])]
+
 
 def case_id(case) -> str:
     seed, bs, h, k, e, r, route, bad, xk, q = case

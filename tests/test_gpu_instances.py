@@ -7,6 +7,7 @@ when it does not apply) and the separate stages, and combine into every
 output type; everything is compared bit for bit with the oracle.
 """
 
+import numpy as np
 import pytest
 import torch
 
@@ -52,3 +53,13 @@ def test_instance_grouped_gemm(rows, k, n, groups, counts):
     case = W.gemm_case(950 + k, rows, k, n, groups, stride=(k + 31) // 32 * 32 + 32, counts=counts)
     log(f"instance grouped gemm rows={rows} k={k} n={n}")
     assert_same(case, run_gpu(case), f"k={k}")
+
+
+@pytest.mark.parametrize("rows,k,n,groups,counts", IC.FUSED_GEMM_CASES,
+                         ids=[f"k{c[1]}" for c in IC.FUSED_GEMM_CASES])
+def test_instance_grouped_gemm_swiglu(rows, k, n, groups, counts):
+    from test_gpu_gemm_swiglu import assert_rows, make_case, run_fused
+
+    case, ws, ts = make_case(960 + k, rows, k, n, groups, counts)
+    log(f"instance grouped gemm + swiglu rows={rows} k={k} n={n}")
+    assert_rows(case, ws, ts, run_fused(case, ws, ts), np.arange(rows), f"k={k}")

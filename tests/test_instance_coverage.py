@@ -82,7 +82,7 @@ def selection():
         subprocess.run(["g++", "-std=c++17", "-O1", f"-I{CSRC}", src, "-o", exe], check=True)
         lines = [f"p {c[1]} {c[2]} {c[3]} {c[4]}" for c in IC.PIPELINE_CASES]
         lines += [f"e {n}" for _, n in IC.EPILOGUE_NS]
-        lines += [f"g {c[1]}" for c in IC.GEMM_CASES]
+        lines += [f"g {c[1]}" for c in IC.GEMM_CASES + IC.FUSED_GEMM_CASES]
         r = subprocess.run([exe], input="\n".join(lines) + "\n", capture_output=True, text=True, check=True)
     out = r.stdout.splitlines()
     tables = {}
@@ -93,7 +93,7 @@ def selection():
     epi = [tuple(map(int, line.split()[1:])) for line in out[6:] if line.startswith("e ")]
     gemm = [int(line.split()[1]) for line in out[6:] if line.startswith("g ")]
     assert len(pipe) == len(IC.PIPELINE_CASES) and len(epi) == len(IC.EPILOGUE_NS)
-    assert len(gemm) == len(IC.GEMM_CASES)
+    assert len(gemm) == len(IC.GEMM_CASES) + len(IC.FUSED_GEMM_CASES)
     return tables, pipe, epi, gemm
 
 
@@ -132,7 +132,7 @@ def expected(tables):
         "deq_swiglu_quant_kernel": set(t["epilogue"]),
         "layout_count_kernel": set(t["layout"]),
         "layout_rank_kernel": set(t["layout"]),
-        "grouped_gemm_kernel": {(0,), (1,)},
+        "grouped_gemm_kernel": {(t, f) for t in (0, 1) for f in (0, 1)},
     }
     return exp
 
@@ -142,8 +142,8 @@ def reached(selection):
     got = {k: set() for k in ("fused_kernel", "dispatch_kernel", "combine_rows_kernel", "combine_kernel",
                               "deq_swiglu_quant_kernel", "layout_count_kernel", "layout_rank_kernel",
                               "grouped_gemm_kernel")}
-    for tail in gemm:
-        got["grouped_gemm_kernel"].add((tail,))
+    for i, tail in enumerate(gemm):  # the plain cases, then the fused ones
+        got["grouped_gemm_kernel"].add((tail, int(i >= len(IC.GEMM_CASES))))
     for case, ans in zip(IC.PIPELINE_CASES, pipe):
         seed, bs, h, k, e, r, route, bad, xk, q = case
         applies, fvpl, dvpl, kmax, chunks, lw, lr, tiles = ans
@@ -173,8 +173,8 @@ def test_tables_list_exactly_the_compiled_instances(selection, compiled):
         have = compiled.get(family, set())
         if family == "combine_kernel":  # <Recv, Out, 32 entries, 8 elements, 4 waves, nt load, nt store>
             have = {a[:2] for a in have}
-        elif family == "grouped_gemm_kernel":  # <tile M, tile N, waves M, waves N, k tail>
-            have = {a[-1:] for a in have}
+        elif family == "grouped_gemm_kernel":  # <tile M, tile N, waves M, waves N, k tail, fused>
+            have = {a[-2:] for a in have}
         elif family == "dispatch_kernel":
             assert all(len(a) == 3 for a in have), f"dispatch_kernel template arguments changed: {have}"
         assert have == want, f"{family}: compiled {sorted(have)} but the tables give {sorted(want)}"
