@@ -32,7 +32,9 @@ its own JSON line (rows/s).  ``--stage gemm`` times the first expert matmul
 (int8 receive rows x int8 expert weights -> int32, grouped by expert) on one
 GPU's share of the large shape on a 16-rank expert-parallel group (32768
 rows, 16 experts, k = 7168, 2 x 2048 output columns) and prints its own line
-(rows/s, with int8 TOP/s against the MFMA peak).
+(rows/s, with int8 TOP/s against the MFMA peak).  ``--stage gemm_swiglu``
+times the same matmul with its epilogue fused (int8 rows in, int8 rows of
+width 2048 out), beside the two separate calls in the same run.
 
 Output: one JSON line on stdout.  ``--gpus N`` with N > 1 exits: the bench
 measures one GPU.
@@ -64,11 +66,15 @@ KERNEL_SOURCES = {
     "dispatch": [os.path.join(CSRC, "dispatch.hip")] + KERNEL_HEADERS,
     "combine": [os.path.join(CSRC, "combine.hip")] + KERNEL_HEADERS,
     "fused": [os.path.join(CSRC, "fused.hip")] + KERNEL_HEADERS,
-    "epilogue": [os.path.join(CSRC, "epilogue.hip")] + KERNEL_HEADERS,
-    "gemm": [os.path.join(CSRC, "gemm.hip"), os.path.join(CSRC, "gemm.h")] + KERNEL_HEADERS,
+    "epilogue": [os.path.join(CSRC, "epilogue.hip"), os.path.join(CSRC, "swiglu.h")] + KERNEL_HEADERS,
+    "gemm": [os.path.join(CSRC, "gemm.hip"), os.path.join(CSRC, "gemm.h"), os.path.join(CSRC, "swiglu.h")]
+    + KERNEL_HEADERS,
 }
+KERNEL_SOURCES["gemm_swiglu"] = KERNEL_SOURCES["gemm"]
 EPILOGUE_METRIC = "expert epilogue (dequant + SwiGLU + int8 requant) rows/s and HBM GB/s (% of peak)"
 GEMM_METRIC = "first expert matmul (int8 x int8 -> int32, grouped by expert) rows/s and TOP/s (% of peak)"
+GEMM_SWIGLU_METRIC = ("first expert matmul with its dequant + SwiGLU + int8 requant epilogue fused, rows/s and "
+                      "TOP/s (% of peak)")
 MFMA_I8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, 5.0 POP/s
 
 
@@ -235,10 +241,10 @@ def main(argv=None) -> int:
                          "buffer (multi-source notify, per-source dispatch and combine)")
     ap.add_argument("--skip-kernels-only", action="store_true",
                     help="with the fused path, do not also time the dispatch and combine kernels alone")
-    ap.add_argument("--stage", default="pipeline", choices=["pipeline", "epilogue", "gemm"],
+    ap.add_argument("--stage", default="pipeline", choices=["pipeline", "epilogue", "gemm", "gemm_swiglu"],
                     help="pipeline: layout + notify + dispatch + combine (the headline); epilogue: the "
                          "expert-side dequant + SwiGLU + int8 requant kernel on its own; gemm: the first "
-                         "expert matmul on its own")
+                         "expert matmul on its own; gemm_swiglu: the matmul with that epilogue fused")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, then WRITE_SIZE) of a bench "
                          "run into profiles/traffic_*.json and exit")
@@ -275,6 +281,8 @@ def main(argv=None) -> int:
         return bench_epilogue(args, M, torch, W, dev)
     if args.stage == "gemm":
         return bench_gemm(args, M, torch, W, dev)
+    if args.stage == "gemm_swiglu":
+        return bench_gemm_swiglu(args, M, torch, W, dev)
     quant = args.mode == "int8"
 
     log(f"generating workload {args.workload}")
@@ -781,6 +789,133 @@ def bench_gemm(args, M, torch, W, dev) -> int:
     return 0
 
 
+def gemm_swiglu_bytes(rows: int, n: int, k: int, groups: int) -> int:
+    """Bytes the fused matmul and epilogue must move at least once: the k
+    codes and the token scale of every row, every expert's 2n weight rows and
+    2n column scales, the n int8 codes and inverse scale written per row, and
+    the counts."""
+    return rows * (k + 4) + groups * 2 * n * (k + 4) + rows * (n + 4) + groups * 4
+
+
+def bench_gemm_swiglu(args, M, torch, W, dev) -> int:
+    """The first expert matmul with its epilogue fused, on the shape of
+    ``--stage gemm`` (2048 activation columns from 2 x 2048 weight rows per
+    expert); caches flushed before each timed call.  The same run times the
+    two separate calls (the matmul to int32, then the epilogue over every
+    row) for comparison."""
+    import numpy as np
+
+    c = W.GEMM_CONFIG
+    rows, k, n2, groups = c["rows"], c["k"], c["n"], c["groups"]
+    n = n2 // 2
+    stride = M.moe_recv_row_bytes(k, M.MOE_INT8_ROWSCALE)
+    log(f"generating inputs rows={rows} k={k} n={n} groups={groups}")
+    case = W.gemm_case(c["seed"], rows, k, n2, groups, stride=stride)
+    ws, ts = W.gemm_swiglu_scales(c["seed"], rows, k, n, groups)
+    a = torch.from_numpy(case.a.reshape(-1).view("uint8")).to(dev)
+    wt = torch.from_numpy(case.w.view("uint8")).to(dev)
+    gc = torch.from_numpy(case.group_count).to(dev)
+    ws_d = torch.from_numpy(ws).to(dev)
+    ts_d = torch.from_numpy(ts).to(dev)
+    rb = M.moe_recv_row_bytes(n, M.MOE_INT8_ROWSCALE)
+    out = torch.zeros(rows * rb, dtype=torch.uint8, device=dev)
+    wsp = torch.empty(M.moe_gemm_swiglu_quant_workspace_bytes(rows, n), dtype=torch.uint8, device=dev)
+    acc = torch.zeros((rows, n2), dtype=torch.int32, device=dev)
+    out2 = torch.zeros(rows * rb, dtype=torch.uint8, device=dev)
+    owned = int(min(max(case.group_count.astype("int64").clip(0).sum(), 0), rows))
+    flush = torch.ones(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    flush_out = torch.zeros((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fused():
+        M.moe_grouped_gemm_swiglu_quant_i8(a, stride, rows, k, gc, wt, ws_d, ts_d, out, wsp)
+
+    def two_calls():
+        M.moe_grouped_gemm_i8(a, stride, rows, k, gc, wt, acc)
+        M.moe_deq_swiglu_quant(acc, ws_d[0], ts_d, out2)
+
+    def timed(fn, steps):
+        hev = HipEvents(args.event_flags)
+        ev = [(hev.new(), hev.new()) for _ in range(steps)]
+        for e0, e1 in ev:
+            torch.sum(flush, dim=0, out=flush_out)
+            hev.record(e0, stream)
+            fn()
+            hev.record(e1, stream)
+        torch.cuda.synchronize()
+        us = [hev.ms(e0, e1) * 1e3 for e0, e1 in ev]
+        hev.close()
+        return us
+
+    log(f"warm-up x{args.warmup}")
+    for _ in range(args.warmup):
+        torch.sum(flush, dim=0, out=flush_out)
+        fused()
+        two_calls()
+    torch.cuda.synchronize()
+    log(f"timed x{args.steps}: fused")
+    us = timed(fused, args.steps)
+    log(f"timed x{args.steps}: two calls")
+    us2 = timed(two_calls, args.steps)
+    mean_us, mean2 = statistics.mean(us), statistics.mean(us2)
+    ops = gemm_ops(owned, n2, k)
+    tops = ops / (mean_us * 1e-6) / 1e12
+    alg = gemm_swiglu_bytes(owned, n, k, groups)
+    cpu = None
+    if args.cpu_budget > 0:
+        import oracle
+
+        log(f"cpu baseline (oracle, ~{args.cpu_budget:.0f} s)")
+        oracle.default()
+        done, t0, batch = 0, time.perf_counter(), 8
+        while True:
+            sel = (W.u64(c["seed"], 40 + done // batch, batch) % np.uint64(owned)).astype("int64")
+            accs, grp = oracle.grouped_gemm_i8(case.a, k, case.group_count, case.w, rows=sel)
+            for i, m in enumerate(sel):
+                oracle.swiglu_quant_row(accs[i], ws[grp[i]], ts[m])
+            done += batch
+            el = time.perf_counter() - t0
+            if el >= args.cpu_budget or done >= 4096:
+                break
+        cpu = dict(value=done / el, unit="rows/s", cores=1, kind="oracle",
+                   sample=f"{done} random rows of the {rows} (each: {n2} x {k} products, then the epilogue), "
+                          f"{el:.1f} s on one host thread",
+                   host_cpu=host_cpu_model(), host_nproc=os.cpu_count())
+    line = {
+        "metric": GEMM_SWIGLU_METRIC,
+        "value": owned / (mean_us * 1e-6),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": mean_us * 1e-3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "payload": "int8 receive rows and int8 expert weights in, int8 rows (codes + fp32 inverse scale) out",
+        "data": "synthetic",
+        "config": {"workload": "gemm_swiglu", "rows": rows, "owned_rows": owned, "k": k, "n": n,
+                   "weight_rows_per_expert": n2, "groups": groups, "row_bytes": stride,
+                   "parallelism": "1 GPU"},
+        "step": "one moe_grouped_gemm_swiglu_quant_i8 call (clear, matmul with the activation, quantisation), "
+                "caches flushed before it",
+        "timer": f"HIP events on the kernels' stream ({args.event_flags})",
+        "stages_us": {"gemm_swiglu": {"mean": mean_us, "p10": pct(us, 0.1), "p50": pct(us, 0.5),
+                                      "p90": pct(us, 0.9)},
+                      "two_calls": {"mean": mean2, "p10": pct(us2, 0.1), "p50": pct(us2, 0.5),
+                                    "p90": pct(us2, 0.9)}},
+        "ops_per_launch": ops,
+        "algorithmic_bytes": {"gemm_swiglu": alg},
+        "roofline": {"bound": "mfma", "kernel": "grouped_gemm_swiglu", "achieved": tops,
+                     "peak": MFMA_I8_PEAK_TOPS, "unit": "TOP/s", "frac": tops / MFMA_I8_PEAK_TOPS,
+                     "traffic": load_traffic("gemm_swiglu", "gemm_swiglu", f"n{n}")},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def library_int8_reference(torch, hev, stream, flush, flush_out, rows, k, n, group_count, reps):
     """The vendor library's int8 x int8 -> int32 GEMM (torch._int_mm, which
     calls hipBLASLt on this stack) at the same sizes, after the same flush,
@@ -1079,7 +1214,15 @@ def ingest_pmc(args, fetch_csv: str, write_csv: str) -> int:
     w = None
     import workloads as W
 
-    if args.stage == "gemm":
+    if args.stage == "gemm_swiglu":
+        cg = W.GEMM_CONFIG
+        workload, mode = "gemm_swiglu", f"n{cg['n'] // 2}"
+        counts = W.gemm_case(cg["seed"], 1, 16, 1, cg["groups"], owned=cg["rows"]).group_count
+        owned = int(min(counts.astype("int64").sum(), cg["rows"]))
+        # the fused instance only (the run also times the plain matmul)
+        kernels = (("gemm_swiglu", ("true>(moe::GemmArgs)",),
+                    gemm_swiglu_bytes(owned, cg["n"] // 2, cg["k"], cg["groups"])),)
+    elif args.stage == "gemm":
         cg = W.GEMM_CONFIG
         workload, mode = "gemm", f"n{cg['n']}"
         counts = W.gemm_case(cg["seed"], 1, 16, 1, cg["groups"], owned=cg["rows"]).group_count

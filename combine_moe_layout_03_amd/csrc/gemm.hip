@@ -354,10 +354,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
     static_assert(WN == 2 && kMI % 2 == 0, "gate and up halves of a pair of waves");
     constexpr int kHalf = kMI / 2;
     static_assert(2 * kHalf * kNI * kWave * 16 <= TM * kSK, "a pair's exchange fits in one slot");
-    barrier();
-    uint8_t* const pool = wave < 2 ? sa0 : wave < 4 ? sa1 : wave < 6 ? sb0 : sb1;
-    uint8_t* const mine = pool + (wave % 2) * (kHalf * kNI * kWave * 16);
-    const uint8_t* const theirs = pool + ((wave % 2) ^ 1) * (kHalf * kNI * kWave * 16);
+    // the scales first, so their loads overlap the exchange below
     const int j_base = static_cast<int>(col_tile) * (TN / 2) + lane % 16;
     const float* ws = a.weight_scale + static_cast<int64_t>(group) * 2 * a.sn;
     float wg[kNI], wu[kNI];
@@ -367,6 +364,19 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
       wg[j] = ws[jo];
       wu[j] = ws[a.sn + jo];
     }
+    const int row_base = row0 + wm * kWaveM + wn * kHalf * 16 + (lane / 16) * 4;  // this wave's first row
+    float ts[kHalf][4];
+#pragma unroll
+    for (int ii = 0; ii < kHalf; ++ii)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rs = min(row_base + ii * 16 + r, row_end - 1);
+        ts[ii][r] = *reinterpret_cast<const float*>(a.token_scale + static_cast<int64_t>(rs) * a.ts_stride);
+      }
+    barrier();
+    uint8_t* const pool = wave < 2 ? sa0 : wave < 4 ? sa1 : wave < 6 ? sb0 : sb1;
+    uint8_t* const mine = pool + (wave % 2) * (kHalf * kNI * kWave * 16);
+    const uint8_t* const theirs = pool + ((wave % 2) ^ 1) * (kHalf * kNI * kWave * 16);
     // kKeep: the first row tile this wave finishes (0 for the gate wave); a
     // compile-time index, so the accumulators stay in registers
     auto finish = [&](auto keep_c) {
@@ -380,41 +390,39 @@ __global__ __launch_bounds__(kWave * WM * WN) void grouped_gemm_kernel(GemmArgs 
       barrier();
 #pragma unroll
       for (int ii = 0; ii < kHalf; ++ii) {
-        float ts[4];
-        int rows_[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          rows_[r] = row0 + wm * kWaveM + (kKeep + ii) * 16 + (lane / 16) * 4 + r;
-          const int rs = min(rows_[r], row_end - 1);
-          ts[r] = *reinterpret_cast<const float*>(a.token_scale + static_cast<int64_t>(rs) * a.ts_stride);
-        }
-        uint32_t mag[4] = {0, 0, 0, 0};
+        float y[kNI][4];
 #pragma unroll
         for (int j = 0; j < kNI; ++j) {
           const i32x4 other = *reinterpret_cast<const i32x4*>(theirs + ((ii * kNI + j) * kWave + lane) * 16);
           const i32x4 gate = kKeep == 0 ? acc[kKeep + ii][j] : other;
           const i32x4 up = kKeep == 0 ? other : acc[kKeep + ii][j];
-          const int jo = j_base + j * 16;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float y = swiglu(gate[r], up[r], wg[j], wu[j], ts[r]);
-            if (rows_[r] < row_end && jo < a.sn) {
-              const uint32_t b = __float_as_uint(y) & 0x7fffffffu;  // |y| orders as an integer
-              mag[r] = mag[r] > b ? mag[r] : b;
-              a.act[static_cast<int64_t>(rows_[r]) * a.sn + jo] = y;
-            }
-          }
+          for (int r = 0; r < 4; ++r) y[j][r] = swiglu(gate[r], up[r], wg[j], wu[j], ts[ii][r]);
         }
-        // the row's maximum over its 16 lanes (the tile's columns), then
-        // over the launch's column tiles through the global maximum
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
+          const int row = row_base + ii * 16 + r;
+          uint32_t mag = 0;
+#pragma unroll
+          for (int j = 0; j < kNI; ++j) {
+            const int jo = j_base + j * 16;
+            const uint32_t b = jo < a.sn ? __float_as_uint(y[j][r]) & 0x7fffffffu : 0u;  // |y| orders as an integer
+            mag = mag > b ? mag : b;
+          }
+          // the row's maximum over its 16 lanes (the tile's columns), then
+          // over the launch's column tiles through the global maximum
 #pragma unroll
           for (int d = 1; d < 16; d <<= 1) {
-            const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(mag[r]), d, kWave));
-            mag[r] = mag[r] > o ? mag[r] : o;
+            const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(mag), d, kWave));
+            mag = mag > o ? mag : o;
           }
-          if (lane % 16 == 0 && rows_[r] < row_end) atomicMax(a.amax + rows_[r], mag[r]);
+          if (row < row_end) {
+            if (lane % 16 == 0) atomicMax(a.amax + row, mag);
+            float* dst = a.act + static_cast<int64_t>(row) * a.sn;
+#pragma unroll
+            for (int j = 0; j < kNI; ++j)
+              if (j_base + j * 16 < a.sn) dst[j_base + j * 16] = y[j][r];
+          }
         }
       }
     };
