@@ -59,6 +59,22 @@
 // each weight column tile by two, rather than all eight (at n_tiles % 4 !=
 // 0: row slots in order, column tiles innermost).
 //
+// The fused form (section 4.8.1: GMM1 with its PerTokenDequantSwiGLU
+// epilogue on the accumulators) reads each expert's weights as 2 sn rows,
+// gate rows then up rows; its column tile j covers gate rows [128 j, 128 j +
+// 128) and the up rows sn above them, so the waves wn = 0 hold gate sums and
+// wn = 1 the up sums of the same rows and activation columns.  After the k
+// loop the two waves of a pair swap half their sums through LDS, compute the
+// activations of their rows with the epilogue kernel's arithmetic (swiglu.h),
+// store them as floats to the caller's workspace and fold each row's largest
+// magnitude into a per-row word with an atomic max (an integer max of the
+// sign-cleared bit patterns, exact in any order).  A second kernel then
+// quantises every owned row from its maximum exactly as the epilogue kernel
+// does.  The activation arithmetic is bound by the vector ALU; here it runs
+// while the matrix cores wait, which is why the two separate calls are the
+// faster path at the benchmarked shape (the fused one needs half the
+// intermediate memory).
+//
 // The counts live on the device and the host does not read them, so the
 // launch has ceil(rows / 256) + groups row slots (enough for any counts whose
 // total is at most rows: expert g needs at most c_g / 256 + 1 tiles), rounded
