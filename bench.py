@@ -857,6 +857,20 @@ def bench_gemm_swiglu(args, M, torch, W, dev) -> int:
     us = timed(fused, args.steps)
     log(f"timed x{args.steps}: two calls")
     us2 = timed(two_calls, args.steps)
+    log("copy ceiling")
+    hev = HipEvents(args.event_flags)
+    dst = torch.empty_like(flush)
+    for _ in range(2):
+        torch.neg(flush, out=dst)
+    c0, c1 = hev.new(), hev.new()
+    hev.record(c0, stream)
+    for _ in range(10):
+        torch.neg(flush, out=dst)
+    hev.record(c1, stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * flush.numel() * 4 * 10 / (hev.ms(c0, c1) * 1e-3) / 1e9
+    hev.close()
+    del dst
     mean_us, mean2 = statistics.mean(us), statistics.mean(us2)
     ops = gemm_ops(owned, n2, k)
     tops = ops / (mean_us * 1e-6) / 1e12
@@ -910,6 +924,7 @@ def bench_gemm_swiglu(args, M, torch, W, dev) -> int:
         "roofline": {"bound": "mfma", "kernel": "grouped_gemm_swiglu", "achieved": tops,
                      "peak": MFMA_I8_PEAK_TOPS, "unit": "TOP/s", "frac": tops / MFMA_I8_PEAK_TOPS,
                      "traffic": load_traffic("gemm_swiglu", "gemm_swiglu", f"n{n}")},
+        "copy_ceiling_gbps": copy_gbps,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
