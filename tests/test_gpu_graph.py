@@ -129,3 +129,67 @@ def test_graph_expert_side_replays_match_oracle():
         torch.cuda.synchronize()
     exp_o, _ = oracle.grouped_gemm_i8(other.a, k, other.group_count, wts)
     assert np.array_equal(other_out.cpu().numpy(), exp_o), "eager matmul between replays"
+
+
+def test_graph_fused_expert_side_replays_match_oracle():
+    """The matmul with its epilogue fused (three kernels: the row maxima
+    cleared by a fill kernel, the matmul with the activation, the
+    quantisation) captured once and replayed on new rows and new per-expert
+    counts, with eager fused calls on other buffers between replays; every
+    replay against the oracle, rows of no expert untouched."""
+    import combine_moe_layout_03_amd as M
+
+    rows, k, n, groups, stride = 300, 160, 40, 4, 192
+    base = W.gemm_case(950, 1, k, 2 * n, groups)
+    ws, ts = W.gemm_swiglu_scales(950, rows, k, n, groups)
+    a = torch.zeros(rows * stride, dtype=torch.uint8, device="cuda")
+    gc = torch.zeros(groups, dtype=torch.int32, device="cuda")
+    w_d = torch.from_numpy(base.w.view(np.uint8)).cuda()
+    ws_d, ts_d = torch.from_numpy(ws).cuda(), torch.from_numpy(ts).cuda()
+    rb = M.moe_recv_row_bytes(n, M.MOE_INT8_ROWSCALE)
+    out = torch.full((rows * rb,), 0xA5, dtype=torch.uint8, device="cuda")
+    wsp = torch.empty(M.moe_gemm_swiglu_quant_workspace_bytes(rows, n), dtype=torch.uint8, device="cuda")
+
+    def step():
+        M.moe_grouped_gemm_swiglu_quant_i8(a, stride, rows, k, gc, w_d, ws_d, ts_d, out, wsp)
+
+    log("graph fused expert side: eager warm-up")
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    log("graph fused expert side: capture")
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    other = W.gemm_case(951, 120, k, 2 * n, groups, stride=stride, counts=[30, 30, 30, 30])
+    other_a = torch.from_numpy(other.a.reshape(-1).view(np.uint8)).cuda()
+    other_out = torch.zeros(120 * rb, dtype=torch.uint8, device="cuda")
+    other_ws = torch.empty(M.moe_gemm_swiglu_quant_workspace_bytes(120, n), dtype=torch.uint8, device="cuda")
+    off = (n + 31) // 32 * 32
+    for r, counts in enumerate(([100, 0, 150, 20], [300, 0, 0, 0], [10, 20, 30, 40])):
+        c = W.gemm_case(960 + r, rows, k, 2 * n, groups, stride=stride, counts=counts)
+        a.copy_(torch.from_numpy(c.a.reshape(-1).view(np.uint8)))
+        gc.copy_(torch.from_numpy(c.group_count))
+        out.fill_(0xA5)
+        torch.cuda.synchronize()
+        log(f"graph fused expert side: replay {r}")
+        graph.replay()
+        torch.cuda.synchronize()
+        acc, grp = oracle.grouped_gemm_i8(c.a, k, c.group_count, base.w)
+        raw = out.cpu().numpy().reshape(rows, rb)
+        for m in range(rows):
+            if grp[m] < 0:
+                assert (raw[m] == 0xA5).all(), f"replay {r}: row {m} of no expert was written"
+                continue
+            codes, inv, _ = oracle.swiglu_quant_row(acc[m], ws[grp[m]], ts[m])
+            assert np.array_equal(raw[m, :n].view(np.int8), codes), f"replay {r}: row {m} codes"
+            assert raw[m, off:off + 4].view(np.uint32)[0] == np.float32(inv).view(np.uint32), \
+                f"replay {r}: row {m} scale"
+        M.moe_grouped_gemm_swiglu_quant_i8(other_a, stride, 120, k, torch.from_numpy(other.group_count).cuda(),
+                                           w_d, ws_d, ts_d, other_out, other_ws)
+        torch.cuda.synchronize()
+    acc_o, grp_o = oracle.grouped_gemm_i8(other.a, k, other.group_count, base.w)
+    raw_o = other_out.cpu().numpy().reshape(120, rb)
+    for m in range(120):
+        codes, inv, _ = oracle.swiglu_quant_row(acc_o[m], ws[grp_o[m]], ts[m])
+        assert np.array_equal(raw_o[m, :n].view(np.int8), codes), f"eager fused call between replays, row {m}"
