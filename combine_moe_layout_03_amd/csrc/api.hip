@@ -523,11 +523,11 @@ const char* moe_status_str(int status) {
     case MOE_OK: return "ok";
     case MOE_ERR_NULL_PTR: return "a required pointer is NULL";
     case MOE_ERR_BAD_SHAPE: return "bad shape (a size is out of range)";
-    case MOE_ERR_BAD_ALIGN: return "pointer not aligned (16 bytes for rows, 4 for index arrays)";
+    case MOE_ERR_BAD_ALIGN: return "pointer or row stride not aligned as the entry point requires";
     case MOE_ERR_BAD_DTYPE: return "unsupported element type for this argument";
-    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than moe_layout_workspace_bytes()";
-    case MOE_ERR_BUFFER_TOO_SMALL: return "receive buffer smaller than bs * topk rows";
-    case MOE_ERR_UNSUPPORTED: return "size not supported by the library (see MOE_MAX_* and hidden % 8)";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than its size query returns";
+    case MOE_ERR_BUFFER_TOO_SMALL: return "receive or output buffer smaller than the call needs";
+    case MOE_ERR_UNSUPPORTED: return "size outside the library's limits (MOE_MAX_*, MOE_GEMM_MAX_*, divisibility)";
     case MOE_ERR_HIP: return "HIP launch failed (see moe_last_hip_error)";
     case MOE_ERR_SCRATCH_LIMIT:
       return "shape needs more workspace than the static scratch of the no-alloc entry point "
