@@ -337,8 +337,11 @@ int moe_deq_swiglu_quant(const int32_t* acc, int32_t rows, int32_t n, const floa
  *
  * Requires rows >= 0, k >= 1, n >= 1, groups >= 1, aRowBytes >= k (else
  * MOE_ERR_BAD_SHAPE); k % 16 == 0, k <= MOE_GEMM_MAX_K, n <= MOE_GEMM_MAX_N,
- * groups <= MOE_GEMM_MAX_GROUPS (else MOE_ERR_UNSUPPORTED); aRowBytes a
- * multiple of 16 (else MOE_ERR_BAD_ALIGN).  rows == 0 enqueues nothing. */
+ * groups <= MOE_GEMM_MAX_GROUPS, and at most 2^24 workgroups in the launch
+ * (row slots ceil(rows / 256) + groups, rounded up to a multiple of 16 when
+ * ceil(n / 256) % 4 == 0, times ceil(n / 256)) (else MOE_ERR_UNSUPPORTED);
+ * aRowBytes a multiple of 16 (else MOE_ERR_BAD_ALIGN); outBytes as above
+ * (else MOE_ERR_BUFFER_TOO_SMALL).  rows == 0 enqueues nothing. */
 int moe_grouped_gemm_i8(const void* a, int64_t aRowBytes, int32_t rows, int32_t k,
                         const int32_t* groupCount, int32_t groups, const void* w, int32_t n,
                         int32_t* out, size_t outBytes, void* stream);
@@ -376,8 +379,10 @@ int moe_gemm_swiglu_quant_workspace_bytes(int32_t rows, int32_t n, size_t* bytes
  * Requires rows >= 0, k >= 1, n >= 1, groups >= 1, aRowBytes >= k,
  * tokenScaleStride a multiple of 4 and >= 4 (else MOE_ERR_BAD_SHAPE);
  * k % 16 == 0, k <= MOE_GEMM_MAX_K, n % 4 == 0, 2n <= MOE_GEMM_MAX_N, groups
- * <= MOE_GEMM_MAX_GROUPS (else MOE_ERR_UNSUPPORTED); aRowBytes a multiple of
- * 16 (else MOE_ERR_BAD_ALIGN); a small workspace gives
+ * <= MOE_GEMM_MAX_GROUPS, and at most 2^24 workgroups in the matmul launch
+ * (moe_grouped_gemm_i8's count with ceil(n / 128) column tiles) (else
+ * MOE_ERR_UNSUPPORTED); aRowBytes a multiple of 16 (else MOE_ERR_BAD_ALIGN);
+ * a small out buffer gives MOE_ERR_BUFFER_TOO_SMALL, a small workspace
  * MOE_ERR_WORKSPACE_TOO_SMALL.  rows == 0 enqueues nothing.  Enqueues three
  * kernels (clear the row maxima, the matmul with the activation, the
  * quantisation). */
