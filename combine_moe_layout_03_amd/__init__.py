@@ -145,6 +145,38 @@ def _dev(t: Optional[torch.Tensor], name: str, dtype=None, optional: bool = Fals
     return t.data_ptr()
 
 
+def _need(t: Optional[torch.Tensor], name: str, count: int) -> None:
+    """Raise unless ``t`` (if given) holds at least ``count`` elements: the
+    library takes bare pointers, so an undersized tensor would be written or
+    read past its end."""
+    if isinstance(t, torch.Tensor) and t.numel() < count:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {count}")
+
+
+def _experts(expert_num_per_rank: int, rank_size: int) -> Optional[int]:
+    """E = EPR * R when the library accepts the pair (else None: the call's
+    own status reports it, and there is no size to check against)."""
+    if expert_num_per_rank >= 1 and rank_size >= 1 and expert_num_per_rank * rank_size <= MOE_MAX_EXPERTS:
+        return expert_num_per_rank * rank_size
+    return None
+
+
+def _need_routes(expert_num_per_rank: int, rank_size: int, put_offset: Optional[torch.Tensor],
+                 recv_base: Optional[torch.Tensor], num_src: int = 1) -> None:
+    e = _experts(expert_num_per_rank, rank_size)
+    if e is not None:
+        _need(put_offset, "put_offset", e * num_src)
+        _need(recv_base, "recv_base", rank_size)
+
+
+def _need_scales(token_scale: torch.Tensor, rows: int, stride: int) -> None:
+    if rows > 0 and stride >= 4:
+        need = (rows - 1) * stride + 4
+        have = token_scale.numel() * token_scale.element_size()
+        if have < need:
+            raise ValueError(f"token_scale holds {have} bytes, rows at stride {stride} need {need}")
+
+
 def moe_recv_row_bytes(hidden: int, recv_type: int) -> int:
     out = _SZ(0)
     _check("moe_recv_row_bytes", _lib.moe_recv_row_bytes(hidden, recv_type, ctypes.byref(out)))
@@ -158,6 +190,16 @@ def moe_layout_workspace_bytes(bs: int, topk: int, num_experts: int) -> int:
     return out.value
 
 
+def _need_layout(bs, topk, expert_num_per_rank, rank_size, token_per_expert, token_per_rank, send_token_idx,
+                 bad_id_count) -> None:
+    e = _experts(expert_num_per_rank, rank_size)
+    if e is not None:
+        _need(token_per_expert, "token_per_expert", e)
+        _need(token_per_rank, "token_per_rank", rank_size)
+    _need(send_token_idx, "send_token_idx", bs * topk)
+    _need(bad_id_count, "bad_id_count", 1)
+
+
 def moe_layout(topk_idx: torch.Tensor, expert_num_per_rank: int, rank_size: int,
                token_per_expert: torch.Tensor, token_per_rank: torch.Tensor,
                send_token_idx: torch.Tensor, bad_id_count: Optional[torch.Tensor] = None,
@@ -165,6 +207,8 @@ def moe_layout(topk_idx: torch.Tensor, expert_num_per_rank: int, rank_size: int,
     if topk_idx.dim() != 2:
         raise ValueError("topk_idx must be [bs, topk]")
     bs, topk = topk_idx.shape
+    _need_layout(bs, topk, expert_num_per_rank, rank_size, token_per_expert, token_per_rank, send_token_idx,
+                 bad_id_count)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("moe_layout", _lib.moe_layout(
         _dev(topk_idx, "topk_idx", torch.int32), bs, topk, expert_num_per_rank, rank_size,
@@ -183,6 +227,8 @@ def moe_layout_no_alloc(topk_idx: torch.Tensor, expert_num_per_rank: int, rank_s
     if topk_idx.dim() != 2:
         raise ValueError("topk_idx must be [bs, topk]")
     bs, topk = topk_idx.shape
+    _need_layout(bs, topk, expert_num_per_rank, rank_size, token_per_expert, token_per_rank, send_token_idx,
+                 bad_id_count)
     _check("moe_layout_no_alloc", _lib.moe_layout_no_alloc(
         _dev(topk_idx, "topk_idx", torch.int32), bs, topk, expert_num_per_rank, rank_size,
         _dev(token_per_expert, "token_per_expert", torch.int32),
@@ -194,6 +240,12 @@ def moe_layout_no_alloc(topk_idx: torch.Tensor, expert_num_per_rank: int, rank_s
 def moe_notify(token_per_expert: torch.Tensor, expert_num_per_rank: int, rank_size: int,
                put_offset: torch.Tensor, recv_count: torch.Tensor, recv_base: torch.Tensor,
                recv_token_per_expert: torch.Tensor, stream=None) -> None:
+    e = _experts(expert_num_per_rank, rank_size)
+    if e is not None:
+        for t, name in ((token_per_expert, "token_per_expert"), (recv_token_per_expert, "recv_token_per_expert")):
+            _need(t, name, e)
+        _need(recv_count, "recv_count", rank_size)
+    _need_routes(expert_num_per_rank, rank_size, put_offset, recv_base)
     _check("moe_notify", _lib.moe_notify(
         _dev(token_per_expert, "token_per_expert", torch.int32), expert_num_per_rank, rank_size,
         _dev(put_offset, "put_offset", torch.int32), _dev(recv_count, "recv_count", torch.int32),
@@ -208,6 +260,8 @@ def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, send_token_idx: torch.
         raise ValueError("x must be [bs, hidden] and topk_idx [bs, topk]")
     bs, hidden = x.shape
     topk = topk_idx.shape[1]
+    _need(send_token_idx, "send_token_idx", bs * topk)
+    _need_routes(expert_num_per_rank, rank_size, put_offset, recv_base)
     _check("moe_dispatch", _lib.moe_dispatch(
         _dev(x, "x"), dtype_code(x.dtype), bs, hidden, topk,
         _dev(topk_idx, "topk_idx", torch.int32), _dev(send_token_idx, "send_token_idx", torch.int32),
@@ -225,6 +279,9 @@ def moe_combine(recv_x: torch.Tensor, recv_type: int, hidden: int, topk_idx: tor
     bs, topk = topk_idx.shape
     if out.dim() != 2 or tuple(out.shape) != (bs, hidden):
         raise ValueError("out must be [bs, hidden]")
+    _need(topk_weights, "topk_weights", bs * topk)
+    _need(send_token_idx, "send_token_idx", bs * topk)
+    _need_routes(expert_num_per_rank, rank_size, put_offset, recv_base)
     _check("moe_combine", _lib.moe_combine(
         _dev(recv_x, "recv_x"), recv_type, recv_x.numel() * recv_x.element_size(), bs, hidden, topk,
         _dev(topk_idx, "topk_idx", torch.int32), _dev(topk_weights, "topk_weights", torch.float32),
@@ -242,6 +299,11 @@ def moe_notify_multi(token_per_expert: torch.Tensor, expert_num_per_rank: int, r
     num_src, e = token_per_expert.shape
     if tuple(put_offset.shape) != (e, num_src):
         raise ValueError("put_offset must be [E, num_src]")
+    if _experts(expert_num_per_rank, rank_size) not in (None, e):
+        raise ValueError("token_per_expert must have expert_num_per_rank * rank_size columns")
+    _need(recv_count, "recv_count", rank_size)
+    _need(recv_base, "recv_base", rank_size)
+    _need(recv_token_per_expert, "recv_token_per_expert", e)
     _check("moe_notify_multi", _lib.moe_notify_multi(
         _dev(token_per_expert, "token_per_expert", torch.int32), num_src, expert_num_per_rank,
         rank_size, _dev(put_offset, "put_offset", torch.int32),
@@ -258,6 +320,8 @@ def moe_dispatch_src(x: torch.Tensor, topk_idx: torch.Tensor, send_token_idx: to
         raise ValueError("x must be [bs, hidden], topk_idx [bs, topk], put_offset [E, num_src]")
     bs, hidden = x.shape
     topk = topk_idx.shape[1]
+    _need(send_token_idx, "send_token_idx", bs * topk)
+    _need_routes(expert_num_per_rank, rank_size, put_offset, recv_base, put_offset.shape[1])
     _check("moe_dispatch_src", _lib.moe_dispatch_src(
         _dev(x, "x"), dtype_code(x.dtype), bs, hidden, topk,
         _dev(topk_idx, "topk_idx", torch.int32), _dev(send_token_idx, "send_token_idx", torch.int32),
@@ -276,6 +340,9 @@ def moe_combine_src(recv_x: torch.Tensor, recv_type: int, hidden: int, topk_idx:
     bs, topk = topk_idx.shape
     if out.dim() != 2 or tuple(out.shape) != (bs, hidden):
         raise ValueError("out must be [bs, hidden]")
+    _need(topk_weights, "topk_weights", bs * topk)
+    _need(send_token_idx, "send_token_idx", bs * topk)
+    _need_routes(expert_num_per_rank, rank_size, put_offset, recv_base, put_offset.shape[1])
     _check("moe_combine_src", _lib.moe_combine_src(
         _dev(recv_x, "recv_x"), recv_type, recv_x.numel() * recv_x.element_size(), bs, hidden, topk,
         _dev(topk_idx, "topk_idx", torch.int32), _dev(topk_weights, "topk_weights", torch.float32),
@@ -304,6 +371,13 @@ def moe_layout_notify_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, expert_n
         raise ValueError("x must be [bs, hidden] and topk_idx [bs, topk]")
     bs, hidden = x.shape
     topk = topk_idx.shape[1]
+    _need_layout(bs, topk, expert_num_per_rank, rank_size, token_per_expert, token_per_rank, send_token_idx,
+                 bad_id_count)
+    e = _experts(expert_num_per_rank, rank_size)
+    if e is not None:
+        _need(recv_token_per_expert, "recv_token_per_expert", e)
+        _need(recv_count, "recv_count", rank_size)
+    _need_routes(expert_num_per_rank, rank_size, put_offset, recv_base)
     i32 = torch.int32
     _check("moe_layout_notify_dispatch", _lib.moe_layout_notify_dispatch(
         _dev(x, "x"), dtype_code(x.dtype), bs, hidden, topk, _dev(topk_idx, "topk_idx", i32),
@@ -331,8 +405,11 @@ def moe_deq_swiglu_quant(acc: torch.Tensor, weight_scale: torch.Tensor, token_sc
     n = acc.shape[1] // 2
     if weight_scale.numel() != 2 * n:
         raise ValueError("weight_scale must hold 2n floats")
+    if n_rows > acc.shape[0]:
+        raise ValueError("rows exceeds acc's rows")
     if not token_scale.is_cuda:
         raise ValueError("token_scale must be a device tensor")
+    _need_scales(token_scale, n_rows, token_scale_stride)
     _check("moe_deq_swiglu_quant", _lib.moe_deq_swiglu_quant(
         _dev(acc, "acc", torch.int32), n_rows, n, _dev(weight_scale, "weight_scale", torch.float32),
         token_scale.data_ptr(), token_scale_stride, _dev(out, "out"), out.numel() * out.element_size(),
@@ -394,6 +471,7 @@ def moe_grouped_gemm_swiglu_quant_i8(a: torch.Tensor, a_row_bytes: int, rows: in
         raise ValueError("a is smaller than (rows - 1) * a_row_bytes + k bytes")
     if not token_scale.is_cuda:
         raise ValueError("token_scale must be a device tensor")
+    _need_scales(token_scale, rows, token_scale_stride)
     _check("moe_grouped_gemm_swiglu_quant_i8", _lib.moe_grouped_gemm_swiglu_quant_i8(
         _dev(a, "a"), a_row_bytes, rows, k, _dev(group_count, "group_count", torch.int32), groups,
         _dev(w, "w"), n, _dev(weight_scale, "weight_scale", torch.float32), token_scale.data_ptr(),

@@ -266,6 +266,44 @@ def test_binding_rejects_host_tensors(M):
                      torch.zeros((4, 2), dtype=torch.int32))
 
 
+def test_binding_rejects_undersized_arrays(M):
+    """The C calls take bare pointers, so the binding checks each array's
+    length against the shape arguments before anything reaches the library
+    (host tensors suffice: the length check comes first)."""
+    import torch
+
+    i32 = dict(dtype=torch.int32)
+    bs, k, epr, r = 4, 2, 2, 2
+    idx = torch.zeros((bs, k), **i32)
+
+    def raises(name, fn, *args, **kw):
+        with pytest.raises(ValueError, match=name):
+            fn(*args, **kw)
+
+    raises("token_per_expert", M.moe_layout, idx, epr, r, torch.zeros(3, **i32), torch.zeros(2, **i32),
+           torch.zeros((bs, k), **i32))
+    raises("token_per_rank", M.moe_layout, idx, epr, r, torch.zeros(4, **i32), torch.zeros(1, **i32),
+           torch.zeros((bs, k), **i32))
+    raises("send_token_idx", M.moe_layout_no_alloc, idx, epr, r, torch.zeros(4, **i32), torch.zeros(2, **i32),
+           torch.zeros(7, **i32))
+    raises("recv_base", M.moe_notify, torch.zeros(4, **i32), epr, r, torch.zeros(4, **i32),
+           torch.zeros(2, **i32), torch.zeros(1, **i32), torch.zeros(4, **i32))
+    raises("put_offset", M.moe_dispatch, torch.zeros((bs, 64), dtype=torch.bfloat16), idx,
+           torch.zeros((bs, k), **i32), torch.zeros(3, **i32), torch.zeros(2, **i32), epr, r, True,
+           torch.zeros(1 << 12, dtype=torch.uint8))
+    raises("topk_weights", M.moe_combine, torch.zeros(1 << 12, dtype=torch.uint8), M.MOE_INT8_ROWSCALE, 64,
+           idx, torch.zeros(bs * k - 1), torch.zeros((bs, k), **i32), torch.zeros(4, **i32),
+           torch.zeros(2, **i32), epr, r, torch.zeros((bs, 64), dtype=torch.bfloat16))
+    raises("put_offset", M.moe_dispatch_src, torch.zeros((bs, 64), dtype=torch.bfloat16), idx,
+           torch.zeros((bs, k), **i32), torch.zeros((3, 2), **i32), torch.zeros(2, **i32), epr, r, 1, True,
+           torch.zeros(1 << 12, dtype=torch.uint8))
+    raises("token_scale", M.moe_deq_swiglu_quant, torch.zeros((3, 16), **i32), torch.zeros(16),
+           torch.zeros(2), torch.zeros(1 << 10, dtype=torch.uint8))
+    # a pair the library rejects (E above MOE_MAX_EXPERTS) is left to its status code: no length check
+    with pytest.raises(ValueError, match="device tensor"):
+        M.moe_layout(idx, 4096, 1, torch.zeros(4, **i32), torch.zeros(1, **i32), torch.zeros((bs, k), **i32))
+
+
 def test_product_path_never_touches_the_oracle():
     """Nothing in the package or the header refers to the CPU oracle."""
     pkg = os.path.join(ROOT, "combine_moe_layout_03_amd")
