@@ -460,11 +460,13 @@ __global__ __launch_bounds__(256) void clear_u32_kernel(uint32_t* p, int64_t n) 
 constexpr int kQuantRows = 4;  // waves (rows) per workgroup
 __global__ __launch_bounds__(kWave * kQuantRows) void act_quant_kernel(GemmArgs a) {
   const int lane = threadIdx.x % kWave, wave = uniform(static_cast<int>(threadIdx.x / kWave));
+  // the counts' total in 64 bits, as the matmul finds its rows (the counts
+  // are the caller's, and several near 2^31 would wrap a 32-bit sum)
   int64_t owned = 0;
   for (int g0 = 0; g0 < a.groups; g0 += kWave) {
     const int g = g0 + lane;
-    const int c = g < a.groups ? max(a.group_count[g], 0) : 0;
-    owned += __shfl(wave_inclusive_scan(c), kWave - 1, kWave);
+    const int64_t c = g < a.groups ? max(a.group_count[g], 0) : 0;
+    owned += __shfl(wave_scan_i64(c, lane), kWave - 1, kWave);
     if (owned >= a.rows) break;
   }
   owned = min(owned, a.rows);

@@ -84,6 +84,8 @@ def _slot(counts, rows, slot, tm):
     (700, 384, 600, "owned:690:3"),
     (600, 1536, 260, [300, 290]),
     (300, 1392, 256, [300]),
+    # counts whose sum passes 2^31: the slot search sums in 64 bits
+    (300, 128, 512, [2 ** 31 - 1, 2 ** 31 - 1, 5]),
 ])
 def test_grid_covers_owned_outputs_once_and_loads_stay_in_bounds(rows, k, n, counts):
     tm, tn, wm, wn, sk, groups_c, xrows = _shape()

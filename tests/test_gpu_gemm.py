@@ -119,6 +119,8 @@ def boundary_tile_rows(case, seed, n_random=32):
     (2000, 64, 128, 130, "owned:2000", 504),
     # counts past the capacity: the last expert is cut at `rows`
     (1000, 96, 48, 3, [400, 400, 400], 505),
+    # counts whose sum passes 2^31: the first expert owns every row
+    (300, 128, 96, 3, [2 ** 31 - 1, 2 ** 31 - 1, 5], 515),
     # n = 1 and a single expert
     (257, 48, 1, 1, [257], 506),
     # 4 and 8 column tiles (the XCD-aware tile order), empty and negative counts,

@@ -120,6 +120,8 @@ def assert_rows(case, ws, ts, got, rows, what):
     (1000, 96, 48, 3, [400, 400, 400], 707),
     # 8 column tiles, 9 experts, k 8.5 stages
     (1500, 1088, 1024, 9, "owned:1490", 708),
+    # counts whose sum passes 2^31 (the first expert owns every row)
+    (300, 128, 64, 3, [2 ** 31 - 1, 2 ** 31 - 1, 5], 709),
 ])
 def test_fused_matches_oracle(rows, k, n, groups, counts, seed):
     case, ws, ts = make_case(seed, rows, k, n, groups, counts)
