@@ -152,7 +152,10 @@ int moe_layout_no_alloc(const int32_t* topkIdx, int32_t bs, int32_t topk, int32_
  *      recvCount          device int32 [R]: rows in rank r's region.
  *      recvBase           device int32 [R]: first row of rank r's region
  *                         (exclusive scan of recvCount).
- *      recvTokenPerExpert device int32 [E]: rows each expert receives. */
+ *      recvTokenPerExpert device int32 [E]: rows each expert receives.
+ * The counts are moe_layout's: non-negative, with a total that fits in
+ * int32.  Other counts give unspecified offsets; dispatch and combine still
+ * touch no row outside their receive buffer. */
 int moe_notify(const int32_t* tokenPerExpert, int32_t expertNumPerRank, int32_t rankSize,
                int32_t* putOffset, int32_t* recvCount, int32_t* recvBase,
                int32_t* recvTokenPerExpert, void* stream);
