@@ -2,16 +2,21 @@
  * A plain C client of libmoe_ep.so: the four stages of the EP-normal
  * pipeline ("UMDK/CAM communication acceleration library deep analysis v2",
  * section 2: layout 2.3, notify 2.4, dispatch with dynamic int8 2.5,
- * combine 2.6) and their one-launch form (section 3.2), driven through the
+ * combine 2.6) and their one-launch form (section 3.2), then the expert side
+ * on the receive buffer in place (section 4.3 stage 2: the grouped int8
+ * matmul GMM1 over the received experts' rows, and the same matmul with its
+ * section 4.8.1 dequant + SwiGLU + int8 epilogue fused), driven through the
  * C ABI with the HIP runtime alone -- no Python, no torch -- and every output
  * compared bit for bit with the CPU oracle (liboracle.so, test
- * infrastructure) on the same inputs.
+ * infrastructure) on the same inputs; the oracle's expert side reads the
+ * oracle's own receive rows.
  *
  * Inputs come from splitmix64 (Steele, Lea and Flood, "Fast splittable
  * pseudorandom number generators", 2014) as raw bit patterns: bf16 rows with
  * exponents spread over 2^-7 .. 2^3 and one all-zero row, k distinct expert
  * ids per token with about 2 % of the entries replaced by ids outside
- * [0, E), and routing weights in (0, 1).
+ * [0, E), and routing weights in (0, 1); int8 expert weights uniform, and
+ * column scales near 2^-13 so that the gate values come out of order 1.
  *
  * Exit status 0 when every comparison holds, 1 on a mismatch, 2 on a call
  * that fails.  Test program only.
@@ -36,12 +41,19 @@ int oracle_dispatch(const uint16_t *x, int x_kind, int64_t bs, int64_t h, int64_
                     const int32_t *send_token_idx, const int32_t *put_offset, const int32_t *recv_base,
                     int64_t epr, int64_t ranks, int quant, int64_t rows, uint16_t *recv_rows, int8_t *codes,
                     float *inv);
+int oracle_grouped_gemm_i8(const int8_t *a, int64_t a_stride, int64_t rows, int64_t k,
+                           const int32_t *group_count, int64_t groups, const int8_t *w, int64_t n,
+                           const int64_t *row_list, int64_t nlist, int32_t *out, int32_t *row_group);
+int oracle_swiglu_quant_row(const int32_t *acc, int64_t n, const float *weight_scale, float token_scale,
+                            int8_t *codes, float *inv, float *act_out);
 int oracle_combine(const uint16_t *recv_rows, const int8_t *codes, const float *inv, int recv_kind, int64_t bs,
                    int64_t h, int64_t k, const int32_t *topk_idx, const float *topk_w,
                    const int32_t *send_token_idx, const int32_t *put_offset, const int32_t *recv_base,
                    int64_t epr, int64_t ranks, int64_t rows, void *out, int out_kind, float *acc_scratch);
 
-enum { BS = 300, H = 520, K = 6, EPR = 4, R = 8, E = EPR * R, N = BS * K };
+/* H % 16 == 0 (the matmul's k) but not a multiple of 32 (a ragged scale
+ * offset); NA activation columns from 2 NA gate and up columns per expert. */
+enum { BS = 300, H = 528, K = 6, EPR = 4, R = 8, E = EPR * R, N = BS * K, NA = 64 };
 
 static uint64_t rng_state = 0x5eed0c11e47ULL;
 static uint64_t splitmix64(void) {
@@ -114,6 +126,84 @@ static void expect_rows(const char *what, const uint8_t *recv, size_t row_bytes,
       return;
     }
   }
+}
+
+/* The expert side on the receive buffer in place: the grouped matmul to
+ * int32, and the fused matmul + epilogue to int8 rows, against the oracle's
+ * matmul and row epilogue over the oracle's receive rows. */
+static void expert_side(const void *d_recv, size_t row_bytes, const int32_t *d_counts, const int8_t *o_codes,
+                        const float *o_inv, const int32_t *o_counts) {
+  const size_t wbytes = (size_t)E * 2 * NA * H;
+  int8_t *w = malloc(wbytes);
+  float *ws = malloc(sizeof(float) * E * 2 * NA);
+  if (!w || !ws) exit(2);
+  for (size_t i = 0; i < wbytes; ++i) w[i] = (int8_t)(splitmix64() >> 56);
+  for (int i = 0; i < E * 2 * NA; ++i) {
+    const uint64_t u = splitmix64();
+    const uint32_t bits = (uint32_t)(112 + u % 4) << 23 | (uint32_t)((u >> 8) & 0x7fffff);
+    memcpy(&ws[i], &bits, 4);
+  }
+  void *d_w = dev_copy(w, wbytes);
+  void *d_ws = dev_copy(ws, sizeof(float) * E * 2 * NA);
+  int32_t *d_acc = NULL;
+  HIP_OK(hipMalloc((void **)&d_acc, sizeof(int32_t) * N * 2 * NA));
+  HIP_OK(hipMemset(d_acc, 0x5a, sizeof(int32_t) * N * 2 * NA));
+  size_t q_bytes = 0, wsp_bytes = 0;
+  MOE_OK_(moe_recv_row_bytes(NA, MOE_INT8_ROWSCALE, &q_bytes));
+  MOE_OK_(moe_gemm_swiglu_quant_workspace_bytes(N, NA, &wsp_bytes));
+  uint8_t *d_q = NULL;
+  HIP_OK(hipMalloc((void **)&d_q, q_bytes * N));
+  HIP_OK(hipMemset(d_q, 0xa5, q_bytes * N));
+  void *d_wsp = dev_alloc(wsp_bytes);
+  const size_t scale_off = (H + 31) / 32 * 32;
+  MOE_OK_(moe_grouped_gemm_i8(d_recv, (int64_t)row_bytes, N, H, d_counts, E, d_w, 2 * NA, d_acc,
+                              sizeof(int32_t) * N * 2 * NA, NULL));
+  MOE_OK_(moe_grouped_gemm_swiglu_quant_i8(d_recv, (int64_t)row_bytes, N, H, d_counts, E, d_w, NA, d_ws,
+                                           (const uint8_t *)d_recv + scale_off, (int64_t)row_bytes, d_q,
+                                           q_bytes * N, d_wsp, wsp_bytes, NULL));
+  HIP_OK(hipDeviceSynchronize());
+  int32_t *acc = host_copy(d_acc, sizeof(int32_t) * N * 2 * NA);
+  uint8_t *q = host_copy(d_q, q_bytes * N);
+
+  int32_t *o_acc = calloc((size_t)N * 2 * NA, sizeof(int32_t));
+  int32_t *o_grp = malloc(sizeof(int32_t) * N);
+  if (!o_acc || !o_grp) exit(2);
+  if (oracle_grouped_gemm_i8(o_codes, H, N, H, o_counts, E, w, 2 * NA, NULL, N, o_acc, o_grp)) {
+    fprintf(stderr, "oracle matmul failed\n");
+    exit(2);
+  }
+  int owned = 0, bad_acc = -1, bad_q = -1;
+  for (int m = 0; m < N; ++m) {
+    const uint8_t *row = q + (size_t)m * q_bytes;
+    if (o_grp[m] < 0) {
+      /* rows of no expert: neither call writes them */
+      for (int j = 0; j < 2 * NA; ++j)
+        if (acc[(size_t)m * 2 * NA + j] != 0x5a5a5a5a && bad_acc < 0) bad_acc = m;
+      for (size_t b = 0; b < q_bytes; ++b)
+        if (row[b] != 0xa5 && bad_q < 0) bad_q = m;
+      continue;
+    }
+    ++owned;
+    if (memcmp(acc + (size_t)m * 2 * NA, o_acc + (size_t)m * 2 * NA, sizeof(int32_t) * 2 * NA) && bad_acc < 0)
+      bad_acc = m;
+    int8_t codes[NA];
+    float inv = 0;
+    if (oracle_swiglu_quant_row(o_acc + (size_t)m * 2 * NA, NA, ws + (size_t)o_grp[m] * 2 * NA, o_inv[m], codes,
+                                &inv, NULL)) {
+      fprintf(stderr, "oracle epilogue failed on row %d\n", m);
+      exit(2);
+    }
+    if ((memcmp(row, codes, NA) || memcmp(row + (NA + 31) / 32 * 32, &inv, 4)) && bad_q < 0) bad_q = m;
+  }
+  if (bad_acc >= 0) fprintf(stderr, "MISMATCH grouped matmul: row %d\n", bad_acc);
+  if (bad_q >= 0) fprintf(stderr, "MISMATCH fused matmul + epilogue: row %d\n", bad_q);
+  failures += (bad_acc >= 0) + (bad_q >= 0);
+  printf("c client, expert side on the receive buffer: %s (%d owned rows of %d, %d experts, k %d, "
+         "%d gate + %d up columns)\n",
+         bad_acc < 0 && bad_q < 0 ? "bit-exact" : "MISMATCH", owned, N, E, H, NA, NA);
+  free(w); free(ws); free(acc); free(q); free(o_acc); free(o_grp);
+  HIP_OK(hipFree(d_w)); HIP_OK(hipFree(d_ws)); HIP_OK(hipFree(d_acc)); HIP_OK(hipFree(d_q));
+  HIP_OK(hipFree(d_wsp));
 }
 
 int main(void) {
@@ -221,6 +311,7 @@ int main(void) {
     uint16_t *out = host_copy(d_out, sizeof(uint16_t) * BS * H);
     expect_equal("combine output", out, o_out, sizeof(uint16_t) * BS * H);
     free(out);
+    if (form == 0) expert_side(d_recv, row_bytes, d_rtpe, o_codes, o_inv, o_rtpe);
     printf("c client, %s: %s (bs %d, h %d, topk %d, %d experts, %d ranks, %lld bad ids)\n", name,
            failures ? "MISMATCH" : "bit-exact", BS, H, K, E, R, (long long)o_bad);
     HIP_OK(hipFree(d_tpe)); HIP_OK(hipFree(d_tpr)); HIP_OK(hipFree(d_sti)); HIP_OK(hipFree(d_bad));

@@ -1,8 +1,10 @@
-"""The C ABI from plain C: tests/c_client.c drives the four stages and their
-one-launch form through include/moe_ep.h with the HIP runtime alone (no
-Python, no torch) and compares every output with the CPU oracle, bit for
-bit.  The CPU test builds and links it (gcc, a second compiler reading the
-header as C); the GPU test runs it as a child process."""
+"""The C ABI from plain C: tests/c_client.c drives the four stages, their
+one-launch form and the expert side on the receive buffer (the grouped
+matmul and the fused matmul + epilogue) through include/moe_ep.h with the
+HIP runtime alone (no Python, no torch) and compares every output with the
+CPU oracle, bit for bit.  The CPU test builds and links it (gcc, a second
+compiler reading the header as C); the GPU test runs it as a child
+process."""
 
 import os
 import subprocess
@@ -40,8 +42,8 @@ def test_c_client_builds_and_links():
 def test_c_client_runs_bit_exact():
     if not os.path.exists(BIN) or os.path.getmtime(BIN) < os.path.getmtime(SRC):
         build_client()
-    print("[gpu] c client: four stages, then the one-launch form", flush=True)
+    print("[gpu] c client: four stages, the expert side, then the one-launch form", flush=True)
     r = subprocess.run([BIN], capture_output=True, text=True, timeout=120)
     print(r.stdout, flush=True)
     assert r.returncode == 0, r.stderr + r.stdout
-    assert r.stdout.count("bit-exact") == 2
+    assert r.stdout.count("bit-exact") == 3
