@@ -38,6 +38,20 @@ def test_c_client_builds_and_links():
         assert lib in r.stdout
 
 
+def test_c_client_oracle_declarations_match_the_oracle(tmp_path):
+    """The client declares the oracle's functions itself (the oracle has no
+    header); compiled after the oracle's own definitions, any difference is
+    a conflicting-types error."""
+    import re
+
+    decls = re.findall(r"^int oracle_\w+\([^;]*\);", open(SRC).read(), flags=re.M | re.S)
+    assert len(decls) >= 6
+    probe = tmp_path / "decls.c"
+    probe.write_text(f'#include "{os.path.join(ORACLEDIR, "moe_oracle.c")}"\n' + "\n".join(decls) + "\n")
+    r = subprocess.run(["gcc", "-std=c11", "-fsyntax-only", "-Werror", str(probe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 @pytest.mark.gpu
 def test_c_client_runs_bit_exact():
     if not os.path.exists(BIN) or os.path.getmtime(BIN) < os.path.getmtime(SRC):
