@@ -257,6 +257,49 @@ def test_fused_rejects_on_host(M):
     assert L.moe_fused_supported(16, 8, 2, 4, 2, 0, 2, ctypes.byref(out)) == 4   # quant flag
 
 
+def test_grouped_gemm_swiglu_rejects_on_host(M):
+    """The fused matmul + epilogue call: every shape, limit, alignment, NULL,
+    buffer and workspace error returns before anything is enqueued."""
+    L = M._lib
+    rb = M.moe_recv_row_bytes(2048, M.MOE_INT8_ROWSCALE)
+    ws_need = M.moe_gemm_swiglu_quant_workspace_bytes(64, 2048)
+    assert ws_need == 64 * 2048 * 4 + 256
+    ok = dict(a_row_bytes=7296, rows=64, k=7168, groups=16, n=2048, ts_stride=7296, out_bytes=64 * rb,
+              ws_bytes=ws_need)
+
+    def call(a=P, a_row_bytes=ok["a_row_bytes"], rows=ok["rows"], k=ok["k"], gc=P, groups=ok["groups"], w=P,
+             n=ok["n"], wsc=P, ts=P, ts_stride=ok["ts_stride"], out=P, out_bytes=ok["out_bytes"], wsp=P,
+             ws_bytes=ok["ws_bytes"]):
+        return L.moe_grouped_gemm_swiglu_quant_i8(a, a_row_bytes, rows, k, gc, groups, w, n, wsc, ts, ts_stride,
+                                                  out, out_bytes, wsp, ws_bytes, None)
+
+    assert call(rows=-1) == 2 and call(k=0) == 2 and call(n=0) == 2 and call(groups=0) == 2
+    assert call(a_row_bytes=7152) == 2                       # shorter than k
+    assert call(ts_stride=2) == 2 and call(ts_stride=6) == 2  # token-scale stride below 4 or not a multiple
+    assert call(k=7160, a_row_bytes=7168) == 7               # k % 16
+    assert call(n=2046) == 7 and call(n=32772) == 7          # n % 4; 2n above MOE_GEMM_MAX_N
+    assert call(k=65552, a_row_bytes=65552) == 7 and call(groups=65537) == 7
+    assert call(a_row_bytes=7304) == 3                       # row stride not a multiple of 16
+    assert call(rows=0, a=None, gc=None, w=None, wsc=None, ts=None, out=None, wsp=None) == 0
+    for name in ("a", "gc", "w", "wsc", "ts", "out", "wsp"):
+        assert call(**{name: None}) == 1, name
+    assert call(a=P + 8) == 3 and call(w=P + 8) == 3 and call(out=P + 8) == 3 and call(wsp=P + 8) == 3
+    assert call(gc=P + 2) == 3 and call(wsc=P + 2) == 3 and call(ts=P + 2) == 3
+    assert call(out_bytes=64 * rb - 1) == 6
+    assert call(ws_bytes=ws_need - 1) == 5
+    # more workgroups than one launch takes: (rows / 256 + groups) row slots x n / 128 column tiles
+    big_rows, big_n = 2 ** 31 - 1, 32768
+    big_rb = M.moe_recv_row_bytes(big_n, M.MOE_INT8_ROWSCALE)
+    assert call(rows=big_rows, a_row_bytes=16, k=16, n=big_n, out_bytes=big_rows * big_rb,
+                ws_bytes=M.moe_gemm_swiglu_quant_workspace_bytes(big_rows, big_n)) == 7
+    # the size query
+    out = ctypes.c_size_t(0)
+    assert L.moe_gemm_swiglu_quant_workspace_bytes(64, 2048, None) == 1
+    assert L.moe_gemm_swiglu_quant_workspace_bytes(-1, 2048, ctypes.byref(out)) == 2
+    assert L.moe_gemm_swiglu_quant_workspace_bytes(64, 0, ctypes.byref(out)) == 2
+    assert L.moe_gemm_swiglu_quant_workspace_bytes(0, 8, ctypes.byref(out)) == 0 and out.value == 0
+
+
 def test_binding_rejects_host_tensors(M):
     import torch
 
