@@ -125,6 +125,22 @@ def test_layout_rejects_on_host(M):
     assert L.moe_layout(P, 16, 8, 16, 16, P, P, P, P + 1, None, 0, None) == 3
 
 
+def test_layout_no_alloc_rejects_on_host(M):
+    # the same argument errors as moe_layout, and shapes beyond the static
+    # scratch, all before any HIP call
+    L = M._lib
+    assert L.moe_layout_no_alloc(P, -1, 8, 16, 16, P, P, P, None, None) == 2
+    assert L.moe_layout_no_alloc(P, 16, 33, 16, 16, P, P, P, None, None) == 7
+    assert L.moe_layout_no_alloc(P, 16, 8, 2049, 1, P, P, P, None, None) == 7
+    assert L.moe_layout_no_alloc(P, 16, 8, 16, 16, None, P, P, None, None) == 1
+    assert L.moe_layout_no_alloc(None, 16, 8, 16, 16, P, P, P, None, None) == 1
+    assert L.moe_layout_no_alloc(P + 2, 16, 8, 16, 16, P, P, P, None, None) == 3
+    assert L.moe_layout_no_alloc(P, 16, 8, 16, 16, P, P, P, P + 1, None) == 3
+    # the per-tile count table of 300000 x 8 entries at 256 experts exceeds the 1 MiB scratch
+    assert M.moe_layout_workspace_bytes(300000, 8, 256) > M.MOE_NO_ALLOC_SCRATCH_BYTES
+    assert L.moe_layout_no_alloc(P, 300000, 8, 16, 16, P, P, P, None, None) == 9
+
+
 def test_notify_rejects_on_host(M):
     L = M._lib
     assert L.moe_notify(P, 0, 4, P, P, P, P, None) == 2
